@@ -1,0 +1,29 @@
+"""CPU oracle for dynamic sparse attention in causal prefill (test infrastructure).
+
+Plain, slow NumPy fp64 statements of what the hot path computes. Only the
+test suite, the smoke check and the benchmark's CPU-baseline leg use this
+package; the product path never imports it.
+"""
+from .minf_oracle import (  # noqa: F401
+    BLOCK,
+    topk_lowidx,
+    attend_rows,
+    dense_attn,
+    causal_mask_row,
+    ashape_mask_row,
+    vs_last_query_probs,
+    vs_column_diag_sums,
+    vs_index,
+    vs_block_set,
+    vs_column_set,
+    vs_mask_block,
+    pool_blocks,
+    block_scores,
+    block_index,
+    bs_mask_block,
+    ashape_mask_block,
+    build_vs_index,
+    build_block_index,
+    sparse_attn,
+    plan_mask_block,
+)
