@@ -1,0 +1,81 @@
+"""Build libminf.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
+
+Usage: python -m dynamic_sparse_attention_index_amd.build [--jobs N]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libminf.so")
+OBJ_DIR = os.path.join(HERE, "_build")
+
+SOURCES = ["attn.hip", "vs_index.hip", "bs_index.hip", "api.cpp"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def common_flags() -> list:
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-Wall",
+        "-Wno-unused-result",
+        # keep the compiler from forming packed fp32 VALU ops
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        f"-I{os.path.join(ROOT, 'include')}",
+        f"-I{CSRC}",
+    ]
+
+
+def _compile(src: str) -> str:
+    out = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", out]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed for {src}:\n{res.stderr}")
+    return out
+
+
+def build(jobs: int = 4, verbose: bool = False) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=4)
+    args = ap.parse_args(argv)
+    build(args.jobs, verbose=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,437 @@
+// C ABI of the library: argument validation, workspace carving, launches.
+// Every check runs before the first launch; a failed check launches nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/minf.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace minf;
+
+namespace {
+
+thread_local std::string g_detail;
+
+minf_status fail(minf_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+minf_status hip_fail(hipError_t e, const char* where) {
+  return fail(MINF_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t count) {
+    T* p = (T*)(base + off);
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+int64_t nblocks(int64_t n) { return (n + kBlock - 1) / kBlock; }
+
+minf_status check_common(const void* q, const void* k, int64_t n, int hq, int hkv, int d, int64_t max_n) {
+  if (!q || !k) return fail(MINF_E_INVALID_ARG, "q and k must be non-null device pointers");
+  if (n < 1) return fail(MINF_E_INVALID_ARG, "n must be >= 1 (got %lld)", (long long)n);
+  if (hq < 1 || hkv < 1) return fail(MINF_E_INVALID_ARG, "hq and hkv must be >= 1");
+  if (hq % hkv != 0) return fail(MINF_E_INVALID_ARG, "hq (%d) must be a multiple of hkv (%d)", hq, hkv);
+  if (d != kHeadDim) return fail(MINF_E_UNSUPPORTED, "head dim %d is not supported (only 128)", d);
+  if (n > max_n) return fail(MINF_E_UNSUPPORTED, "n = %lld exceeds the supported %lld", (long long)n, (long long)max_n);
+  return MINF_OK;
+}
+
+minf_status check_scale(float scale) {
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(MINF_E_INVALID_ARG, "scale must be finite and > 0");
+  return MINF_OK;
+}
+
+minf_status check_heads(const int32_t* heads, int n_heads, int hq) {
+  if (n_heads < 0) return fail(MINF_E_INVALID_ARG, "n_heads must be >= 0");
+  if (n_heads > 0 && !heads) return fail(MINF_E_INVALID_ARG, "heads must be a host array of n_heads ids");
+  std::vector<char> seen(hq, 0);
+  for (int i = 0; i < n_heads; ++i) {
+    if (heads[i] < 0 || heads[i] >= hq) return fail(MINF_E_INVALID_ARG, "heads[%d] = %d out of [0, %d)", i, heads[i], hq);
+    if (seen[heads[i]]) return fail(MINF_E_INVALID_ARG, "head %d listed twice", heads[i]);
+    seen[heads[i]] = 1;
+  }
+  return MINF_OK;
+}
+
+minf_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return MINF_OK;
+  if (!ws) return fail(MINF_E_WORKSPACE, "workspace is null but %zu bytes are required", need);
+  if (((uintptr_t)ws) % 16 != 0) return fail(MINF_E_WORKSPACE, "workspace must be 16-byte aligned");
+  if (ws_bytes < need) return fail(MINF_E_WORKSPACE, "workspace has %zu bytes, %zu required", ws_bytes, need);
+  return MINF_OK;
+}
+
+// ---------------- VS workspace
+int vs_max_chunks(int64_t n) { return (int)std::min<int64_t>(nblocks(n), 2048); }
+
+struct VsWs {
+  float *part_m, *part_l, *row_m, *row_il, *vcol, *slsum, *dpart;
+  size_t bytes;
+};
+
+VsWs carve_vs(void* base, int64_t n, int n_heads) {
+  Carver c{(char*)base};
+  const size_t nh = (size_t)std::max(n_heads, 1);
+  const size_t mc = (size_t)vs_max_chunks(n);
+  const size_t nt = (size_t)nblocks(n);
+  VsWs w;
+  w.part_m = c.take<float>(nh * 64 * mc);
+  w.part_l = c.take<float>(nh * 64 * mc);
+  w.row_m = c.take<float>(nh * 64);
+  w.row_il = c.take<float>(nh * 64);
+  w.vcol = c.take<float>(nh * (size_t)n);
+  w.slsum = c.take<float>(nh * (size_t)n);
+  w.dpart = c.take<float>(nh * nt * 128);
+  w.bytes = c.off;
+  return w;
+}
+
+minf_status run_vs_scores(const void* q, const void* k, int64_t n, int hq, int hkv, const int32_t* heads,
+                          int n_heads, int last_q, float scale, const VsWs& w, hipStream_t stream) {
+  const int grp = hq / hkv;
+  // group the listed heads by KV head, at most 4 per group (one wave each)
+  std::vector<VsGroup> groups;
+  for (int kv = 0; kv < hkv; ++kv) {
+    VsGroup cur{};
+    cur.kv = kv;
+    for (int i = 0; i < n_heads; ++i) {
+      if (heads[i] / grp != kv) continue;
+      cur.head[cur.cnt] = heads[i];
+      cur.slot[cur.cnt] = i;
+      if (++cur.cnt == 4) {
+        groups.push_back(cur);
+        cur = VsGroup{};
+        cur.kv = kv;
+      }
+    }
+    if (cur.cnt) groups.push_back(cur);
+  }
+  const int ntiles = (int)nblocks(n);
+  for (size_t g0 = 0; g0 < groups.size(); g0 += kMaxVsGroups) {
+    VsLaunch a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.n = (int)n;
+    a.r = (int)std::min<int64_t>(last_q, n);
+    a.ngroups = (int)std::min<size_t>(kMaxVsGroups, groups.size() - g0);
+    const int want = std::max(1, (2048 + a.ngroups - 1) / a.ngroups);
+    int nch = std::min(std::min(want, ntiles), vs_max_chunks(n));
+    a.tiles_per_chunk = (ntiles + nch - 1) / nch;
+    a.nchunks = (ntiles + a.tiles_per_chunk - 1) / a.tiles_per_chunk;
+    a.ntiles = ntiles;
+    a.n_slots = n_heads;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_m = w.part_m;
+    a.part_l = w.part_l;
+    a.row_m = w.row_m;
+    a.row_il = w.row_il;
+    a.vcol = w.vcol;
+    a.slsum = w.slsum;
+    a.dpart = w.dpart;
+    for (int i = 0; i < a.ngroups; ++i) a.groups[i] = groups[g0 + i];
+    hipError_t e = launch_vs_scores(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "VS score kernels");
+  }
+  return MINF_OK;
+}
+
+minf_status check_vs_args(const void* q, const void* k, int64_t n, int hq, int hkv, int d, const int32_t* heads,
+                          int n_heads, int last_q, float scale, void* ws, size_t ws_bytes) {
+  minf_status s;
+  if ((s = check_common(q, k, n, hq, hkv, d, kMaxTokens)) != MINF_OK) return s;
+  if ((s = check_scale(scale)) != MINF_OK) return s;
+  if ((s = check_heads(heads, n_heads, hq)) != MINF_OK) return s;
+  if (last_q < 1) return fail(MINF_E_INVALID_ARG, "last_q must be >= 1");
+  if (last_q > 64) return fail(MINF_E_UNSUPPORTED, "last_q > 64 is not supported");
+  if (n_heads == 0) return MINF_OK;
+  return check_ws(ws, ws_bytes, minf_vs_index_workspace_size(n, n_heads));
+}
+
+// ---------------- BS workspace
+struct BsWs {
+  float *qbar, *kbar_t;
+  size_t bytes;
+};
+
+BsWs carve_bs(void* base, int64_t n, int hkv, int n_heads) {
+  Carver c{(char*)base};
+  const size_t nb = (size_t)nblocks(n);
+  BsWs w;
+  w.qbar = c.take<float>((size_t)std::max(n_heads, 1) * nb * kHeadDim);
+  w.kbar_t = c.take<float>((size_t)std::max(std::min(hkv, std::max(n_heads, 1)), 1) * nb * kHeadDim);
+  w.bytes = c.off;
+  return w;
+}
+
+// ---------------- sparse attention workspace
+size_t bitmap_words(int64_t n) { return (size_t)(nblocks(n) >> 5) + 1; }
+
+}  // namespace
+
+extern "C" {
+
+const char* minf_status_string(minf_status s) {
+  switch (s) {
+    case MINF_OK: return "MINF_OK";
+    case MINF_E_INVALID_ARG: return "MINF_E_INVALID_ARG";
+    case MINF_E_UNSUPPORTED: return "MINF_E_UNSUPPORTED";
+    case MINF_E_WORKSPACE: return "MINF_E_WORKSPACE";
+    case MINF_E_HIP: return "MINF_E_HIP";
+    default: return "MINF_E_UNKNOWN";
+  }
+}
+
+const char* minf_last_error_detail(void) { return g_detail.c_str(); }
+
+int minf_abi_version(void) { return 1; }
+
+size_t minf_vs_index_workspace_size(int64_t n, int n_heads) {
+  if (n < 1 || n_heads < 0) return 0;
+  return carve_vs(nullptr, n, n_heads).bytes;
+}
+
+minf_status minf_vs_scores(const void* q, const void* k, int64_t n, int hq, int hkv, int d, const int32_t* heads,
+                           int n_heads, int last_q, float scale, float* v_out, float* sl_out, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+  g_detail.clear();
+  minf_status s = check_vs_args(q, k, n, hq, hkv, d, heads, n_heads, last_q, scale, workspace, ws_bytes);
+  if (s != MINF_OK) return s;
+  if (n_heads > 0 && (!v_out || !sl_out)) return fail(MINF_E_INVALID_ARG, "v_out and sl_out must be non-null");
+  if (n_heads == 0) return MINF_OK;
+  VsWs w = carve_vs(workspace, n, n_heads);
+  if ((s = run_vs_scores(q, k, n, hq, hkv, heads, n_heads, last_q, scale, w, stream)) != MINF_OK) return s;
+  const size_t bytes = (size_t)n_heads * (size_t)n * sizeof(float);
+  hipError_t e = hipMemcpyAsync(v_out, w.vcol, bytes, hipMemcpyDeviceToDevice, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(sl_out, w.slsum, bytes, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy of VS scores");
+  return MINF_OK;
+}
+
+minf_status minf_build_vs_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                const int32_t* heads, int n_heads, int last_q, int k_v, int k_s, float scale,
+                                int32_t* v_idx, int32_t* s_idx, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  g_detail.clear();
+  minf_status s = check_vs_args(q, k, n, hq, hkv, d, heads, n_heads, last_q, scale, workspace, ws_bytes);
+  if (s != MINF_OK) return s;
+  if (k_v < 0 || k_s < 0) return fail(MINF_E_INVALID_ARG, "k_v and k_s must be >= 0");
+  const int kv_eff = (int)std::min<int64_t>(k_v, n);
+  const int ks_eff = (int)std::min<int64_t>(k_s, n);
+  if (n_heads > 0 && ((kv_eff > 0 && !v_idx) || (ks_eff > 0 && !s_idx)))
+    return fail(MINF_E_INVALID_ARG, "v_idx / s_idx must be non-null when their budget is > 0");
+  if (n_heads == 0) return MINF_OK;
+  VsWs w = carve_vs(workspace, n, n_heads);
+  if ((s = run_vs_scores(q, k, n, hq, hkv, heads, n_heads, last_q, scale, w, stream)) != MINF_OK) return s;
+  hipError_t e = hipSuccess;
+  if (kv_eff > 0) e = launch_topk_rows(w.vcol, n, n_heads, (int)n, kv_eff, v_idx, kv_eff, stream);
+  if (e == hipSuccess && ks_eff > 0) e = launch_topk_rows(w.slsum, n, n_heads, (int)n, ks_eff, s_idx, ks_eff, stream);
+  if (e != hipSuccess) return hip_fail(e, "VS top-k kernel");
+  return MINF_OK;
+}
+
+size_t minf_block_index_workspace_size(int64_t n, int hq, int hkv, int n_heads) {
+  (void)hq;
+  if (n < 1 || n_heads < 0 || hkv < 1) return 0;
+  return carve_bs(nullptr, n, hkv, n_heads).bytes;
+}
+
+minf_status minf_build_block_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                   const int32_t* heads, int n_heads, int k_b, int32_t* blk_idx, int32_t* blk_cnt,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_common(q, k, n, hq, hkv, d, kMaxTokens)) != MINF_OK) return s;
+  if ((s = check_heads(heads, n_heads, hq)) != MINF_OK) return s;
+  if (k_b < 1) return fail(MINF_E_INVALID_ARG, "k_b must be >= 1");
+  if (n_heads == 0) return MINF_OK;
+  if (!blk_idx || !blk_cnt) return fail(MINF_E_INVALID_ARG, "blk_idx and blk_cnt must be non-null");
+  if ((s = check_ws(workspace, ws_bytes, minf_block_index_workspace_size(n, hq, hkv, n_heads))) != MINF_OK) return s;
+  BsWs w = carve_bs(workspace, n, hkv, n_heads);
+  const int grp = hq / hkv;
+  // distinct KV heads in first-use order, and each query head's KV slot
+  std::vector<int32_t> kv_heads, kv_slot(n_heads), q_slots(n_heads);
+  for (int i = 0; i < n_heads; ++i) {
+    const int kv = heads[i] / grp;
+    auto it = std::find(kv_heads.begin(), kv_heads.end(), kv);
+    kv_slot[i] = (int32_t)(it - kv_heads.begin());
+    if (it == kv_heads.end()) kv_heads.push_back(kv);
+    q_slots[i] = i;
+  }
+  std::vector<int32_t> kv_slots(kv_heads.size());
+  for (size_t i = 0; i < kv_heads.size(); ++i) kv_slots[i] = (int32_t)i;
+  const int nb = (int)nblocks(n);
+  hipError_t e = launch_block_pool((const uint16_t*)q, (int)n, heads, q_slots.data(), n_heads, w.qbar, nullptr, stream);
+  if (e == hipSuccess)
+    e = launch_block_pool((const uint16_t*)k, (int)n, kv_heads.data(), kv_slots.data(), (int)kv_heads.size(),
+                          nullptr, w.kbar_t, stream);
+  if (e == hipSuccess) e = launch_block_topk(w.qbar, w.kbar_t, kv_slot.data(), n_heads, nb, k_b, blk_idx, blk_cnt, stream);
+  if (e != hipSuccess) return hip_fail(e, "block index kernels");
+  return MINF_OK;
+}
+
+minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const int32_t* heads, int n_heads,
+                            float* out, hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_common(x, x, n, h_total, 1, d, kMaxTokens)) != MINF_OK) return s;
+  if ((s = check_heads(heads, n_heads, h_total)) != MINF_OK) return s;
+  if (n_heads == 0) return MINF_OK;
+  if (!out) return fail(MINF_E_INVALID_ARG, "out must be non-null");
+  std::vector<int32_t> slots(n_heads);
+  for (int i = 0; i < n_heads; ++i) slots[i] = i;
+  hipError_t e = launch_block_pool((const uint16_t*)x, (int)n, heads, slots.data(), n_heads, out, nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e, "pooling kernel");
+  return MINF_OK;
+}
+
+size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
+  if (n < 1 || hq < 1) return 0;
+  return align_up((size_t)hq * 2 * bitmap_words(n) * sizeof(uint32_t));
+}
+
+static minf_status check_attn_common(const void* q, const void* k, const void* v, void* o, int64_t n, int hq,
+                                     int hkv, int d, float scale, int64_t max_n) {
+  minf_status s;
+  if ((s = check_common(q, k, n, hq, hkv, d, max_n)) != MINF_OK) return s;
+  if (!v || !o) return fail(MINF_E_INVALID_ARG, "v and o must be non-null device pointers");
+  return check_scale(scale);
+}
+
+static minf_status launch_all_heads(AttnLaunch& a, int hq, hipStream_t stream) {
+  for (int h0 = 0; h0 < hq; h0 += kMaxLaunchHeads) {
+    a.head0 = h0;
+    a.nh = std::min(kMaxLaunchHeads, hq - h0);
+    hipError_t e = launch_attn(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel");
+  }
+  return MINF_OK;
+}
+
+minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t n, int hq,
+                             int hkv, int d, float scale, const minf_head_plan* plans, void* workspace,
+                             size_t ws_bytes, hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_attn_common(q, k, v, o, n, hq, hkv, d, scale, kMaxTokens)) != MINF_OK) return s;
+  if (!plans) return fail(MINF_E_INVALID_ARG, "plans must be a host array of hq entries");
+  bool any_vs = false;
+  for (int h = 0; h < hq; ++h) {
+    const minf_head_plan& p = plans[h];
+    switch (p.kind) {
+      case MINF_KIND_DENSE: break;
+      case MINF_KIND_ASHAPE:
+        if (p.sink < 0 || p.local < 0) return fail(MINF_E_INVALID_ARG, "head %d: sink and local must be >= 0", h);
+        break;
+      case MINF_KIND_VS:
+        if (p.k_v < 0 || p.k_s < 0) return fail(MINF_E_INVALID_ARG, "head %d: k_v and k_s must be >= 0", h);
+        if ((p.k_v > 0 && !p.v_idx) || (p.k_s > 0 && !p.s_idx))
+          return fail(MINF_E_INVALID_ARG, "head %d: v_idx / s_idx null with a positive count", h);
+        any_vs = true;
+        break;
+      case MINF_KIND_BLOCK:
+        if (p.k_b < 1) return fail(MINF_E_INVALID_ARG, "head %d: k_b must be >= 1", h);
+        if (!p.blk_idx || !p.blk_cnt) return fail(MINF_E_INVALID_ARG, "head %d: blk_idx / blk_cnt are null", h);
+        break;
+      default: return fail(MINF_E_INVALID_ARG, "head %d: unknown plan kind %d", h, p.kind);
+    }
+  }
+  if (any_vs && (s = check_ws(workspace, ws_bytes, minf_sparse_attn_workspace_size(n, hq))) != MINF_OK) return s;
+
+  AttnLaunch a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.n = (int)n;
+  a.nb = (int)nblocks(n);
+  a.hq = hq;
+  a.hkv = hkv;
+  a.grp = hq / hkv;
+  a.causal = 1;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  const size_t words = 2 * bitmap_words(n);  // full-block bitmap, then the partial-last-block one
+  std::vector<const int32_t*> vs_s;
+  std::vector<int32_t> vs_k;
+  std::vector<uint32_t*> vs_bits;
+  for (int h = 0; h < hq; ++h) {
+    if (plans[h].kind != MINF_KIND_VS) continue;
+    vs_s.push_back(plans[h].s_idx);
+    vs_k.push_back(plans[h].k_s);
+    vs_bits.push_back((uint32_t*)workspace + (size_t)h * words);
+  }
+  if (!vs_s.empty()) {
+    hipError_t e = launch_vs_offset_bits(vs_s.data(), vs_k.data(), vs_bits.data(), (int)vs_s.size(), (int)n, stream);
+    if (e != hipSuccess) return hip_fail(e, "VS offset bitmap kernel");
+  }
+  for (int h0 = 0; h0 < hq; h0 += kMaxLaunchHeads) {
+    const int nh = std::min(kMaxLaunchHeads, hq - h0);
+    for (int i = 0; i < nh; ++i) {
+      const minf_head_plan& p = plans[h0 + i];
+      AttnHead& d2 = a.heads[i];
+      d2 = AttnHead{};
+      d2.kind = p.kind;
+      d2.sink = p.sink;
+      d2.local = p.local;
+      d2.k_v = p.kind == MINF_KIND_VS ? p.k_v : 0;
+      d2.k_b = p.k_b;
+      d2.v_idx = p.v_idx;
+      d2.obits = p.kind == MINF_KIND_VS ? (const uint32_t*)workspace + (size_t)(h0 + i) * words : nullptr;
+      d2.blk_idx = p.blk_idx;
+      d2.blk_cnt = p.blk_cnt;
+    }
+    a.head0 = h0;
+    a.nh = nh;
+    hipError_t e = launch_attn(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
+  }
+  return MINF_OK;
+}
+
+minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t n, int hq,
+                            int hkv, int d, float scale, int causal, hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_attn_common(q, k, v, o, n, hq, hkv, d, scale, (int64_t)1 << 24)) != MINF_OK) return s;
+  AttnLaunch a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.n = (int)n;
+  a.nb = (int)nblocks(n);
+  a.hq = hq;
+  a.hkv = hkv;
+  a.grp = hq / hkv;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  for (int i = 0; i < kMaxLaunchHeads; ++i) a.heads[i] = AttnHead{};
+  return launch_all_heads(a, hq, stream);
+}
+
+}  // extern "C"

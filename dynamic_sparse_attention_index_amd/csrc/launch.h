@@ -1,0 +1,72 @@
+// Internal host-side launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace minf {
+
+constexpr int kMaxLaunchHeads = 32;  // heads described in one attention launch (kernel arguments)
+constexpr int kMaxVsGroups = 32;     // VS head groups in one index launch
+constexpr int64_t kMaxTokens = 1 << 20;  // largest n the in-LDS bitmaps cover (16384 blocks)
+
+struct AttnHead {
+  int32_t kind, sink, local, k_v, k_b, pad;
+  const int32_t* v_idx;    // VS: ascending columns
+  const uint32_t* obits;   // VS: bitmap of block offsets covered by the slashes
+  const int32_t* blk_idx;  // BLOCK
+  const int32_t* blk_cnt;  // BLOCK
+};
+
+struct AttnLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int32_t n, nb, hq, hkv, grp, head0, nh, causal;
+  float scale_log2;
+  AttnHead heads[kMaxLaunchHeads];
+};
+
+hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);
+hipError_t launch_vs_offset_bits(const int32_t* const* s_idx, const int32_t* k_s, uint32_t* const* bits,
+                                 int count, int n, hipStream_t stream);
+
+struct VsGroup {
+  int32_t kv;        // KV head of the group
+  int32_t cnt;       // query heads in the group (1..4)
+  int32_t head[4];   // query head ids
+  int32_t slot[4];   // output slots (position in the caller's head list)
+};
+
+struct VsLaunch {
+  const uint16_t* q;
+  const uint16_t* k;
+  int32_t n, r, ngroups, nchunks, tiles_per_chunk, ntiles, n_slots;
+  float scale_log2;
+  float* part_m;   // [n_slots][64][nchunks]
+  float* part_l;   // [n_slots][64][nchunks]
+  float* row_m;    // [n_slots][64]
+  float* row_il;   // [n_slots][64]
+  float* vcol;     // [n_slots][n]
+  float* slsum;    // [n_slots][n]
+  float* dpart;    // [n_slots][ntiles][128]
+  VsGroup groups[kMaxVsGroups];
+};
+
+hipError_t launch_vs_scores(const VsLaunch& a, hipStream_t stream);
+hipError_t launch_topk_rows(const float* src, int64_t src_stride, int rows, int n, int k, int32_t* dst,
+                            int64_t dst_stride, hipStream_t stream);
+
+// Pool heads[i] of x ([h][n][128] bf16) into slot slots[i] of out_rm ([slot][nb][128])
+// and/or out_t ([slot][128][nb]); either output may be null.
+hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, const int32_t* slots, int n_heads,
+                             float* out_rm, float* out_t, hipStream_t stream);
+// Scores and top-k for n_heads pooled query heads (qbar slots 0..n_heads-1), head i
+// reading pooled keys kbar_t slot kvslot[i]; writes blk_idx/blk_cnt slot i.
+hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
+                             int k_b, int32_t* blk_idx, int32_t* blk_cnt, hipStream_t stream);
+
+}  // namespace minf

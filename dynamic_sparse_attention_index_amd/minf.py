@@ -1,0 +1,246 @@
+"""Python binding of libminf.so: argument marshalling only.
+
+Each function has the name of the C entry point it calls. Tensors are torch
+tensors on the GPU (bf16 for Q/K/V/O, int32 for indices); outputs and
+workspaces are allocated with torch (device memory plumbing) unless the
+caller passes them in. Every step of the computation runs in the library's
+HIP kernels; there is no fallback path. Importing this module raises if the
+library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libminf.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "minf.h")
+
+MINF_OK = 0
+KIND = {"dense": 0, "ashape": 1, "vs": 2, "block": 3}
+
+
+class MinfError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name} ({status}): {detail}")
+        self.status = status
+        self.name = name
+        self.detail = detail
+
+
+class HeadPlan(ctypes.Structure):
+    """Mirror of minf_head_plan."""
+    _fields_ = [
+        ("kind", ctypes.c_int32),
+        ("sink", ctypes.c_int32),
+        ("local", ctypes.c_int32),
+        ("k_v", ctypes.c_int32),
+        ("k_s", ctypes.c_int32),
+        ("k_b", ctypes.c_int32),
+        ("v_idx", ctypes.c_void_p),
+        ("s_idx", ctypes.c_void_p),
+        ("blk_idx", ctypes.c_void_p),
+        ("blk_cnt", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m dynamic_sparse_attention_index_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    ip = ctypes.POINTER(ctypes.c_int32)
+    sigs = {
+        "minf_status_string": (ctypes.c_char_p, [i32]),
+        "minf_last_error_detail": (ctypes.c_char_p, []),
+        "minf_abi_version": (i32, []),
+        "minf_vs_index_workspace_size": (sz, [i64, i32]),
+        "minf_build_vs_index": (i32, [vp, vp, i64, i32, i32, i32, ip, i32, i32, i32, i32, f32, vp, vp, vp, sz, vp]),
+        "minf_vs_scores": (i32, [vp, vp, i64, i32, i32, i32, ip, i32, i32, f32, vp, vp, vp, sz, vp]),
+        "minf_block_index_workspace_size": (sz, [i64, i32, i32, i32]),
+        "minf_build_block_index": (i32, [vp, vp, i64, i32, i32, i32, ip, i32, i32, vp, vp, vp, sz, vp]),
+        "minf_block_pool": (i32, [vp, i64, i32, i32, ip, i32, vp, vp]),
+        "minf_sparse_attn_workspace_size": (sz, [i64, i32]),
+        "minf_sparse_attn": (i32, [vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, ctypes.POINTER(HeadPlan), vp, sz, vp]),
+        "minf_dense_attn": (i32, [vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, i32, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def header_functions() -> list:
+    """Names of the functions include/minf.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"\b(minf_[a-z_0-9]+)\s*\(", text)) - {"minf_head_plan"})
+
+
+def library():
+    return _lib
+
+
+def _check(status: int):
+    if status != MINF_OK:
+        name = _lib.minf_status_string(status).decode()
+        detail = _lib.minf_last_error_detail().decode()
+        raise MinfError(status, name, detail)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor on the GPU")
+
+
+def _heads_arr(heads):
+    heads = [int(h) for h in heads]
+    arr = (ctypes.c_int32 * max(1, len(heads)))(*heads)
+    return arr, len(heads)
+
+
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def minf_build_vs_index(q, k, heads, last_q=64, k_v=1000, k_s=6096, scale=None, workspace=None, stream=None):
+    """VS index for query heads `heads`: (v_idx [n_heads, min(k_v, n)], s_idx [n_heads, min(k_s, n)])."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    arr, nh = _heads_arr(heads)
+    kv_eff, ks_eff = min(k_v, n), min(k_s, n)
+    v_idx = torch.empty((nh, kv_eff), dtype=torch.int32, device=q.device)
+    s_idx = torch.empty((nh, ks_eff), dtype=torch.int32, device=q.device)
+    ws, wsb = _workspace(_lib.minf_vs_index_workspace_size(n, nh), q.device, workspace)
+    _check(_lib.minf_build_vs_index(_ptr(q), _ptr(k), n, hq, hkv, d, arr, nh, last_q, k_v, k_s, _scale(scale, d),
+                                    _ptr(v_idx), _ptr(s_idx), _ptr(ws), wsb, _stream(stream)))
+    return v_idx, s_idx
+
+
+def minf_vs_scores(q, k, heads, last_q=64, scale=None, workspace=None, stream=None):
+    """Column sums and diagonal sums of the last-query softmax: (v [n_heads, n], sl [n_heads, n])."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    arr, nh = _heads_arr(heads)
+    v = torch.empty((nh, n), dtype=torch.float32, device=q.device)
+    sl = torch.empty((nh, n), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(_lib.minf_vs_index_workspace_size(n, nh), q.device, workspace)
+    _check(_lib.minf_vs_scores(_ptr(q), _ptr(k), n, hq, hkv, d, arr, nh, last_q, _scale(scale, d), _ptr(v), _ptr(sl),
+                               _ptr(ws), wsb, _stream(stream)))
+    return v, sl
+
+
+def minf_build_block_index(q, k, heads, k_b=256, workspace=None, stream=None):
+    """Block index: (blk_idx [n_heads, n_b, k_b] padded with -1, blk_cnt [n_heads, n_b])."""
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    arr, nh = _heads_arr(heads)
+    nb = (n + 63) // 64
+    blk_idx = torch.empty((nh, nb, k_b), dtype=torch.int32, device=q.device)
+    blk_cnt = torch.empty((nh, nb), dtype=torch.int32, device=q.device)
+    ws, wsb = _workspace(_lib.minf_block_index_workspace_size(n, hq, hkv, nh), q.device, workspace)
+    _check(_lib.minf_build_block_index(_ptr(q), _ptr(k), n, hq, hkv, d, arr, nh, k_b, _ptr(blk_idx), _ptr(blk_cnt),
+                                       _ptr(ws), wsb, _stream(stream)))
+    return blk_idx, blk_cnt
+
+
+def minf_block_pool(x, heads, stream=None):
+    """64-row block means of x [h, n, d] for the listed heads: [n_heads, n_b, d] float32."""
+    _need(x, torch.bfloat16, "x")
+    h, n, d = x.shape
+    arr, nh = _heads_arr(heads)
+    out = torch.empty((nh, (n + 63) // 64, d), dtype=torch.float32, device=x.device)
+    _check(_lib.minf_block_pool(_ptr(x), n, h, d, arr, nh, _ptr(out), _stream(stream)))
+    return out
+
+
+def make_plans(plans):
+    """Convert per-head plan dicts into the C struct array (keeps tensor references alive)."""
+    arr = (HeadPlan * len(plans))()
+    keep = []
+    for h, p in enumerate(plans):
+        kind = p["kind"]
+        e = arr[h]
+        e.kind = KIND[kind]
+        if kind == "ashape":
+            e.sink, e.local = int(p["sink"]), int(p["local"])
+        elif kind == "vs":
+            vi, si = p["v_idx"], p["s_idx"]
+            for t, nm in ((vi, "v_idx"), (si, "s_idx")):
+                _need(t, torch.int32, nm)
+            e.k_v, e.k_s = vi.numel(), si.numel()
+            e.v_idx, e.s_idx = vi.data_ptr(), si.data_ptr()
+            keep += [vi, si]
+        elif kind == "block":
+            bi, bc = p["blk_idx"], p["blk_cnt"]
+            _need(bi, torch.int32, "blk_idx")
+            _need(bc, torch.int32, "blk_cnt")
+            e.k_b = bi.shape[-1]
+            e.blk_idx, e.blk_cnt = bi.data_ptr(), bc.data_ptr()
+            keep += [bi, bc]
+        elif kind != "dense":
+            raise ValueError(f"unknown plan kind {kind!r}")
+    return arr, keep
+
+
+def minf_sparse_attn(q, k, v, plans, scale=None, out=None, lse=None, with_lse=True, workspace=None, stream=None):
+    """Sparse attention over per-head plans: (o [hq, n, d] bf16, lse [hq, n] float32 or None)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, nm)
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    if len(plans) != hq:
+        raise ValueError("one plan per query head is required")
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and with_lse:
+        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
+    arr, keep = plans if isinstance(plans, tuple) else make_plans(plans)
+    ws, wsb = _workspace(_lib.minf_sparse_attn_workspace_size(n, hq), q.device, workspace)
+    _check(_lib.minf_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, hq, hkv, d, _scale(scale, d), arr,
+                                 _ptr(ws), wsb, _stream(stream)))
+    del keep
+    return o, lse
+
+
+def minf_dense_attn(q, k, v, scale=None, causal=True, out=None, lse=None, with_lse=True, stream=None):
+    """Dense FlashAttention baseline: (o [hq, n, d] bf16, lse [hq, n] float32 or None)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, nm)
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    o = torch.empty_like(q) if out is None else out
+    if lse is None and with_lse:
+        lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
+    _check(_lib.minf_dense_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, hq, hkv, d, _scale(scale, d),
+                                1 if causal else 0, _stream(stream)))
+    return o, lse

@@ -1,0 +1,188 @@
+/*
+ * minf.h - C ABI of the MI355X (gfx950) dynamic sparse attention library.
+ *
+ * The library implements the online half of MInference-style sparse prefill
+ * for causal attention: per-head index construction (Vertical-Slash,
+ * Block-Sparse; A-shape needs none) and a sparse FlashAttention that computes
+ * only the selected 64x64 key blocks and gathered key columns, plus a dense
+ * causal FlashAttention used as the baseline.
+ *
+ * Sources (web pages): "MInference 1.0 article: million-token inference on a
+ * single A100", sections "Method" and "Latency and sparse patterns in
+ * kernels" (Fig. 3, Fig. 4); "KV-cache-centric efficient long-context
+ * methods" talk transcript, section "KV-cache-centric methods" (MInference
+ * and the three-step dynamic-sparse framework); the MInference abstract on
+ * the authors' page (pattern fixed offline, sparse index built online from
+ * the pattern, sparse kernels use the pattern and index).
+ *
+ * Conventions for every call:
+ *  - Tensors are device pointers. bf16 tensors are passed as raw 16-bit
+ *    storage. Q and O are [hq][n][d], K and V are [hkv][n][d], row-major and
+ *    contiguous. d must be 128 (otherwise MINF_E_UNSUPPORTED).
+ *  - GQA: query head h reads KV head h / (hq / hkv); hq % hkv == 0.
+ *  - The caller owns every buffer (inputs, outputs, workspace). The library
+ *    allocates nothing and keeps no pointer after a call returns.
+ *  - Work is enqueued on `stream` and the call returns after enqueue; results
+ *    are valid once the stream has reached that point. There is no hidden
+ *    device synchronisation.
+ *  - Arguments are validated before any launch; a failed validation returns
+ *    a status and launches nothing. A HIP launch error returns MINF_E_HIP;
+ *    minf_last_error_detail() then holds the HIP error text (thread-local).
+ *  - Budgets larger than what exists are clamped ("full budget").
+ *  - Identical inputs give bitwise-identical outputs and indices (no float
+ *    atomics; every reduction has a fixed order).
+ *  - Softmax scale: the pages never state it; callers normally pass
+ *    1/sqrt(d). A scale <= 0 or non-finite is rejected.
+ */
+#ifndef MINF_H
+#define MINF_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int minf_status;
+#define MINF_OK 0
+#define MINF_E_INVALID_ARG 1 /* null pointer, bad size, bad head list, ... */
+#define MINF_E_UNSUPPORTED 2 /* valid request this build does not implement (d != 128, last_q > 64) */
+#define MINF_E_WORKSPACE 3   /* workspace pointer null or smaller than required */
+#define MINF_E_HIP 4         /* a HIP runtime call or launch failed */
+
+/* Human-readable name of a status code. Never returns NULL. */
+const char* minf_status_string(minf_status s);
+
+/* Detail text of the last failure on the calling thread ("" if none). */
+const char* minf_last_error_detail(void);
+
+/* Library ABI version (incremented when a signature or struct changes). */
+int minf_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Vertical-Slash index ("Method": the attention between the last queries and
+ * all keys estimates the best vertical and slash indices).
+ *
+ * For each listed query head h (KV head g = h / (hq/hkv)), with
+ * r = min(last_q, n) and rows I = [n - r, n):
+ *   P[i][j] = softmax over j <= i of scale * q_i . k_j        (i in I)
+ *   v[j]    = sum_i P[i][j]                 (column sums)
+ *   sl[dl]  = sum_i P[i][i - dl]            (diagonal sums, dl = i - j >= 0)
+ *   v_idx   = top-min(k_v, n) of v,  s_idx = top-min(k_s, n) of sl,
+ *   ties to the lower index, each list sorted ascending.
+ *
+ * heads    host array of n_heads distinct query head ids in [0, hq).
+ * last_q   1..64 (MINF_E_UNSUPPORTED above 64).
+ * v_idx    device int32 [n_heads][min(k_v, n)]  ascending column ids.
+ * s_idx    device int32 [n_heads][min(k_s, n)]  ascending diagonal offsets.
+ * workspace / ws_bytes  device scratch of at least
+ *          minf_vs_index_workspace_size(n, n_heads) bytes, 256-byte aligned.
+ * k_v, k_s >= 0 (0 gives an empty list).
+ * ---------------------------------------------------------------------- */
+size_t minf_vs_index_workspace_size(int64_t n, int n_heads);
+minf_status minf_build_vs_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                const int32_t* heads, int n_heads, int last_q, int k_v, int k_s,
+                                float scale, int32_t* v_idx, int32_t* s_idx, void* workspace,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Debug export of the VS estimate before top-k: v_out and sl_out are device
+ * float [n_heads][n] (column sums and diagonal sums as defined above). Same
+ * arguments, workspace size and errors as minf_build_vs_index. */
+minf_status minf_vs_scores(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                           const int32_t* heads, int n_heads, int last_q, float scale,
+                           float* v_out, float* sl_out, void* workspace, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Block-Sparse index ("Method": mean pooling of Q and K over 64-token blocks,
+ * and its commutativity with the matrix product, estimate the block index).
+ *
+ * For each listed query head h, with n_b = ceil(n / 64):
+ *   Qbar[b] = mean of q_i over block b, Kbar[c] likewise (a partial last
+ *   block averages its own rows); score(b, c) = Qbar[b] . Kbar[c], c <= b;
+ *   row b keeps the top-min(k_b, b+1) blocks c, ties to the lower c.
+ *
+ * blk_idx  device int32 [n_heads][n_b][k_b], ascending, padded with -1.
+ * blk_cnt  device int32 [n_heads][n_b] = min(k_b, b + 1).
+ * workspace / ws_bytes  at least minf_block_index_workspace_size(n, hq, hkv, n_heads).
+ * k_b >= 1.
+ * ---------------------------------------------------------------------- */
+size_t minf_block_index_workspace_size(int64_t n, int hq, int hkv, int n_heads);
+minf_status minf_build_block_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                   const int32_t* heads, int n_heads, int k_b, int32_t* blk_idx,
+                                   int32_t* blk_cnt, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* Debug export of the pooling step: out is device float [n_heads][n_b][d],
+ * the 64-row block means of x ([h_total][n][d] bf16) for the listed heads. */
+minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const int32_t* heads,
+                            int n_heads, float* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse FlashAttention ("Latency and sparse patterns in kernels", Fig. 4:
+ * verticals as 1x64 pieces, slashes as 64x64 blocks; talk transcript:
+ * blockwise sparse computation on top of FlashAttention).
+ *
+ * One plan per query head. With b = floor(i / 64), the set of keys row i
+ * attends to is:
+ *   MINF_KIND_DENSE  : j <= i.
+ *   MINF_KIND_ASHAPE : j <= i and (j < sink or i - j < local).
+ *   MINF_KIND_VS     : j <= i and (block(j) in Bs(b) or j in v_idx), where
+ *                      Bs(b) = { floor((i' - dl) / 64) : i' in block b,
+ *                      dl in s_idx, i' - dl >= 0 } (slash lines covered by
+ *                      whole 64x64 blocks).
+ *   MINF_KIND_BLOCK  : j <= i and block(j) in blk_idx[b][0 .. blk_cnt[b]).
+ * O_i = softmax over that set of scale * q_i . k_j, applied to V (fp32
+ * online softmax and accumulation, bf16 MFMA products, bf16 output). An
+ * empty set gives O_i = 0 and LSE_i = -inf.
+ *
+ * o    device bf16 [hq][n][d].   lse  device float [hq][n] or NULL
+ *      (natural-log sum of exponentials of the scaled scores over the set).
+ * plans host array [hq]; index pointers inside it are device pointers that
+ *      must stay valid until the stream reaches the call. v_idx entries must
+ *      be ascending and unique; s_idx entries are offsets in [0, n); blk_idx
+ *      rows ascending with -1 padding. Out-of-range entries are ignored.
+ * workspace / ws_bytes  at least minf_sparse_attn_workspace_size(n, hq).
+ * ---------------------------------------------------------------------- */
+#define MINF_KIND_DENSE 0
+#define MINF_KIND_ASHAPE 1
+#define MINF_KIND_VS 2
+#define MINF_KIND_BLOCK 3
+
+typedef struct minf_head_plan {
+  int32_t kind;           /* MINF_KIND_* */
+  int32_t sink;           /* A-shape: sink tokens (>= 0) */
+  int32_t local;          /* A-shape: local window tokens (>= 0) */
+  int32_t k_v;            /* VS: entries in v_idx (>= 0) */
+  int32_t k_s;            /* VS: entries in s_idx (>= 0) */
+  int32_t k_b;            /* BLOCK: row stride of blk_idx (>= 1) */
+  const int32_t* v_idx;   /* VS: device, ascending column ids */
+  const int32_t* s_idx;   /* VS: device, diagonal offsets */
+  const int32_t* blk_idx; /* BLOCK: device [n_b][k_b] */
+  const int32_t* blk_cnt; /* BLOCK: device [n_b] */
+} minf_head_plan;
+
+size_t minf_sparse_attn_workspace_size(int64_t n, int hq);
+minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t n, int hq, int hkv, int d, float scale,
+                             const minf_head_plan* plans, void* workspace, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* Dense FlashAttention baseline (the comparison kernel of Fig. 3).
+ * causal != 0: row i attends to j <= i; causal == 0: to every j < n.
+ * Same layouts as minf_sparse_attn; needs no workspace. */
+minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int64_t n, int hq, int hkv, int d, float scale, int causal,
+                            hipStream_t stream);
+
+/* Number of 64x64 key blocks and gathered key columns the last minf_sparse_attn
+ * / minf_dense_attn launch on this thread was planned to compute is not kept;
+ * callers count work from the index themselves. */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MINF_H */

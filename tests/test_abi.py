@@ -1,0 +1,134 @@
+"""The C ABI library loads, exports what include/minf.h declares, and rejects
+bad arguments with exact status codes before any launch (CPU only: every case
+here fails validation, so no device pointer is ever dereferenced)."""
+import ctypes
+import math
+
+import pytest
+
+from dynamic_sparse_attention_index_amd import minf
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: each call below fails validation first
+LIB = minf.library()
+
+
+def _heads(*h):
+    return (ctypes.c_int32 * max(1, len(h)))(*h), len(h)
+
+
+def test_exports_every_declared_function():
+    names = minf.header_functions()
+    assert {"minf_build_vs_index", "minf_build_block_index", "minf_sparse_attn", "minf_dense_attn"} <= set(names)
+    for name in names:
+        assert hasattr(LIB, name), name
+
+
+def test_status_strings():
+    assert LIB.minf_status_string(OK) == b"MINF_OK"
+    assert LIB.minf_status_string(INVALID) == b"MINF_E_INVALID_ARG"
+    assert LIB.minf_status_string(UNSUPPORTED) == b"MINF_E_UNSUPPORTED"
+    assert LIB.minf_status_string(WORKSPACE) == b"MINF_E_WORKSPACE"
+    assert LIB.minf_status_string(HIP) == b"MINF_E_HIP"
+    assert LIB.minf_status_string(99) == b"MINF_E_UNKNOWN"
+    assert LIB.minf_abi_version() == 1
+
+
+def test_workspace_sizes():
+    assert LIB.minf_vs_index_workspace_size(0, 1) == 0
+    a = LIB.minf_vs_index_workspace_size(4096, 1)
+    b = LIB.minf_vs_index_workspace_size(4096, 2)
+    c = LIB.minf_vs_index_workspace_size(8192, 2)
+    assert 0 < a < b < c and a % 256 == 0
+    # at least the column and diagonal sums of every head
+    assert b >= 2 * 2 * 4096 * 4
+    assert LIB.minf_block_index_workspace_size(4096, 8, 8, 4) >= (4 + 4) * 64 * 128 * 4
+    assert LIB.minf_sparse_attn_workspace_size(1 << 20, 32) >= 32 * (16384 // 32) * 4
+
+
+def _dense(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, n=128, hq=2, hkv=1, d=128, scale=0.1, causal=1)
+    a.update(kw)
+    return LIB.minf_dense_attn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["n"], a["hq"], a["hkv"], a["d"],
+                               a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(v=None), INVALID), (dict(o=None), INVALID),
+    (dict(n=0), INVALID), (dict(hq=3, hkv=2), INVALID), (dict(hkv=0), INVALID),
+    (dict(d=64), UNSUPPORTED), (dict(scale=0.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(n=(1 << 24) + 1), UNSUPPORTED),
+])
+def test_dense_rejects(kw, code):
+    assert _dense(**kw) == code
+    assert LIB.minf_last_error_detail() != b""
+
+
+def _vs(heads=(0,), ws=FAKE, ws_bytes=None, **kw):
+    a = dict(q=FAKE, k=FAKE, n=4096, hq=2, hkv=1, d=128, last_q=64, k_v=8, k_s=8, scale=0.1, v=FAKE, s=FAKE)
+    a.update(kw)
+    arr, nh = _heads(*heads)
+    if ws_bytes is None:
+        ws_bytes = LIB.minf_vs_index_workspace_size(a["n"], nh)
+    return LIB.minf_build_vs_index(a["q"], a["k"], a["n"], a["hq"], a["hkv"], a["d"], arr, nh, a["last_q"], a["k_v"],
+                                   a["k_s"], a["scale"], a["v"], a["s"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(last_q=65), UNSUPPORTED), (dict(last_q=0), INVALID), (dict(k_v=-1), INVALID), (dict(k_s=-2), INVALID),
+    (dict(heads=(0, 0)), INVALID), (dict(heads=(2,)), INVALID), (dict(heads=(-1,)), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=1024), WORKSPACE), (dict(ws=ctypes.c_void_p(0x10004)), WORKSPACE),
+    (dict(v=None), INVALID), (dict(n=(1 << 20) + 64), UNSUPPORTED), (dict(d=256), UNSUPPORTED),
+    (dict(k=None), INVALID),
+])
+def test_vs_index_rejects(kw, code):
+    assert _vs(**kw) == code
+
+
+def test_block_index_rejects():
+    arr, nh = _heads(0)
+    ws = LIB.minf_block_index_workspace_size(4096, 2, 1, 1)
+    call = lambda **kw: LIB.minf_build_block_index(  # noqa: E731
+        kw.get("q", FAKE), FAKE, kw.get("n", 4096), 2, 1, 128, arr, nh, kw.get("k_b", 16), kw.get("idx", FAKE), FAKE,
+        kw.get("ws", FAKE), kw.get("wsb", ws), None)
+    assert call(k_b=0) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=16) == WORKSPACE
+    assert call(q=None) == INVALID
+    assert call(n=0) == INVALID
+
+
+def _plans(*specs):
+    arr = (minf.HeadPlan * len(specs))()
+    for e, s in zip(arr, specs):
+        for key, val in s.items():
+            setattr(e, key, val)
+    return arr
+
+
+def _sparse(plans, ws=FAKE, n=4096, hq=2):
+    return LIB.minf_sparse_attn(FAKE, FAKE, FAKE, FAKE, None, n, hq, 1, 128, 0.1, plans, ws,
+                                LIB.minf_sparse_attn_workspace_size(n, hq), None)
+
+
+def test_sparse_attn_rejects():
+    assert _sparse(None) == INVALID
+    assert _sparse(_plans(dict(kind=7), dict(kind=0))) == INVALID
+    assert _sparse(_plans(dict(kind=1, sink=-1), dict(kind=0))) == INVALID
+    assert _sparse(_plans(dict(kind=2, k_v=4), dict(kind=0))) == INVALID  # null v_idx
+    assert _sparse(_plans(dict(kind=2, k_s=4, s_idx=0x10000), dict(kind=0)), ws=None) == WORKSPACE
+    assert _sparse(_plans(dict(kind=3, k_b=0), dict(kind=0))) == INVALID
+    assert _sparse(_plans(dict(kind=3, k_b=4), dict(kind=0))) == INVALID  # null blk_idx
+    assert _sparse(_plans(dict(kind=0), dict(kind=0)), n=(1 << 20) + 1) == UNSUPPORTED
+    assert b"kind" in LIB.minf_last_error_detail() or LIB.minf_last_error_detail() != b""
+
+
+def test_python_binding_names_match_c():
+    for name in ("minf_build_vs_index", "minf_build_block_index", "minf_sparse_attn", "minf_dense_attn",
+                 "minf_vs_scores", "minf_block_pool"):
+        assert callable(getattr(minf, name))
+
+
+def test_default_scale():
+    assert minf._scale(None, 128) == pytest.approx(1 / math.sqrt(128))

@@ -1,0 +1,237 @@
+"""GPU path (through the C ABI) against the CPU oracle, element by element.
+
+Sizes span several 64x64 tiles and a ragged tail; the oracle finishes each in
+seconds. Bars: index sets exact under the margin rule (tests/parity.py);
+bf16 attention outputs within max-abs 2e-2 of the fp64 oracle; LSE within
+2e-3; repeated runs bitwise identical.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity import check_lse, check_topk, max_abs, to_np
+from workload import injected_vs_index, planted_qkv
+
+pytestmark = pytest.mark.gpu
+OUT_TOL = 2e-2
+SCALE = 1 / math.sqrt(128)
+
+
+def _qkv(n, hq, hkv, seed, **kw):
+    print(f"[case] n={n} hq={hq} hkv={hkv} seed={seed} {kw}", flush=True)
+    return planted_qkv(n, hq, hkv, seed=seed, device="cuda", **kw)
+
+
+def _np_plans(plans):
+    out = []
+    for p in plans:
+        q = dict(kind=p["kind"])
+        for key in ("sink", "local"):
+            if key in p:
+                q[key] = p[key]
+        for key in ("v_idx", "s_idx", "blk_idx", "blk_cnt"):
+            if key in p:
+                q[key] = p[key].cpu().numpy().astype(np.int64)
+        out.append(q)
+    return out
+
+
+def _attn_parity(minf, q, k, v, plans, rows=None, tol=OUT_TOL):
+    hq = q.shape[0]
+    o, lse = minf.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    torch.cuda.synchronize()
+    want_o, want_l = O.sparse_attn(to_np(q), to_np(k), to_np(v), hq, k.shape[0], SCALE, _np_plans(plans), rows=rows)
+    got_o = to_np(o) if rows is None else to_np(o)[:, rows]
+    got_l = to_np(lse) if rows is None else to_np(lse)[:, rows]
+    err = max_abs(got_o, want_o)
+    print(f"  max-abs err {err:.3e}", flush=True)
+    assert err <= tol
+    check_lse(got_l, want_l)
+    return o, lse
+
+
+@pytest.mark.parametrize("n,hq,hkv", [(64, 1, 1), (200, 2, 1), (1000, 4, 2), (4160, 2, 2), (1, 1, 1), (65, 2, 2)])
+def test_dense_causal(gpu_lib, n, hq, hkv):
+    q, k, v, _ = _qkv(n, hq, hkv, 11)
+    o, lse = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE)
+    torch.cuda.synchronize()
+    wo, wl = O.dense_attn(to_np(q), to_np(k), to_np(v), hq, hkv, SCALE)
+    assert max_abs(to_np(o), wo) <= OUT_TOL
+    check_lse(to_np(lse), wl)
+
+
+@pytest.mark.parametrize("n", [200, 1000])
+def test_dense_noncausal(gpu_lib, n):
+    q, k, v, _ = _qkv(n, 2, 1, 12)
+    o, lse = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE, causal=False)
+    torch.cuda.synchronize()
+    wo, wl = O.dense_attn(to_np(q), to_np(k), to_np(v), 2, 1, SCALE, causal=False)
+    assert max_abs(to_np(o), wo) <= OUT_TOL
+    check_lse(to_np(lse), wl)
+
+
+@pytest.mark.parametrize("n,sink,local", [(3000, 64, 1024), (1000, 10, 70), (777, 0, 100), (513, 130, 1), (300, 512, 64)])
+def test_ashape(gpu_lib, n, sink, local):
+    q, k, v, _ = _qkv(n, 2, 1, 13)
+    plans = [dict(kind="ashape", sink=sink, local=local)] * 2
+    _attn_parity(gpu_lib, q, k, v, plans)
+
+
+def test_dense_plan_equals_dense_call(gpu_lib):
+    q, k, v, _ = _qkv(1000, 2, 1, 14)
+    o1, l1 = gpu_lib.minf_sparse_attn(q, k, v, [dict(kind="dense")] * 2, scale=SCALE)
+    o2, l2 = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("n,k_b", [(2000, 5), (4096, 16), (1000, 100)])
+def test_block_index_and_attention(gpu_lib, n, k_b):
+    hq, hkv = 4, 2
+    q, k, v, _ = _qkv(n, hq, hkv, 15)
+    heads = [1, 2, 3]
+    bi, bc = gpu_lib.minf_build_block_index(q, k, heads, k_b=k_b)
+    torch.cuda.synchronize()
+    wi, wc, scores = O.build_block_index(to_np(q), to_np(k), hq, hkv, heads, k_b)
+    assert np.array_equal(bc.cpu().numpy(), wc)
+    qn, kn = to_np(q), to_np(k)
+    exact = amb = 0
+    for t, h in enumerate(heads):
+        qbar = O.pool_blocks(qn[h])
+        kbar = O.pool_blocks(kn[h // 2])
+        for b in range(wi.shape[1]):
+            c = int(wc[t, b])
+            row = scores[t][b, : b + 1]
+            abs_tol = 1e-5 * float(np.abs(qbar[b]) @ np.abs(kbar[: b + 1]).max(axis=0))
+            got = bi[t, b, :c].cpu().numpy()
+            if check_topk(row, got, k_b, abs_tol=abs_tol, want=wi[t, b, :c]):
+                exact += 1
+            else:
+                amb += 1
+            assert (bi[t, b, c:].cpu().numpy() == -1).all()
+    print(f"  block rows exact {exact}, ambiguous {amb}")
+    # attention over the GPU-built index
+    plans = [dict(kind="dense")] + [dict(kind="block", blk_idx=bi[t].contiguous(), blk_cnt=bc[t].contiguous())
+                                    for t in range(3)]
+    _attn_parity(gpu_lib, q, k, v, plans)
+
+
+def test_block_pool(gpu_lib):
+    n = 64 * 7 + 9
+    q, k, v, _ = _qkv(n, 3, 3, 16)
+    got = gpu_lib.minf_block_pool(q, [2, 0]).cpu().numpy()
+    qn = to_np(q)
+    for t, h in enumerate([2, 0]):
+        want = O.pool_blocks(qn[h])
+        assert np.max(np.abs(got[t] - want)) <= 1e-5 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.parametrize("n,last_q", [(4096, 64), (1000, 64), (130, 64), (64, 64), (4096 + 37, 17), (40, 64)])
+def test_vs_scores(gpu_lib, n, last_q):
+    hq, hkv = 4, 2
+    q, k, v, _ = _qkv(n, hq, hkv, 17)
+    heads = [0, 1, 3]
+    gv, gs = gpu_lib.minf_vs_scores(q, k, heads, last_q=last_q, scale=SCALE)
+    torch.cuda.synchronize()
+    _, _, wv, ws = O.build_vs_index(to_np(q), to_np(k), hq, hkv, heads, last_q, 1, 1, SCALE)
+    r = min(last_q, n)
+    for t in range(3):
+        assert np.max(np.abs(gv[t].cpu().numpy() - wv[t])) <= 1e-6 + 1e-4 * wv[t].max()
+        assert np.max(np.abs(gs[t].cpu().numpy() - ws[t])) <= 1e-6 + 1e-4 * ws[t].max()
+        assert abs(float(gv[t].double().sum()) - r) < 1e-3 and abs(float(gs[t].double().sum()) - r) < 1e-3
+
+
+@pytest.mark.parametrize("n,k_v,k_s", [(4096, 64, 64), (4096, 8, 4), (2000, 100, 30), (300, 500, 500), (4096, 0, 3)])
+def test_vs_index(gpu_lib, n, k_v, k_s):
+    q, k, v, info = _qkv(n, 2, 1, 18)
+    heads = [0, 1]
+    gvi, gsi = gpu_lib.minf_build_vs_index(q, k, heads, last_q=64, k_v=k_v, k_s=k_s, scale=SCALE)
+    torch.cuda.synchronize()
+    wvi, wsi, wv, ws = O.build_vs_index(to_np(q), to_np(k), 2, 1, heads, 64, k_v, k_s, SCALE)
+    for t in range(2):
+        check_topk(wv[t], gvi[t].cpu().numpy(), k_v, abs_tol=1e-7, want=wvi[t])
+        check_topk(ws[t], gsi[t].cpu().numpy(), k_s, abs_tol=1e-7, want=wsi[t])
+
+
+def test_vs_index_c1_exact_and_planted(gpu_lib):
+    # 1 head, N = 4096, last_q = 64, k_v = k_s = 64, calibrated plant (7, 14)
+    q, k, v, info = _qkv(4096, 1, 1, 1000)
+    gvi, gsi = gpu_lib.minf_build_vs_index(q, k, [0], last_q=64, k_v=64, k_s=64, scale=SCALE)
+    torch.cuda.synchronize()
+    wvi, wsi, wv, ws = O.build_vs_index(to_np(q), to_np(k), 1, 1, [0], 64, 64, 64, SCALE)
+    assert check_topk(wv[0], gvi[0].cpu().numpy(), 64, want=wvi[0])  # unambiguous on this seed
+    assert check_topk(ws[0], gsi[0].cpu().numpy(), 64, want=wsi[0])
+    assert set(info.columns[0]) <= set(gvi[0].cpu().tolist())
+    assert set(info.offsets) <= set(gsi[0].cpu().tolist())
+
+
+@pytest.mark.parametrize("n,k_v,k_s", [(4096, 64, 64), (3000, 200, 100), (1000, 1000, 0), (777, 5, 777), (2500, 1500, 40)])
+def test_vs_attention_gpu_index(gpu_lib, n, k_v, k_s):
+    hq, hkv = 2, 1
+    q, k, v, _ = _qkv(n, hq, hkv, 19)
+    vi, si = gpu_lib.minf_build_vs_index(q, k, [0, 1], last_q=64, k_v=k_v, k_s=k_s, scale=SCALE)
+    plans = [dict(kind="vs", v_idx=vi[t].contiguous(), s_idx=si[t].contiguous()) for t in range(2)]
+    _attn_parity(gpu_lib, q, k, v, plans)
+
+
+@pytest.mark.parametrize("n", [4096, 8192 + 100])
+def test_vs_attention_injected_local(gpu_lib, n):
+    # local slashes [0, k_s) and scattered verticals: the gather path at a high column count
+    q, k, v, info = _qkv(n, 2, 2, 20)
+    plans = []
+    for h in range(2):
+        vi, si = injected_vs_index(n, 600, 200 + 300 * h, info.columns[h], info.offsets, seed=21 + h)
+        plans.append(dict(kind="vs", v_idx=vi.cuda(), s_idx=si.cuda()))
+    _attn_parity(gpu_lib, q, k, v, plans)
+
+
+def test_vs_empty_rows(gpu_lib):
+    n = 300
+    q, k, v, _ = _qkv(n, 2, 1, 22)
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    plans = [dict(kind="vs", v_idx=e, s_idx=e),
+             dict(kind="vs", v_idx=e, s_idx=torch.tensor([64], dtype=torch.int32, device="cuda"))]
+    o, lse = _attn_parity(gpu_lib, q, k, v, plans)
+    assert (o[0] == 0).all() and torch.isneginf(lse[0]).all()
+    assert (o[1, :64] == 0).all() and torch.isneginf(lse[1, :64]).all()
+
+
+@pytest.mark.parametrize("n", [200, 2048 + 64])
+def test_full_budgets_match_dense(gpu_lib, n):
+    q, k, v, _ = _qkv(n, 4, 2, 23)
+    nb = (n + 63) // 64
+    vi, si = gpu_lib.minf_build_vs_index(q, k, [0], last_q=64, k_v=n, k_s=n, scale=SCALE)
+    bi, bc = gpu_lib.minf_build_block_index(q, k, [1], k_b=nb)
+    plans = [dict(kind="vs", v_idx=vi[0].contiguous(), s_idx=si[0].contiguous()),
+             dict(kind="block", blk_idx=bi[0].contiguous(), blk_cnt=bc[0].contiguous()),
+             dict(kind="ashape", sink=0, local=n), dict(kind="ashape", sink=n, local=0)]
+    o, lse = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    torch.cuda.synchronize()
+    wo, wl = O.dense_attn(to_np(q), to_np(k), to_np(v), 4, 2, SCALE)
+    assert max_abs(to_np(o), wo) <= OUT_TOL
+    check_lse(to_np(lse), wl)
+
+
+def test_mixed_heads_gqa_and_determinism(gpu_lib):
+    n, hq, hkv = 2048 + 77, 8, 2
+    q, k, v, info = _qkv(n, hq, hkv, 24)
+    vi, si = gpu_lib.minf_build_vs_index(q, k, [0, 3, 5], last_q=64, k_v=100, k_s=150, scale=SCALE)
+    bi, bc = gpu_lib.minf_build_block_index(q, k, [1, 6], k_b=8)
+    plans = [None] * hq
+    for t, h in enumerate([0, 3, 5]):
+        plans[h] = dict(kind="vs", v_idx=vi[t].contiguous(), s_idx=si[t].contiguous())
+    for t, h in enumerate([1, 6]):
+        plans[h] = dict(kind="block", blk_idx=bi[t].contiguous(), blk_cnt=bc[t].contiguous())
+    plans[2] = dict(kind="ashape", sink=64, local=256)
+    plans[4] = dict(kind="dense")
+    plans[7] = dict(kind="ashape", sink=3, local=1000)
+    o1, l1 = _attn_parity(gpu_lib, q, k, v, plans)
+    o2, l2 = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    vi2, si2 = gpu_lib.minf_build_vs_index(q, k, [0, 3, 5], last_q=64, k_v=100, k_s=150, scale=SCALE)
+    bi2, bc2 = gpu_lib.minf_build_block_index(q, k, [1, 6], k_b=8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(vi, vi2) and torch.equal(si, si2) and torch.equal(bi, bi2) and torch.equal(bc, bc2)
