@@ -1,0 +1,381 @@
+"""Benchmark: one sparse-prefill attention layer (index build + sparse attention).
+
+Default workload: the 32-query-head / 8-KV-head GQA layer at N = 1,048,576
+tokens, every head Vertical-Slash (1000 verticals, 6096 slashes, last 64
+queries), bf16 inputs seeded and planted (see workload/gen.py). A step is the
+whole hot path for the layer: the VS index of all 32 heads built from the
+data, then sparse attention over it. Inputs are resident in HBM before timing.
+
+Printed (one JSON line): latency per layer, the attention kernel's achieved
+MFMA TFLOP/s over the blocks and columns it computes against the bf16 peak,
+the in-house dense causal FlashAttention on the same inputs (speedup), an
+index-injected track with the pages' local-slash structure, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+BLOCK_FLOP = 4 * 64 * 64 * 128   # QK^T and PV of one 64x64 block, d = 128
+COL_FLOP = 4 * 64 * 128          # one gathered key column for a 64-row query block
+METRIC = "sparse prefill attn latency/layer at 128K–1M tok; MFMA util; speedup vs dense"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c5_gqa_1m_vs")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-injected", action="store_true")
+    ap.add_argument("--dense-runs", type=int, default=1)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- work accounting
+def vs_work(v_idx, s_idx, n):
+    """(computed 64x64 blocks, gathered columns) of one VS head, summed over query blocks."""
+    import torch
+    nb = (n + 63) // 64
+    dev = v_idx.device
+    dl = s_idx.long()
+    off = torch.zeros(nb + 1, dtype=torch.bool, device=dev)
+    q = dl // 64
+    off[q] = True
+    rho = dl % 64
+    off[(q + 1)[rho > 0].clamp(max=nb)] = True
+    off = off[:nb]
+    blocks = int(torch.cumsum(off.long(), 0).sum())  # sum over b of |{o in O : o <= b}|
+    cb = (v_idx.long() // 64)
+    cols = 0
+    bs = torch.arange(nb, device=dev)
+    for part in torch.split(bs, 2048):
+        rel = part[:, None] - cb[None, :]
+        ok = rel >= 0
+        hit = off[rel.clamp(min=0)]
+        cols += int((ok & ~hit).sum())
+    return blocks, cols
+
+
+def ashape_blocks(n, sink, local):
+    nb = (n + 63) // 64
+    sb = min((sink + 63) // 64, nb)
+    tot = 0
+    for b in range(nb):
+        lo = max(0, (64 * b - local + 1) // 64) if local > 0 else b + 1
+        tot += len(set(range(min(sb, b + 1))) | set(range(lo, b + 1)))
+    return tot
+
+
+# ---------------------------------------------------------------- CPU oracle sample
+def cpu_baseline(q, k, v, kinds, cfg, plans_gpu, n, blocks_per_head):
+    """Time the fp64 oracle on a bounded sample and scale it to one layer."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    scale = 1 / math.sqrt(128)
+    h = kinds.index("vs") if "vs" in kinds else 0
+    g = h // (cfg["hq"] // cfg["hkv"])
+    qh = q[h].float().cpu().numpy()
+    kg = k[g].float().cpu().numpy()
+    vg = v[g].float().cpu().numpy()
+    t0 = time.perf_counter()
+    reps = 0
+    while kinds[h] == "vs" and (reps == 0 or time.perf_counter() - t0 < 3.0):
+        O.vs_index(qh, kg, cfg["last_q"], cfg["k_v"], cfg["k_s"], scale)
+        reps += 1
+    t_index = (time.perf_counter() - t0) / max(reps, 1)
+    nb = (n + 63) // 64
+    rng = np.random.default_rng(0)
+    # first, last and 14 seeded query blocks (about 10-20 s of CPU work at 1M tokens)
+    mid = rng.choice(np.arange(1, nb - 1), size=min(14, max(nb - 2, 0)), replace=False).tolist()
+    sample_blocks = sorted({0, nb - 1, *mid})
+    p = plans_gpu[h]
+    plan = {key: (val.cpu().numpy() if hasattr(val, "cpu") else val) for key, val in p.items()}
+    t0 = time.perf_counter()
+    for b in sample_blocks:
+        rows = np.arange(64 * b, min(64 * b + 64, n))
+        O.sparse_attn(qh[None], kg[None], vg[None], 1, 1, scale, [plan], rows=rows)
+    t_attn = time.perf_counter() - t0
+    # scale: index cost per VS head; attention cost per query block of the layer
+    n_vs = sum(1 for x in kinds if x == "vs")
+    layer_s = t_index * n_vs + (t_attn / len(sample_blocks)) * nb * len(kinds)
+    return {
+        "value": layer_s * 1e3,
+        "unit": "ms/layer (extrapolated)",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: VS index of 1 head at N={n} ({t_index:.1f} s per head) and sparse attention "
+                   f"of {len(sample_blocks)} query blocks of that head ({t_attn:.1f} s); scaled to {n_vs} "
+                   f"VS-index heads and {nb} query blocks x {len(kinds)} heads"),
+        "sample_seconds": round(t_index * max(reps, 1) + t_attn, 2),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                                   "(heads shard across GPUs without exchange; see DESIGN.md)"}))
+        sys.exit(2)
+    import torch
+
+    from dynamic_sparse_attention_index_amd import minf
+    from workload import CONFIGS, config_kinds, injected_vs_index, planted_qkv
+
+    torch.cuda.set_device(0)
+    cfg = CONFIGS[args.config]
+    n, hq, hkv = cfg["n"], cfg["hq"], cfg["hkv"]
+    kinds = config_kinds(args.config)
+    scale = 1 / math.sqrt(128)
+    seed = 1000 + cfg["index"]
+    t0 = time.perf_counter()
+    q, k, v, info = planted_qkv(n, hq, hkv, seed=seed, device="cuda")
+    torch.cuda.synchronize()
+    print(f"[bench] inputs {args.config}: n={n} hq={hq} hkv={hkv} kinds={kinds.count('vs')} VS / "
+          f"{kinds.count('block')} BS / {kinds.count('ashape')} A ({time.perf_counter() - t0:.1f} s)",
+          file=sys.stderr, flush=True)
+
+    if args.calib_copy_mib > 0:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] calibration copy of {args.calib_copy_mib} MiB done", file=sys.stderr, flush=True)
+
+    vs_heads = [h for h in range(hq) if kinds[h] == "vs"]
+    bs_heads = [h for h in range(hq) if kinds[h] == "block"]
+    dev = q.device
+    ws_vs = torch.empty(max(1, minf.library().minf_vs_index_workspace_size(n, len(vs_heads))), dtype=torch.uint8,
+                        device=dev)
+    ws_bs = torch.empty(max(1, minf.library().minf_block_index_workspace_size(n, hq, hkv, len(bs_heads))),
+                        dtype=torch.uint8, device=dev)
+    ws_at = torch.empty(max(1, minf.library().minf_sparse_attn_workspace_size(n, hq)), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, n), dtype=torch.float32, device=dev)
+
+    state = {}
+
+    def build_index():
+        if vs_heads:
+            state["vi"], state["si"] = minf.minf_build_vs_index(q, k, vs_heads, last_q=cfg["last_q"], k_v=cfg["k_v"],
+                                                                k_s=cfg["k_s"], scale=scale, workspace=ws_vs)
+        if bs_heads:
+            state["bi"], state["bc"] = minf.minf_build_block_index(q, k, bs_heads, k_b=cfg["k_b"], workspace=ws_bs)
+
+    def plans_from_state():
+        plans = []
+        for h in range(hq):
+            if kinds[h] == "vs":
+                t = vs_heads.index(h)
+                plans.append(dict(kind="vs", v_idx=state["vi"][t], s_idx=state["si"][t]))
+            elif kinds[h] == "block":
+                t = bs_heads.index(h)
+                plans.append(dict(kind="block", blk_idx=state["bi"][t], blk_cnt=state["bc"][t]))
+            else:
+                plans.append(dict(kind="ashape", sink=cfg["sink"], local=cfg["local"]))
+        return plans
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(record=None):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record(stream)
+        build_index()
+        e1.record(stream)
+        plans = minf.make_plans(plans_from_state())
+        minf.minf_sparse_attn(q, k, v, plans, scale=scale, out=o, lse=lse, workspace=ws_at)
+        e2.record(stream)
+        if record is not None:
+            record.append((e0, e1, e2))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    idx_ms = sum(a.elapsed_time(b) for a, b, _ in recs) / len(recs)
+    attn_ms = sum(b.elapsed_time(c) for _, b, c in recs) / len(recs)
+    step_ms = sum(a.elapsed_time(c) for a, _, c in recs) / len(recs)
+    print(f"[bench] step {step_ms:.2f} ms (index {idx_ms:.3f} ms, attention {attn_ms:.2f} ms; wall {wall_ms:.2f})",
+          file=sys.stderr, flush=True)
+
+    # algorithmic work of the attention launch
+    plans_t = plans_from_state()
+    blocks = cols = 0
+    per_kind = {}
+    head_work = []
+    nb = (n + 63) // 64
+    a_blocks = ashape_blocks(n, cfg["sink"], cfg["local"]) if "ashape" in kinds else 0
+    for h in range(hq):
+        p = plans_t[h]
+        if p["kind"] == "vs":
+            b_, c_ = vs_work(p["v_idx"], p["s_idx"], n)
+        elif p["kind"] == "block":
+            b_, c_ = int(p["blk_cnt"].long().sum()), 0
+        else:
+            b_, c_ = a_blocks, 0
+        head_work.append((b_, c_))
+        blocks += b_
+        cols += c_
+        pk = per_kind.setdefault(p["kind"], [0, 0, 0])
+        pk[0] += b_
+        pk[1] += c_
+        pk[2] += 1
+    dense_blocks = hq * nb * (nb + 1) // 2
+    flop = blocks * BLOCK_FLOP + cols * COL_FLOP
+    attn_tflops = flop / (attn_ms * 1e-3) / 1e12
+    density = {kd: round((bk + cl / 64) / (cnt * nb * (nb + 1) / 2), 4) for kd, (bk, cl, cnt) in per_kind.items()}
+    print(f"[bench] computed blocks {blocks} + columns {cols} ({flop / 1e12:.1f} TFLOP); density {density}; "
+          f"attention {attn_tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
+
+    # index-build algorithmic HBM bytes: K once per KV group, last queries, and score/index arrays
+    idx_bytes = 0
+    if vs_heads:
+        kv_used = {h // (hq // hkv) for h in vs_heads}
+        idx_bytes += len(kv_used) * n * 128 * 2 + len(vs_heads) * (64 * 128 * 2 + 2 * n * 4 * 2)
+    if bs_heads:
+        kv_used = {h // (hq // hkv) for h in bs_heads}
+        idx_bytes += (len(kv_used) + len(bs_heads)) * n * 128 * 2
+
+    extra = {}
+    # index-injected track: the pages' local-slash / scattered-vertical heads
+    if not args.no_injected and vs_heads:
+        inj = []
+        vi_l, si_l = [], []
+        for t, h in enumerate(vs_heads):
+            g = h // (hq // hkv)
+            a, b = injected_vs_index(n, cfg["k_v"], cfg["k_s"], info.columns[g], info.offsets, seed=seed + 100 + h)
+            vi_l.append(a.cuda())
+            si_l.append(b.cuda())
+        inj_plans = []
+        for h in range(hq):
+            if kinds[h] == "vs":
+                t = vs_heads.index(h)
+                inj_plans.append(dict(kind="vs", v_idx=vi_l[t], s_idx=si_l[t]))
+            else:
+                inj_plans.append(plans_t[h])
+        cp = minf.make_plans(inj_plans)
+        minf.minf_sparse_attn(q, k, v, cp, scale=scale, out=o, lse=lse, workspace=ws_at)
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(max(2, args.steps)):
+            a, b = ev(), ev()
+            a.record(stream)
+            minf.minf_sparse_attn(q, k, v, cp, scale=scale, out=o, lse=lse, workspace=ws_at)
+            b.record(stream)
+            reps.append((a, b))
+        torch.cuda.synchronize()
+        inj_attn_ms = sum(a.elapsed_time(b) for a, b in reps) / len(reps)
+        ib = ic = 0
+        for h in range(hq):
+            if kinds[h] == "vs":
+                t = vs_heads.index(h)
+                b_, c_ = vs_work(vi_l[t], si_l[t], n)
+            else:
+                b_, c_ = head_work[h]
+            ib += b_
+            ic += c_
+        inj_flop = ib * BLOCK_FLOP + ic * COL_FLOP
+        extra["injected_track"] = {
+            "attn_ms": round(inj_attn_ms, 3),
+            "step_ms": round(inj_attn_ms + idx_ms, 3),
+            "attn_tflops": round(inj_flop / (inj_attn_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(inj_flop / (inj_attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "computed_blocks": ib, "gathered_columns": ic,
+            "density": round((ib + ic / 64) / dense_blocks, 5),
+            "note": "slashes [0, k_s) plus planted, verticals seeded-uniform plus planted; index build timed on the data",
+        }
+        print(f"[bench] injected track: attention {inj_attn_ms:.2f} ms, "
+              f"{extra['injected_track']['attn_tflops']} TFLOP/s", file=sys.stderr, flush=True)
+
+    dense = None
+    if not args.no_dense:
+        runs = []
+        for _ in range(args.dense_runs):
+            a, b = ev(), ev()
+            a.record(stream)
+            minf.minf_dense_attn(q, k, v, scale=scale, out=o, lse=lse)
+            b.record(stream)
+            runs.append((a, b))
+        torch.cuda.synchronize()
+        dense_ms = sum(a.elapsed_time(b) for a, b in runs) / len(runs)
+        dense = {
+            "ms": round(dense_ms, 2),
+            "tflops": round(dense_blocks * BLOCK_FLOP / (dense_ms * 1e-3) / 1e12, 1),
+            "speedup_step": round(dense_ms / step_ms, 3),
+            "speedup_attention": round(dense_ms / attn_ms, 3),
+        }
+        if "injected_track" in extra:
+            extra["injected_track"]["speedup_step_vs_dense"] = round(dense_ms / extra["injected_track"]["step_ms"], 2)
+        print(f"[bench] dense {dense_ms:.1f} ms ({dense['tflops']} TFLOP/s), speedup {dense['speedup_step']}x",
+              file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(q, k, v, kinds, cfg, plans_t, n, None)
+        print(f"[bench] cpu oracle sample {cpu['sample_seconds']} s", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": METRIC,
+        "value": round(step_ms, 3),
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic seeded N(0,1) Q/K/V with planted verticals and slashes; index built on device from the data",
+        "config": {"workload": args.config, "tokens": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
+                   "patterns": {kd: kinds.count(kd) for kd in sorted(set(kinds))},
+                   "budgets": {key: cfg[key] for key in ("last_q", "k_v", "k_s", "k_b", "sink", "local") if key in cfg},
+                   "causal": True},
+        "index_ms": round(idx_ms, 3),
+        "attention_ms": round(attn_ms, 3),
+        "index_hbm_gbs": round(idx_bytes / (idx_ms * 1e-3) / 1e9, 1) if idx_ms > 0 else None,
+        "index_hbm_frac": round(idx_bytes / (idx_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if idx_ms > 0 else None,
+        "density": density,
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_kernel", "flop_per_launch": flop,
+                     "flop_rule": "4*64*64*128 per computed 64x64 block + 4*64*128 per gathered column per query block"},
+        "dense": dense,
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

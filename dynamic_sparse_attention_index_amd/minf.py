@@ -219,12 +219,12 @@ def minf_sparse_attn(q, k, v, plans, scale=None, out=None, lse=None, with_lse=Tr
         _need(t, torch.bfloat16, nm)
     hq, n, d = q.shape
     hkv = k.shape[0]
-    if len(plans) != hq:
+    arr, keep = plans if isinstance(plans, tuple) else make_plans(plans)
+    if len(arr) != hq:
         raise ValueError("one plan per query head is required")
     o = torch.empty_like(q) if out is None else out
     if lse is None and with_lse:
         lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
-    arr, keep = plans if isinstance(plans, tuple) else make_plans(plans)
     ws, wsb = _workspace(_lib.minf_sparse_attn_workspace_size(n, hq), q.device, workspace)
     _check(_lib.minf_sparse_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, hq, hkv, d, _scale(scale, d), arr,
                                  _ptr(ws), wsb, _stream(stream)))
