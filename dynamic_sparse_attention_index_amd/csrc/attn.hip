@@ -18,12 +18,17 @@
 //  * products run on 32x32x16 bf16 MFMA in transposed form: S^T = K Q^T and
 //    O^T = V^T P^T, so a lane owns one query row in both the score and the
 //    output accumulators and the online-softmax rescale is lane-local.
-//  * V is transposed while it is staged (global row-major -> LDS [d][key])
-//    with the key order inside each 16-key step permuted to match the score
-//    accumulator's row order, so P goes from accumulator to MFMA operand
-//    without any cross-lane movement.
-//  * K/V tiles are double-buffered in LDS; the next tile's global loads are in
-//    flight while the current tile is computed (one barrier per tile).
+//  * K and V tiles go from HBM straight into LDS with 16-byte direct loads
+//    (global_load_lds_dwordx4: no staging registers, no VALU), row-major with
+//    the 16-byte chunk index of each row XOR-swizzled so that both operand
+//    reads below are free of bank conflicts.
+//  * V is read with the CDNA4 LDS transpose load (ds_read_b64_tr_b16): each
+//    16-lane group turns 4 key rows x 16 d into 16 lanes x 4 keys, which is
+//    the A-operand layout of O^T = V^T P^T; the key order inside each 16-key
+//    step matches the score accumulator's row order, so P goes from
+//    accumulator to MFMA operand without any cross-lane movement.
+//  * tiles are double-buffered in LDS; the next tile's loads are in flight
+//    while the current tile is computed (one barrier per tile).
 #include "common.h"
 #include "launch.h"
 
@@ -31,18 +36,30 @@ namespace minf {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int KSTR = 136;  // halves per K row in LDS (128 + 8 pad: conflict-free 16-byte reads)
-constexpr int VSTR = 72;   // halves per V^T row in LDS (64 keys + 8 pad)
+constexpr int kTileHalves = kBlock * kHeadDim;  // one 64 x 128 bf16 tile, 16 KiB, rows of 256 bytes
 constexpr int kBitWords = (kMaxTokens / kBlock) / 32 + 1;  // 513 words per bitmap
 constexpr int kColChunk = 1024;  // candidate vertical columns compacted per round
 
+// K/V tile buffers are four distinct LDS objects (not one array): the
+// compiler then knows that the direct loads filling one buffer cannot alias
+// the reads of the other, and does not wait for the loads in flight before
+// computing on the current tile.
 struct Smem {
-  uint16_t kt[2][kBlock * KSTR];
-  uint16_t vt[2][kHeadDim * VSTR];
   uint32_t bits[2][kBitWords];
   uint32_t clist[kColChunk];
   int scan[16];
 };
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Chunk swizzle of a tile row: the 16-byte chunk c of row r sits at chunk
+// position c ^ swz(r). swz is a bijection on r mod 16, so 16 consecutive rows
+// read at one chunk hit 16 distinct bank groups; and 4 consecutive rows read
+// at chunks {2m, 2m+1} hit 8 distinct ones.
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 enum : int { KIND_DENSE = 0, KIND_ASHAPE = 1, KIND_VS = 2, KIND_BLOCK = 3 };
 
@@ -129,52 +146,52 @@ struct BlockIter {
   }
 };
 
-struct TileRegs {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-// Global -> registers for one K/V tile. Rows come from `rows_of(x)`, x in [0, 64):
-// the key index, or -1 for a padding row (loaded as zeros).
+// Issue the direct HBM -> LDS copies of one K/V tile. rows_of(x) gives the key
+// index of tile row x (always a valid row; rows past the mask are masked
+// later). Wave w's instruction i fills LDS chunks [256 i + 64 w, +64): rows
+// 16 i + 4 w .. +3, the 16 lanes of a row covering its 16 chunks.
 template <class RowFn>
-__device__ __forceinline__ void load_tile(TileRegs& R, const uint16_t* kh, const uint16_t* vh, RowFn rows_of) {
-  const int tid = threadIdx.x;
-  // K: 16 threads per row, 16 rows per pass
-  const int kdc = tid & 15;
-  const int krow = tid >> 4;
+__device__ __forceinline__ void issue_tile(const uint16_t* kh, const uint16_t* vh, uint16_t* kt, uint16_t* vt,
+                                           RowFn rows_of) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rlo = 4 * wave + (lane >> 4);
+  const int cb = ((lane & 15) ^ swz(rlo)) * 16;  // byte offset of this lane's chunk in its row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int j = rows_of(krow + 16 * i);
-    R.k[i] = j >= 0 ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * kdc) : u32x4{0, 0, 0, 0};
-  }
-  // V: thread owns keys 4*kq .. 4*kq+3 and dims 8*dc .. 8*dc+7
-  const int kq = tid & 15;
-  const int dc = tid >> 4;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int j = rows_of(4 * kq + r);
-    R.v[r] = j >= 0 ? *(const u32x4*)(vh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
+    const int j = rows_of(16 * i + rlo);
+    const size_t off = (size_t)j * (kHeadDim * 2) + cb;
+    __builtin_amdgcn_global_load_lds((const char*)kh + off, (lds_ptr)(kt + (256 * i + 64 * wave) * 8), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const char*)vh + off, (lds_ptr)(vt + (256 * i + 64 * wave) * 8), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& R, uint16_t* kt, uint16_t* vt) {
-  const int tid = threadIdx.x;
-  const int kdc = tid & 15;
-  const int krow = tid >> 4;
+// Per-lane LDS byte offsets of the MFMA operands inside a tile.
+struct OperandOffsets {
+  int k[8];    // K rows r32 (+32 for keys 32-63), chunk 2ks + g
+  int v[4][2]; // V transpose reads: d block mt, key half h (+ 4096 per 16-key step)
+};
+
+__device__ __forceinline__ OperandOffsets operand_offsets() {
+  OperandOffsets o;
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *(u32x4*)(kt + (krow + 16 * i) * KSTR + 8 * kdc) = R.k[i];
-  const int kq = tid & 15;
-  const int dc = tid >> 4;
-  // keys 4kq..4kq+3 land at permuted positions: bits 2 and 3 of the key swapped
-  const int pos = 16 * (kq >> 2) + ((kq & 1) << 3) + ((kq & 2) << 1);
+  for (int ks = 0; ks < 8; ++ks) o.k[ks] = r32 * 256 + (((2 * ks + g) ^ swz(r32)) << 4);
+  // ds_read_b64_tr_b16 source lane i of 16-lane group G supplies the 4 halves
+  // V[kb + i/4][dbase + 4(i%4) ..]; lane i then receives V[kb + e][dbase + i], e = 0..3.
+  const int G = lane >> 4;
+  const int i = lane & 15;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int wsel = e >> 1;
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    uint32_t lo = __builtin_amdgcn_perm(R.v[1][wsel], R.v[0][wsel], sel);
-    uint32_t hi = __builtin_amdgcn_perm(R.v[3][wsel], R.v[2][wsel], sel);
-    *(u32x2*)(vt + (8 * dc + e) * VSTR + pos) = u32x2{lo, hi};
-  }
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + 4 * g + (i >> 2);             // + 16 kk at read time
+      const int chunk = 4 * mt + 2 * (G & 1) + ((i >> 1) & 1);  // d = 32 mt + 16 (G & 1) + 4 (i & 3)
+      o.v[mt][h] = row * 256 + ((chunk ^ swz(row)) << 4) + 8 * (i & 1);
+    }
+  return o;
 }
 
 struct WaveState {
@@ -183,26 +200,31 @@ struct WaveState {
   float m, l;      // running max (log2 units) and this lane's partial sum
 };
 
+// The 64-wide accumulator rescale runs only on tiles where some row of the
+// wave raises its running max (alpha == 1 otherwise, so skipping it is exact).
+// Keeping the max exact (no slack) keeps the dominant probability exactly 1.0
+// in bf16, which the 2e-2 output bar needs when |O| approaches 8.
+constexpr float kRescaleSlack = 0.0f;
+
 // One tile for one wave. mode: 0 = all visible, 1 = element predicate.
 // Predicate: key j visible for row i iff j <= i (causal) or j < n (non-causal),
 // plus the A-shape clause, plus (gather tiles) the column's membership flag.
 template <bool GATHER>
-__device__ __forceinline__ void compute_tile(WaveState& ws, const uint16_t* kt, const uint16_t* vt, int mode,
-                                             int key0, const uint32_t* gcols, int qsel, int row, int n,
-                                             int causal, int ashape, int sink, int local, float sl2) {
+__device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
+                                             const uint16_t* vt, int mode, int key0, const uint32_t* gcols,
+                                             int qsel, int row, int n, int causal, int ashape, int sink, int local,
+                                             float sl2) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
-  const int r32 = lane & 31;
-  f32x16 s[2];
+  const char* kb = (const char*)kt;
+  // S^T = K Q^T: two independent accumulation chains (keys 0-31, 32-63), interleaved
+  f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    s[mt] = f32x16{};
-    const uint16_t* kp = kt + (32 * mt + r32) * KSTR + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      u32x4 a = *(const u32x4*)(kp + 16 * ks);
-      s[mt] = mfma32(a, ws.qr[ks], s[mt]);
-    }
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4 a0 = *(const u32x4*)(kb + oo.k[ks]);
+    const u32x4 a1 = *(const u32x4*)(kb + oo.k[ks] + 32 * 256);
+    s[0] = mfma32(a0, ws.qr[ks], s[0]);
+    s[1] = mfma32(a1, ws.qr[ks], s[1]);
   }
   if (mode) {
 #pragma unroll
@@ -225,15 +247,19 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const uint16_t* kt, 
       }
     }
   }
-  float mx = -INFINITY;
+  float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+  const float m_tile = pair_max32(mx) * sl2;
+  if (__any(m_tile > ws.m + kRescaleSlack)) {
+    const float m_new = fmaxf(ws.m, m_tile);
+    const float alpha = fast_exp2(ws.m - (m_new == -INFINITY ? 0.f : m_new));
+    ws.l *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[mt][i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(ws.m, mx * sl2);
-  const float m_use = m_new == -INFINITY ? 0.f : m_new;
-  const float alpha = fast_exp2(ws.m - m_use);
+    for (int mt = 0; mt < 4; ++mt) ws.o[mt] *= alpha;
+    ws.m = m_new;
+  }
+  const float m_use = ws.m == -INFINITY ? 0.f : ws.m;
   float psum = 0.f;
   u32x4 pk[4];
 #pragma unroll
@@ -250,23 +276,30 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const uint16_t* kt, 
                              pack_bf16x2(p[6], p[7])};
     }
   }
-  ws.l = ws.l * alpha + psum;
-  ws.m = m_new;
+  ws.l += psum;
+  // O^T += V^T P^T: four independent accumulation chains (d = 0-31, ..., 96-127), interleaved
+  const char* vb = (const char*)vt;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) ws.o[mt] *= alpha;
+  for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const uint16_t* vp = vt + (32 * mt + r32) * VSTR + 8 * g;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 a = *(const u32x4*)(vp + 16 * kk);
-      ws.o[mt] = mfma32(a, pk[kk], ws.o[mt]);
+    for (int mt = 0; mt < 4; ++mt) {
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+          (lds_ptr)(vb + oo.v[mt][0] + 4096 * kk)));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+          (lds_ptr)(vb + oo.v[mt][1] + 4096 * kk)));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+      ws.o[mt] = mfma32(u32x4{l2[0], l2[1], h2[0], h2[1]}, pk[kk], ws.o[mt]);
     }
   }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t vt0[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t vt1[kTileHalves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -373,20 +406,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   }
   const int ashape = hd.kind == KIND_ASHAPE;
 
+  const OperandOffsets oo = operand_offsets();
+
   // ---------------- phase A: 64x64 key blocks
   {
-    TileRegs R;
     int c_cur = 0, m_cur = 0, c_nxt = 0, m_nxt = 0;
-    bool have = it.next(c_cur, m_cur);
-    if (have) {
-      load_tile(R, kh, vh, [&](int x) { int j = c_cur * kBlock + x; return j < n ? j : -1; });
-      store_tile(R, sm.kt[0], sm.vt[0]);
-    }
-    __syncthreads();
-    int buf = 0;
-    while (have) {
+    // rows past n (partial last block) repeat row n - 1; they are always masked
+    auto crow = [&](int cblk) { return [&, cblk](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; }; };
+    // one pipelined step: issue the next tile into (ktn, vtn), compute the current one from (ktc, vtc)
+    auto step = [&](uint16_t* ktc, uint16_t* vtc, uint16_t* ktn, uint16_t* vtn) -> bool {
       const bool hn = it.next(c_nxt, m_nxt);
-      if (hn) load_tile(R, kh, vh, [&](int x) { int j = c_nxt * kBlock + x; return j < n ? j : -1; });
+      if (hn) issue_tile(kh, vh, ktn, vtn, crow(c_nxt));
       if (wave_on && ((m_cur >> qsel) & 1)) {
         int full;
         if (p.causal || hd.kind != KIND_DENSE) {
@@ -397,15 +427,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
         } else {
           full = (c_cur + 1) * kBlock <= n;
         }
-        compute_tile<false>(ws, sm.kt[buf], sm.vt[buf], !full, c_cur * kBlock, nullptr, qsel, row, n,
+        compute_tile<false>(ws, oo, ktc, vtc, !full, c_cur * kBlock, nullptr, qsel, row, n,
                             p.causal || hd.kind != KIND_DENSE, ashape, hd.sink, hd.local, sl2);
       }
-      if (hn) store_tile(R, sm.kt[buf ^ 1], sm.vt[buf ^ 1]);
+      wait_vmem();
       __syncthreads();
       c_cur = c_nxt;
       m_cur = m_nxt;
-      have = hn;
-      buf ^= 1;
+      return hn;
+    };
+    bool have = it.next(c_cur, m_cur);
+    if (have) issue_tile(kh, vh, kt0, vt0, crow(c_cur));
+    wait_vmem();
+    __syncthreads();
+    while (have) {
+      if (!step(kt0, vt0, kt1, vt1)) break;
+      have = step(kt1, vt1, kt0, vt0);
     }
   }
 
@@ -443,30 +480,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
       for (int s = kept + tid; s < ntile * kBlock; s += kThreads) sm.clist[s] = 0u;  // padding: no member
       __syncthreads();
       if (ntile > 0) {
-        TileRegs R;
+        // padding slots load row 0 (a valid row) and are never visible
         auto rows_of = [&](int t) {
           return [&, t](int x) -> int {
             const int s = t * kBlock + x;
-            return s < kept ? (int)(sm.clist[s] & 0x3fffffffu) : -1;
+            return s < kept ? (int)(sm.clist[s] & 0x3fffffffu) : 0;
           };
         };
-        load_tile(R, kh, vh, rows_of(0));
-        store_tile(R, sm.kt[0], sm.vt[0]);
-        __syncthreads();
-        int buf = 0;
-        for (int t = 0; t < ntile; ++t) {
-          const bool hn = t + 1 < ntile;
-          if (hn) load_tile(R, kh, vh, rows_of(t + 1));
+        auto gstep = [&](int t, uint16_t* ktc, uint16_t* vtc, uint16_t* ktn, uint16_t* vtn) {
+          if (t + 1 < ntile) issue_tile(kh, vh, ktn, vtn, rows_of(t + 1));
           if (wave_on) {
             // skip the tile when none of its columns belongs to this wave's query block
             // (padding slots were cleared, so they never count)
             const uint32_t* gc = sm.clist + t * kBlock;
             if (__any((gc[lane] >> (30 + qsel)) & 1u))
-              compute_tile<true>(ws, sm.kt[buf], sm.vt[buf], 1, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
+              compute_tile<true>(ws, oo, ktc, vtc, 1, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
           }
-          if (hn) store_tile(R, sm.kt[buf ^ 1], sm.vt[buf ^ 1]);
+          wait_vmem();
           __syncthreads();
-          buf ^= 1;
+        };
+        issue_tile(kh, vh, kt0, vt0, rows_of(0));
+        wait_vmem();
+        __syncthreads();
+        for (int t = 0; t < ntile; t += 2) {
+          gstep(t, kt0, vt0, kt1, vt1);
+          if (t + 1 < ntile) gstep(t + 1, kt1, vt1, kt0, vt0);
         }
       }
       if (any_past) break;
@@ -475,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
 
   // ---------------- finalize
   if (!wave_on) return;
-  const float ltot = ws.l + __shfl_xor(ws.l, 32);
+  const float ltot = pair_sum32(ws.l);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   if (row < n) {
     const int g = lane >> 5;

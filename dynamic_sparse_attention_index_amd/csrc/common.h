@@ -27,11 +27,27 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Round-to-nearest-even fp32 -> bf16 of two values packed into one word (low = a).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-to-nearest-even fp32 -> bf16 of two values packed into one word (low = a);
+// one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 ha = (__bf16)a;
-  __bf16 hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Value of lane l ^ 32 combined with lane l's own: v_permlane32_swap on (x, x)
+// leaves lanes 0-31 of one result and lanes 32-63 of the other holding the
+// partner half, so max / sum of the two results is the pair reduction.
+__device__ __forceinline__ float pair_max32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                            false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                            false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
