@@ -54,10 +54,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Chunk swizzle of a tile row: the 16-byte chunk c of row r sits at chunk
-// position c ^ swz(r). swz is a bijection on r mod 16, so 16 consecutive rows
-// read at one chunk hit 16 distinct bank groups; and 4 consecutive rows read
-// at chunks {2m, 2m+1} hit 8 distinct ones.
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// position c ^ swz(r), swz swapping the two 2-bit halves of r mod 16. It is a
+// bijection on 16 consecutive rows (the K operand reads 16 rows at one chunk:
+// 16 distinct bank groups), and 4 consecutive rows get 4 distinct values of
+// bits 2-3 (the V transpose reads touch 4 rows x 4 aligned chunks: 16
+// distinct bank groups).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -146,21 +148,38 @@ struct BlockIter {
   }
 };
 
-// Issue the direct HBM -> LDS copies of one K/V tile. rows_of(x) gives the key
-// index of tile row x (always a valid row; rows past the mask are masked
-// later). Wave w's instruction i fills LDS chunks [256 i + 64 w, +64): rows
-// 16 i + 4 w .. +3, the 16 lanes of a row covering its 16 chunks.
-template <class RowFn>
-__device__ __forceinline__ void issue_tile(const uint16_t* kh, const uint16_t* vh, uint16_t* kt, uint16_t* vt,
-                                           RowFn rows_of) {
-  const int lane = threadIdx.x & 63;
+// Issue the direct HBM -> LDS copies of one K/V tile. Wave w's instruction i
+// fills LDS chunks [256 i + 64 w, +64): rows 16 i + 4 w .. +3, the 16 lanes of
+// a row covering its 16 chunks (one 256-byte row per 16 lanes, coalesced).
+__device__ __forceinline__ int tile_row_lo() { return 4 * (threadIdx.x >> 6) + ((threadIdx.x & 63) >> 4); }
+__device__ __forceinline__ uint32_t tile_chunk_byte() {
+  return (uint32_t)((((threadIdx.x & 63) & 15) ^ swz(tile_row_lo())) * 16);
+}
+
+// Tile of 64 consecutive key rows starting at a valid row with 64 rows left:
+// uniform base pointers and per-lane 32-bit offsets.
+__device__ __forceinline__ void issue_contig(const char* kbase, const char* vbase, uint16_t* kt, uint16_t* vt,
+                                             uint32_t lane_off) {
   const int wave = threadIdx.x >> 6;
-  const int rlo = 4 * wave + (lane >> 4);
-  const int cb = ((lane & 15) ^ swz(rlo)) * 16;  // byte offset of this lane's chunk in its row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int j = rows_of(16 * i + rlo);
-    const size_t off = (size_t)j * (kHeadDim * 2) + cb;
+    const uint32_t off = lane_off + (uint32_t)i * 16 * 256;
+    __builtin_amdgcn_global_load_lds(kbase + off, (lds_ptr)(kt + (256 * i + 64 * wave) * 8), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vbase + off, (lds_ptr)(vt + (256 * i + 64 * wave) * 8), 16, 0, 0);
+  }
+}
+
+// General tile: rows_of(x) gives the key index of tile row x (always a valid
+// row; rows past the mask are masked later).
+template <class RowFn>
+__device__ __forceinline__ void issue_rows(const uint16_t* kh, const uint16_t* vh, uint16_t* kt, uint16_t* vt,
+                                           RowFn rows_of) {
+  const int wave = threadIdx.x >> 6;
+  const int rlo = tile_row_lo();
+  const uint32_t cb = tile_chunk_byte();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t off = (uint32_t)rows_of(16 * i + rlo) * 256u + cb;
     __builtin_amdgcn_global_load_lds((const char*)kh + off, (lds_ptr)(kt + (256 * i + 64 * wave) * 8), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const char*)vh + off, (lds_ptr)(vt + (256 * i + 64 * wave) * 8), 16, 0, 0);
   }
@@ -168,7 +187,7 @@ __device__ __forceinline__ void issue_tile(const uint16_t* kh, const uint16_t* v
 
 // Per-lane LDS byte offsets of the MFMA operands inside a tile.
 struct OperandOffsets {
-  int k[8];    // K rows r32 (+32 for keys 32-63), chunk 2ks + g
+  int k;       // K row r32, chunk (g ^ swz): chunk 2ks + g of the row is at k ^ (ks << 5)
   int v[4][2]; // V transpose reads: d block mt, key half h (+ 4096 per 16-key step)
 };
 
@@ -177,8 +196,8 @@ __device__ __forceinline__ OperandOffsets operand_offsets() {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int r32 = lane & 31;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) o.k[ks] = r32 * 256 + (((2 * ks + g) ^ swz(r32)) << 4);
+  // (2ks + g) ^ swz = (g ^ swz) ^ 2ks, and the chunk field (bits 4-7) does not overlap the row bits
+  o.k = r32 * 256 + ((g ^ swz(r32)) << 4);
   // ds_read_b64_tr_b16 source lane i of 16-lane group G supplies the 4 halves
   // V[kb + i/4][dbase + 4(i%4) ..]; lane i then receives V[kb + e][dbase + i], e = 0..3.
   const int G = lane >> 4;
@@ -206,14 +225,15 @@ struct WaveState {
 // in bf16, which the 2e-2 output bar needs when |O| approaches 8.
 constexpr float kRescaleSlack = 0.0f;
 
-// One tile for one wave. mode: 0 = all visible, 1 = element predicate.
-// Predicate: key j visible for row i iff j <= i (causal) or j < n (non-causal),
-// plus the A-shape clause, plus (gather tiles) the column's membership flag.
-template <bool GATHER>
+// One tile for one wave. MASK: 0 = every key visible; 1 = causal (j <= i);
+// 2 = general predicate (causal or j < n, plus the A-shape clause);
+// 3 = gathered columns (per-column membership flag and j <= i).
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_GENERAL = 2, MASK_GATHER = 3 };
+
 __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
-                                             const uint16_t* vt, int mode, int key0, const uint32_t* gcols,
-                                             int qsel, int row, int n, int causal, int ashape, int sink, int local,
-                                             float sl2) {
+                                             const uint16_t* vt, int MASK, int key0, const uint32_t* gcols,
+                                             int qsel, int row, int n, int causal, int ashape, int sink,
+                                             int local, float sl2) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const char* kb = (const char*)kt;
@@ -221,31 +241,50 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
   f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const u32x4 a0 = *(const u32x4*)(kb + oo.k[ks]);
-    const u32x4 a1 = *(const u32x4*)(kb + oo.k[ks] + 32 * 256);
+    const int ko = oo.k ^ (ks << 5);
+    const u32x4 a0 = *(const u32x4*)(kb + ko);
+    const u32x4 a1 = *(const u32x4*)(kb + ko + 32 * 256);
     s[0] = mfma32(a0, ws.qr[ks], s[0]);
     s[1] = mfma32(a1, ws.qr[ks], s[1]);
   }
-  if (mode) {
+  // the mask touches only the score registers; MASK is uniform across the wave
+  if (MASK == MASK_CAUSAL) {
+    const int lim = row - key0 - 4 * g;  // key slot kx = kx0 + 4g is visible iff kx0 <= lim
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kx = 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);  // key slot in the tile
-        int j;
-        bool vis;
-        if (GATHER) {
-          uint32_t e = gcols[kx];
-          j = (int)(e & 0x3fffffffu);
-          vis = ((e >> (30 + qsel)) & 1u) && j <= row;
-        } else {
-          j = key0 + kx;
-          vis = causal ? (j <= row) : (j < n);
-          if (ashape) vis = vis && (j < sink || row - j < local);
-        }
-        if (!vis) s[mt][i] = -INFINITY;
+        const int kx0 = 32 * mt + 8 * (i >> 2) + (i & 3);
+        s[mt][i] = kx0 <= lim ? s[mt][i] : -INFINITY;
       }
-    }
+  } else if (MASK == MASK_GENERAL) {
+    // with j = key0 + 4g + kx0: visible iff kx0 <= hi and (kx0 < lo_sink or kx0 > lo_win)
+    const int base = key0 + 4 * g;
+    const int hi = causal ? row - base : n - 1 - base;
+    const int lo_sink = ashape ? sink - base : 1 << 30;
+    const int lo_win = ashape ? row - local - base : -(1 << 30);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kx0 = 32 * mt + 8 * (i >> 2) + (i & 3);
+        const bool vis = kx0 <= hi && (kx0 < lo_sink || kx0 > lo_win);
+        s[mt][i] = vis ? s[mt][i] : -INFINITY;
+      }
+  } else if (MASK == MASK_GATHER) {
+    const uint32_t sh = 30 + qsel;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4 e4 = *(const u32x4*)(gcols + 32 * mt + 8 * q4 + 4 * g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t e = e4[t];
+          const bool vis = ((e >> sh) & 1u) && (int)(e & 0x3fffffffu) <= row;
+          s[mt][4 * q4 + t] = vis ? s[mt][4 * q4 + t] : -INFINITY;
+        }
+      }
   }
   float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
@@ -253,7 +292,9 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
   const float m_tile = pair_max32(mx) * sl2;
   if (__any(m_tile > ws.m + kRescaleSlack)) {
     const float m_new = fmaxf(ws.m, m_tile);
-    const float alpha = fast_exp2(ws.m - (m_new == -INFINITY ? 0.f : m_new));
+    float alpha = fast_exp2(ws.m - (m_new == -INFINITY ? 0.f : m_new));
+    // keeps the rescale a real branch: its body cannot be speculated into a select
+    asm volatile("" : "+v"(alpha));
     ws.l *= alpha;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) ws.o[mt] *= alpha;
@@ -411,15 +452,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   // ---------------- phase A: 64x64 key blocks
   {
     int c_cur = 0, m_cur = 0, c_nxt = 0, m_nxt = 0;
-    // rows past n (partial last block) repeat row n - 1; they are always masked
-    auto crow = [&](int cblk) { return [&, cblk](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; }; };
+    const uint32_t lane_off = (uint32_t)tile_row_lo() * 256u + tile_chunk_byte();
+    const int causal_eff = p.causal || hd.kind != KIND_DENSE;
+    auto issue_block = [&](int cblk, uint16_t* ktn, uint16_t* vtn) {
+      if ((cblk + 1) * kBlock <= n) {
+        const size_t base = (size_t)cblk * kBlock * (kHeadDim * 2);
+        issue_contig((const char*)kh + base, (const char*)vh + base, ktn, vtn, lane_off);
+      } else {
+        // partial last block: rows past n repeat row n - 1 and are always masked
+        issue_rows(kh, vh, ktn, vtn, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
+      }
+    };
     // one pipelined step: issue the next tile into (ktn, vtn), compute the current one from (ktc, vtc)
     auto step = [&](uint16_t* ktc, uint16_t* vtc, uint16_t* ktn, uint16_t* vtn) -> bool {
       const bool hn = it.next(c_nxt, m_nxt);
-      if (hn) issue_tile(kh, vh, ktn, vtn, crow(c_nxt));
+      if (hn) issue_block(c_nxt, ktn, vtn);
       if (wave_on && ((m_cur >> qsel) & 1)) {
         int full;
-        if (p.causal || hd.kind != KIND_DENSE) {
+        if (causal_eff) {
           full = c_cur < qb;
           if (ashape && full)
             full = ((int64_t)c_cur * kBlock + kBlock - 1 < hd.sink) ||
@@ -427,8 +477,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
         } else {
           full = (c_cur + 1) * kBlock <= n;
         }
-        compute_tile<false>(ws, oo, ktc, vtc, !full, c_cur * kBlock, nullptr, qsel, row, n,
-                            p.causal || hd.kind != KIND_DENSE, ashape, hd.sink, hd.local, sl2);
+        const int mask = full ? MASK_NONE : ((causal_eff && !ashape) ? MASK_CAUSAL : MASK_GENERAL);
+        compute_tile(ws, oo, ktc, vtc, mask, c_cur * kBlock, nullptr, qsel, row, n, causal_eff, ashape, hd.sink,
+                     hd.local, sl2);
       }
       wait_vmem();
       __syncthreads();
@@ -437,7 +488,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
       return hn;
     };
     bool have = it.next(c_cur, m_cur);
-    if (have) issue_tile(kh, vh, kt0, vt0, crow(c_cur));
+    if (have) issue_block(c_cur, kt0, vt0);
     wait_vmem();
     __syncthreads();
     while (have) {
@@ -488,18 +539,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
           };
         };
         auto gstep = [&](int t, uint16_t* ktc, uint16_t* vtc, uint16_t* ktn, uint16_t* vtn) {
-          if (t + 1 < ntile) issue_tile(kh, vh, ktn, vtn, rows_of(t + 1));
+          if (t + 1 < ntile) issue_rows(kh, vh, ktn, vtn, rows_of(t + 1));
           if (wave_on) {
             // skip the tile when none of its columns belongs to this wave's query block
             // (padding slots were cleared, so they never count)
             const uint32_t* gc = sm.clist + t * kBlock;
             if (__any((gc[lane] >> (30 + qsel)) & 1u))
-              compute_tile<true>(ws, oo, ktc, vtc, 1, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
+              compute_tile(ws, oo, ktc, vtc, MASK_GATHER, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
           }
           wait_vmem();
           __syncthreads();
         };
-        issue_tile(kh, vh, kt0, vt0, rows_of(0));
+        issue_rows(kh, vh, kt0, vt0, rows_of(0));
         wait_vmem();
         __syncthreads();
         for (int t = 0; t < ntile; t += 2) {
