@@ -320,12 +320,35 @@ static minf_status check_attn_common(const void* q, const void* k, const void* v
   return check_scale(scale);
 }
 
+// Heads per attention launch and per work chunk. A launch takes up to 32
+// heads; the chunk size hg divides both the launch's head count and 64, and
+// equals the GQA group size when it can (those heads read the same K/V).
+static void head_split(int hq, int grp, int h0, int& nh, int& hg) {
+  const int left = hq - h0;
+  if (grp <= kMaxLaunchHeads) {
+    const int per = (kMaxLaunchHeads / grp) * grp;
+    nh = std::min(per, left);
+  } else {
+    nh = std::min(kMaxLaunchHeads, left);
+  }
+  hg = 1;
+  for (int c = 64; c >= 1; c >>= 1)
+    if (c <= grp && nh % c == 0 && grp % c == 0) {
+      hg = c;
+      break;
+    }
+}
+
 static minf_status launch_all_heads(AttnLaunch& a, int hq, hipStream_t stream) {
-  for (int h0 = 0; h0 < hq; h0 += kMaxLaunchHeads) {
+  for (int h0 = 0; h0 < hq;) {
+    int nh, hg;
+    head_split(hq, a.grp, h0, nh, hg);
     a.head0 = h0;
-    a.nh = std::min(kMaxLaunchHeads, hq - h0);
+    a.nh = nh;
+    a.hgroup = hg;
     hipError_t e = launch_attn(a, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel");
+    h0 += nh;
   }
   return MINF_OK;
 }
@@ -388,8 +411,9 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
     hipError_t e = launch_vs_offset_bits(vs_s.data(), vs_k.data(), vs_bits.data(), (int)vs_s.size(), (int)n, stream);
     if (e != hipSuccess) return hip_fail(e, "VS offset bitmap kernel");
   }
-  for (int h0 = 0; h0 < hq; h0 += kMaxLaunchHeads) {
-    const int nh = std::min(kMaxLaunchHeads, hq - h0);
+  for (int h0 = 0; h0 < hq;) {
+    int nh, hg;
+    head_split(hq, a.grp, h0, nh, hg);
     for (int i = 0; i < nh; ++i) {
       const minf_head_plan& p = plans[h0 + i];
       AttnHead& d2 = a.heads[i];
@@ -406,8 +430,10 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
     }
     a.head0 = h0;
     a.nh = nh;
+    a.hgroup = hg;
     hipError_t e = launch_attn(a, stream);
     if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
+    h0 += nh;
   }
   return MINF_OK;
 }

@@ -36,6 +36,8 @@ namespace minf {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs, each with its own L2
+constexpr int kChunk = 64;   // workgroups one XCD runs at once (32 CUs x 2)
 constexpr int kTileHalves = kBlock * kHeadDim;  // one 64 x 128 bf16 tile, 16 KiB, rows of 256 bytes
 constexpr int kBitWords = (kMaxTokens / kBlock) / 32 + 1;  // 513 words per bitmap
 constexpr int kColChunk = 1024;  // candidate vertical columns compacted per round
@@ -345,10 +347,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int npairs = (p.nb + 1) >> 1;
-  const int item = blockIdx.x;
-  if (item >= npairs * p.nh) return;
-  const int hl = item % p.nh;
-  const int pr = npairs - 1 - item / p.nh;  // heaviest (latest) pairs first
+  // XCD-aware work order. Workgroup L runs on XCD L % 8; that XCD's k-th
+  // workgroup takes item (k / C * 8 + L % 8) * C + k % C, so each XCD works
+  // through whole chunks of C consecutive items. A chunk is one group of hg
+  // heads sharing a KV head times C / hg consecutive query-block pairs, and
+  // C = 64 is what one XCD holds at once (32 CUs x 2 workgroups): the
+  // workgroups resident on an XCD stream the same K/V tiles through its L2.
+  // Chunks go heaviest pair block first.
+  const int slot = blockIdx.x >> 3;
+  const int item = ((slot / kChunk) * kXcds + (int)(blockIdx.x & (kXcds - 1))) * kChunk + slot % kChunk;
+  const int hg = p.hgroup;
+  const int ppc = kChunk / hg;                  // pairs per chunk
+  const int npb = (npairs + ppc - 1) / ppc;     // pair blocks
+  const int nhg = p.nh / hg;                    // head groups in this launch
+  const int chunk = item / kChunk;
+  if (chunk >= npb * nhg) return;
+  const int within = item % kChunk;
+  const int pr = (npb - 1 - chunk / nhg) * ppc + within / hg;
+  if (pr >= npairs) return;
+  const int hl = (chunk % nhg) * hg + within % hg;
   const int h = p.head0 + hl;
   const int kvh = h / p.grp;
   const AttnHead hd = p.heads[hl];
@@ -626,9 +643,13 @@ __global__ __launch_bounds__(256) void vs_offset_bits_kernel(const OffBitsLaunch
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   const int npairs = (a.nb + 1) / 2;
-  const long long items = (long long)npairs * a.nh;
-  if (items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, a);
+  if (npairs <= 0 || a.nh <= 0 || a.hgroup <= 0 || a.nh % a.hgroup != 0 || kChunk % a.hgroup != 0)
+    return hipErrorInvalidValue;
+  const int ppc = kChunk / a.hgroup;
+  const long long chunks = (long long)((npairs + ppc - 1) / ppc) * (a.nh / a.hgroup);
+  // the grid covers whole rounds of kXcds chunks so that the item map is a bijection
+  const long long grid = (chunks + kXcds - 1) / kXcds * kXcds * kChunk;
+  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

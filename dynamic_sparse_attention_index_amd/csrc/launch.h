@@ -26,6 +26,8 @@ struct AttnLaunch {
   uint16_t* o;
   float* lse;
   int32_t n, nb, hq, hkv, grp, head0, nh, causal;
+  int32_t hgroup;  // heads per work chunk: divides nh and 64; consecutive heads (they share K/V when
+                   // they fall in one GQA group)
   float scale_log2;
   AttnHead heads[kMaxLaunchHeads];
 };
