@@ -177,10 +177,6 @@ minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o
                             int64_t n, int hq, int hkv, int d, float scale, int causal,
                             hipStream_t stream);
 
-/* Number of 64x64 key blocks and gathered key columns the last minf_sparse_attn
- * / minf_dense_attn launch on this thread was planned to compute is not kept;
- * callers count work from the index themselves. */
-
 #ifdef __cplusplus
 }
 #endif
