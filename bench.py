@@ -84,6 +84,25 @@ def ashape_blocks(n, sink, local):
     return tot
 
 
+# ---------------------------------------------------------------- HBM traffic from the committed profile
+def profiled_traffic(workload):
+    """Calibrated HBM bytes per attention launch from profiles/, if measured on this kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_kernel_{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line:
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    csrc = os.path.join(ROOT, "dynamic_sparse_attention_index_amd", "csrc")
+    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("attn.hip", "common.h")))
+    if kv.get("source_sha256") != sha.hexdigest():
+        return None
+    return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
+
+
 # ---------------------------------------------------------------- CPU oracle sample
 def cpu_baseline(q, k, v, kinds, cfg, plans_gpu, n, blocks_per_head):
     """Time the fp64 oracle on a bounded sample and scale it to one layer."""
@@ -367,7 +386,7 @@ def main():
         "index_hbm_frac": round(idx_bytes / (idx_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if idx_ms > 0 else None,
         "density": density,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(args.config),
                      "kernel": "attn_kernel", "flop_per_launch": flop,
                      "flop_rule": "4*64*64*128 per computed 64x64 block + 4*64*128 per gathered column per query block"},
         "dense": dense,

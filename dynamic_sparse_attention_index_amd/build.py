@@ -38,6 +38,9 @@ def common_flags() -> list:
         "-Wno-unused-result",
         # keep the compiler from forming packed fp32 VALU ops
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # no NaN is produced or tested anywhere (infinities are still honoured): lets fmaxf
+        # skip re-canonicalising every MFMA result before the row-max reduction
+        "-fno-honor-nans",
         f"-I{os.path.join(ROOT, 'include')}",
         f"-I{CSRC}",
     ]

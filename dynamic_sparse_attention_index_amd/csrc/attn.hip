@@ -303,7 +303,6 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
     ws.m = m_new;
   }
   const float m_use = ws.m == -INFINITY ? 0.f : ws.m;
-  float psum = 0.f;
   u32x4 pk[4];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
@@ -311,14 +310,18 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
     for (int h = 0; h < 2; ++h) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(fmaf(s[mt][8 * h + e], sl2, -m_use));
-        psum += p[e];
-      }
+      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s[mt][8 * h + e], sl2, -m_use));
       pk[2 * mt + h] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                              pack_bf16x2(p[6], p[7])};
     }
   }
+  // row sum of the bf16 probabilities the PV product uses (so the weights sum to
+  // exactly one after normalisation): one v_dot2_f32_bf16 per packed pair
+  float psum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) psum = sum_bf16x2(pk[kk][w], psum);
   ws.l += psum;
   // O^T += V^T P^T: four independent accumulation chains (d = 0-31, ..., 96-127), interleaved
   const char* vb = (const char*)vt;

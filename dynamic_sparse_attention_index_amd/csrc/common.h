@@ -36,6 +36,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// acc + (low bf16 of w) + (high bf16 of w), as one v_dot2_f32_bf16 against (1, 1).
+__device__ __forceinline__ float sum_bf16x2(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 // Value of lane l ^ 32 combined with lane l's own: v_permlane32_swap on (x, x)
 // leaves lanes 0-31 of one result and lanes 32-63 of the other holding the
 // partner half, so max / sum of the two results is the pair reduction.

@@ -168,7 +168,8 @@ def test_vs_index_c1_exact_and_planted(gpu_lib):
     assert set(info.offsets) <= set(gsi[0].cpu().tolist())
 
 
-@pytest.mark.parametrize("n,k_v,k_s", [(4096, 64, 64), (3000, 200, 100), (1000, 1000, 0), (777, 5, 777), (2500, 1500, 40)])
+@pytest.mark.parametrize("n,k_v,k_s", [(4096, 64, 64), (3000, 200, 100), (1000, 1000, 0), (777, 5, 777), (2500, 1500, 40),
+                                       (2500, 2500, 40), (700, 500, 0)])
 def test_vs_attention_gpu_index(gpu_lib, n, k_v, k_s):
     hq, hkv = 2, 1
     q, k, v, _ = _qkv(n, hq, hkv, 19)
