@@ -321,9 +321,13 @@ static minf_status check_attn_common(const void* q, const void* k, const void* v
 }
 
 // Heads per attention launch and per work chunk. A launch takes up to 32
-// heads; the chunk size hg divides both the launch's head count and 64, and
-// equals the GQA group size when it can (those heads read the same K/V).
-static void head_split(int hq, int grp, int h0, int& nh, int& hg) {
+// heads; the chunk size hg divides both the launch's head count and 64.
+// Dense launches group the heads of one GQA group in a chunk (they read the
+// same K/V tiles in the same order). Sparse launches use one head per chunk:
+// per-head index sets differ, while the 64 consecutive query-block pairs of
+// one head select the same block offsets, so walking keys in ascending order
+// they reach each key block at about the same step and share it through L2.
+static void head_split(int hq, int grp, int h0, bool group_heads, int& nh, int& hg) {
   const int left = hq - h0;
   if (grp <= kMaxLaunchHeads) {
     const int per = (kMaxLaunchHeads / grp) * grp;
@@ -332,6 +336,7 @@ static void head_split(int hq, int grp, int h0, int& nh, int& hg) {
     nh = std::min(kMaxLaunchHeads, left);
   }
   hg = 1;
+  if (!group_heads) return;
   for (int c = 64; c >= 1; c >>= 1)
     if (c <= grp && nh % c == 0 && grp % c == 0) {
       hg = c;
@@ -342,7 +347,7 @@ static void head_split(int hq, int grp, int h0, int& nh, int& hg) {
 static minf_status launch_all_heads(AttnLaunch& a, int hq, hipStream_t stream) {
   for (int h0 = 0; h0 < hq;) {
     int nh, hg;
-    head_split(hq, a.grp, h0, nh, hg);
+    head_split(hq, a.grp, h0, true, nh, hg);
     a.head0 = h0;
     a.nh = nh;
     a.hgroup = hg;
@@ -413,7 +418,7 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
   }
   for (int h0 = 0; h0 < hq;) {
     int nh, hg;
-    head_split(hq, a.grp, h0, nh, hg);
+    head_split(hq, a.grp, h0, false, nh, hg);
     for (int i = 0; i < nh; ++i) {
       const minf_head_plan& p = plans[h0 + i];
       AttnHead& d2 = a.heads[i];

@@ -93,11 +93,14 @@ struct BlockIter {
     return bits0[ww] | bits1[ww];
   }
 
+  // Bitmap cursor over offsets/blocks [0, vmax]. VS walks its offsets
+  // downwards (key blocks in ascending order, like every other kind), BLOCK
+  // walks its key blocks upwards.
   __device__ void init_bitmap_cursor(int vmax) {
     wmax = vmax >> 5;
-    w = 0;
-    uint32_t u = union_word(0);
-    if (wmax == 0) u &= (vmax & 31) == 31 ? 0xffffffffu : ((1u << ((vmax & 31) + 1)) - 1u);
+    w = kind == KIND_VS ? wmax : 0;
+    uint32_t u = union_word(w);
+    if (w == wmax) u &= (vmax & 31) == 31 ? 0xffffffffu : ((1u << ((vmax & 31) + 1)) - 1u);
     rem = u;
   }
 
@@ -124,28 +127,35 @@ struct BlockIter {
       }
       return false;
     }
+    if (kind == KIND_VS) {
+      // highest remaining offset v first: key block c = b0 + 1 - v ascending
+      while (rem == 0u) {
+        if (--w < 0) return false;
+        rem = union_word(w);
+      }
+      const int bit = 31 - __builtin_clz(rem);
+      rem ^= 1u << bit;
+      const int v = (w << 5) + bit;
+      cout = base - v;
+      const int m1 = has_b1 && bit_at(bits1, v);
+      const int m0 = v >= 1 && bit_at(bits0, v - 1);
+      mem = m0 | (m1 << 1);
+      return true;
+    }
     // bitmap kinds: iterate set bits of the union word by word
     while (rem == 0u) {
       if (++w > wmax) return false;
       uint32_t u = union_word(w);
       if (w == wmax) {
-        int top = (kind == KIND_VS ? base : cmax) & 31;
+        const int top = cmax & 31;
         u &= top == 31 ? 0xffffffffu : ((1u << (top + 1)) - 1u);
       }
       rem = u;
     }
-    int v = (w << 5) + __builtin_ctz(rem);
+    const int v = (w << 5) + __builtin_ctz(rem);
     rem &= rem - 1u;
-    if (kind == KIND_VS) {
-      // v is a block offset measured from b0 + 1: key block c = b0 + 1 - v
-      cout = base - v;
-      int m1 = has_b1 && bit_at(bits1, v);
-      int m0 = v >= 1 && bit_at(bits0, v - 1);
-      mem = m0 | (m1 << 1);
-    } else {
-      cout = v;
-      mem = (int)bit_at(bits0, v) | ((int)bit_at(bits1, v) << 1);
-    }
+    cout = v;
+    mem = (int)bit_at(bits0, v) | ((int)bit_at(bits1, v) << 1);
     return true;
   }
 };
