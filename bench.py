@@ -8,9 +8,11 @@ data, then sparse attention over it. Inputs are resident in HBM before timing.
 
 Printed (one JSON line): latency per layer, the attention kernel's achieved
 MFMA TFLOP/s over the blocks and columns it computes against the bf16 peak,
-the in-house dense causal FlashAttention on the same inputs (speedup), an
-index-injected track with the pages' local-slash structure, and the CPU
-oracle timed on a bounded sample of the same workload.
+the in-house dense causal FlashAttention on the same inputs (speedup), two
+more tracks of the same layer (an index-injected one with the pages'
+local-slash structure, and a structured one on locality-latent data with the
+index built from the data), and the CPU oracle timed on a bounded sample of
+the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -43,6 +45,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-injected", action="store_true")
+    ap.add_argument("--no-structured", action="store_true")
     ap.add_argument("--dense-runs", type=int, default=1)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
@@ -161,7 +164,7 @@ def main():
     import torch
 
     from dynamic_sparse_attention_index_amd import minf
-    from workload import CONFIGS, config_kinds, injected_vs_index, planted_qkv
+    from workload import CONFIGS, STRUCTURED_LATENT, config_kinds, injected_vs_index, planted_qkv
 
     torch.cuda.set_device(0)
     cfg = CONFIGS[args.config]
@@ -198,22 +201,26 @@ def main():
 
     state = {}
 
-    def build_index():
+    def build_index(qx=None, kx=None, st=None):
+        qx = q if qx is None else qx
+        kx = k if kx is None else kx
+        st = state if st is None else st
         if vs_heads:
-            state["vi"], state["si"] = minf.minf_build_vs_index(q, k, vs_heads, last_q=cfg["last_q"], k_v=cfg["k_v"],
-                                                                k_s=cfg["k_s"], scale=scale, workspace=ws_vs)
+            st["vi"], st["si"] = minf.minf_build_vs_index(qx, kx, vs_heads, last_q=cfg["last_q"], k_v=cfg["k_v"],
+                                                          k_s=cfg["k_s"], scale=scale, workspace=ws_vs)
         if bs_heads:
-            state["bi"], state["bc"] = minf.minf_build_block_index(q, k, bs_heads, k_b=cfg["k_b"], workspace=ws_bs)
+            st["bi"], st["bc"] = minf.minf_build_block_index(qx, kx, bs_heads, k_b=cfg["k_b"], workspace=ws_bs)
 
-    def plans_from_state():
+    def plans_from_state(st=None):
+        state_ = state if st is None else st
         plans = []
         for h in range(hq):
             if kinds[h] == "vs":
                 t = vs_heads.index(h)
-                plans.append(dict(kind="vs", v_idx=state["vi"][t], s_idx=state["si"][t]))
+                plans.append(dict(kind="vs", v_idx=state_["vi"][t], s_idx=state_["si"][t]))
             elif kinds[h] == "block":
                 t = bs_heads.index(h)
-                plans.append(dict(kind="block", blk_idx=state["bi"][t], blk_cnt=state["bc"][t]))
+                plans.append(dict(kind="block", blk_idx=state_["bi"][t], blk_cnt=state_["bc"][t]))
             else:
                 plans.append(dict(kind="ashape", sink=cfg["sink"], local=cfg["local"]))
         return plans
@@ -248,31 +255,35 @@ def main():
           file=sys.stderr, flush=True)
 
     # algorithmic work of the attention launch
-    plans_t = plans_from_state()
-    blocks = cols = 0
-    per_kind = {}
-    head_work = []
     nb = (n + 63) // 64
     a_blocks = ashape_blocks(n, cfg["sink"], cfg["local"]) if "ashape" in kinds else 0
-    for h in range(hq):
-        p = plans_t[h]
-        if p["kind"] == "vs":
-            b_, c_ = vs_work(p["v_idx"], p["s_idx"], n)
-        elif p["kind"] == "block":
-            b_, c_ = int(p["blk_cnt"].long().sum()), 0
-        else:
-            b_, c_ = a_blocks, 0
-        head_work.append((b_, c_))
-        blocks += b_
-        cols += c_
-        pk = per_kind.setdefault(p["kind"], [0, 0, 0])
-        pk[0] += b_
-        pk[1] += c_
-        pk[2] += 1
+
+    def count_work(plans_x):
+        blocks_x = cols_x = 0
+        per_kind_x, head_work_x = {}, []
+        for h in range(hq):
+            p = plans_x[h]
+            if p["kind"] == "vs":
+                b_, c_ = vs_work(p["v_idx"], p["s_idx"], n)
+            elif p["kind"] == "block":
+                b_, c_ = int(p["blk_cnt"].long().sum()), 0
+            else:
+                b_, c_ = a_blocks, 0
+            head_work_x.append((b_, c_))
+            blocks_x += b_
+            cols_x += c_
+            pk = per_kind_x.setdefault(p["kind"], [0, 0, 0])
+            pk[0] += b_
+            pk[1] += c_
+            pk[2] += 1
+        dens = {kd: round((bk + cl / 64) / (cnt * nb * (nb + 1) / 2), 4) for kd, (bk, cl, cnt) in per_kind_x.items()}
+        return blocks_x, cols_x, dens, head_work_x
+
+    plans_t = plans_from_state()
+    blocks, cols, density, head_work = count_work(plans_t)
     dense_blocks = hq * nb * (nb + 1) // 2
     flop = blocks * BLOCK_FLOP + cols * COL_FLOP
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
-    density = {kd: round((bk + cl / 64) / (cnt * nb * (nb + 1) / 2), 4) for kd, (bk, cl, cnt) in per_kind.items()}
     print(f"[bench] computed blocks {blocks} + columns {cols} ({flop / 1e12:.1f} TFLOP); density {density}; "
           f"attention {attn_tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
 
@@ -336,6 +347,63 @@ def main():
         print(f"[bench] injected track: attention {inj_attn_ms:.2f} ms, "
               f"{extra['injected_track']['attn_tflops']} TFLOP/s", file=sys.stderr, flush=True)
 
+    # structured track: the same layer on locality-latent data, index built from the data
+    if not args.no_structured:
+        t1 = time.perf_counter()
+        q2, k2, v2, info2 = planted_qkv(n, hq, hkv, seed=seed, device="cuda", latent=STRUCTURED_LATENT)
+        torch.cuda.synchronize()
+        print(f"[bench] structured inputs: latent a^2={STRUCTURED_LATENT[0]} w={STRUCTURED_LATENT[1]} "
+              f"({time.perf_counter() - t1:.1f} s)", file=sys.stderr, flush=True)
+        st2 = {}
+
+        def step2(record=None):
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record(stream)
+            build_index(q2, k2, st2)
+            e1.record(stream)
+            cp2 = minf.make_plans(plans_from_state(st2))
+            minf.minf_sparse_attn(q2, k2, v2, cp2, scale=scale, out=o, lse=lse, workspace=ws_at)
+            e2.record(stream)
+            if record is not None:
+                record.append((e0, e1, e2))
+
+        step2()
+        torch.cuda.synchronize()
+        recs2 = []
+        for _ in range(max(2, args.steps)):
+            step2(recs2)
+        torch.cuda.synchronize()
+        s_idx_ms = sum(a.elapsed_time(b) for a, b, _ in recs2) / len(recs2)
+        s_attn_ms = sum(b.elapsed_time(c) for _, b, c in recs2) / len(recs2)
+        s_step_ms = sum(a.elapsed_time(c) for a, _, c in recs2) / len(recs2)
+        sb, sc, sdens, _ = count_work(plans_from_state(st2))
+        s_flop = sb * BLOCK_FLOP + sc * COL_FLOP
+        diag = {}
+        if vs_heads:
+            w_lat = STRUCTURED_LATENT[1]
+            loc = float((st2["si"] < w_lat).float().mean())
+            rc = ro = 0
+            for t, h in enumerate(vs_heads):
+                g = h // (hq // hkv)
+                cols_g = torch.tensor(info2.columns[g], device=dev, dtype=torch.int32)
+                offs = torch.tensor(info2.offsets, device=dev, dtype=torch.int32)
+                rc += int(torch.isin(cols_g, st2["vi"][t]).sum())
+                ro += int(torch.isin(offs, st2["si"][t]).sum())
+            diag = {"local_slash_frac": round(loc, 4),
+                    "planted_columns_recovered": f"{rc}/{len(vs_heads) * len(info2.columns[0])}",
+                    "planted_offsets_recovered": f"{ro}/{len(vs_heads) * len(info2.offsets)}"}
+        extra["structured_track"] = {
+            "step_ms": round(s_step_ms, 3), "index_ms": round(s_idx_ms, 3), "attn_ms": round(s_attn_ms, 3),
+            "attn_tflops": round(s_flop / (s_attn_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(s_flop / (s_attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "computed_blocks": sb, "gathered_columns": sc, "density": sdens,
+            "latent": {"a2": STRUCTURED_LATENT[0], "w": STRUCTURED_LATENT[1]}, **diag,
+        }
+        print(f"[bench] structured track: step {s_step_ms:.2f} ms (index {s_idx_ms:.3f}, attention {s_attn_ms:.2f}), "
+              f"{extra['structured_track']['attn_tflops']} TFLOP/s, density {sdens}, {diag}",
+              file=sys.stderr, flush=True)
+        del q2, k2, v2, st2
+
     dense = None
     if not args.no_dense:
         runs = []
@@ -353,8 +421,9 @@ def main():
             "speedup_step": round(dense_ms / step_ms, 3),
             "speedup_attention": round(dense_ms / attn_ms, 3),
         }
-        if "injected_track" in extra:
-            extra["injected_track"]["speedup_step_vs_dense"] = round(dense_ms / extra["injected_track"]["step_ms"], 2)
+        for trk in ("injected_track", "structured_track"):
+            if trk in extra:
+                extra[trk]["speedup_step_vs_dense"] = round(dense_ms / extra[trk]["step_ms"], 2)
         print(f"[bench] dense {dense_ms:.1f} ms ({dense['tflops']} TFLOP/s), speedup {dense['speedup_step']}x",
               file=sys.stderr, flush=True)
 

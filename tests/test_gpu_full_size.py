@@ -15,18 +15,18 @@ import torch
 
 import oracle as O
 from parity import check_lse, check_topk, max_abs, to_np
-from workload import CONFIGS, config_kinds, planted_qkv
+from workload import CONFIGS, STRUCTURED_LATENT, config_kinds, planted_qkv
 
 pytestmark = pytest.mark.gpu
 SCALE = 1 / math.sqrt(128)
 
 
-def _run_layer(minf, name):
+def _run_layer(minf, name, latent=None):
     cfg = CONFIGS[name]
     n, hq, hkv = cfg["n"], cfg["hq"], cfg["hkv"]
     kinds = config_kinds(name)
-    print(f"[case] {name}: n={n} hq={hq} hkv={hkv} kinds={kinds}", flush=True)
-    q, k, v, info = planted_qkv(n, hq, hkv, seed=1000 + cfg["index"], device="cuda")
+    print(f"[case] {name}: n={n} hq={hq} hkv={hkv} kinds={kinds} latent={latent}", flush=True)
+    q, k, v, info = planted_qkv(n, hq, hkv, seed=1000 + cfg["index"], device="cuda", latent=latent)
     vs_heads = [h for h in range(hq) if kinds[h] == "vs"]
     bs_heads = [h for h in range(hq) if kinds[h] == "block"]
     out = dict(cfg=cfg, kinds=kinds, q=q, k=k, v=v, vs_heads=vs_heads, bs_heads=bs_heads)
@@ -145,3 +145,11 @@ def test_c5_gqa_all_vs_1m(gpu_lib):
     L = _run_layer(gpu_lib, "c5_gqa_1m_vs")
     _check_vs_index(L, [0])
     _check_attention(L, [0, 13, 31], 1, seed=7)
+
+
+def test_c3_structured_latent_128k(gpu_lib):
+    # locality-latent inputs: local slashes, so most query blocks compute few key blocks
+    L = _run_layer(gpu_lib, "c3_gqa_128k", latent=STRUCTURED_LATENT)
+    _check_vs_index(L, [3, 11])
+    _check_bs_index(L, [2])
+    _check_attention(L, list(range(0, 32, 3)), 2, seed=8)

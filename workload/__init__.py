@@ -6,6 +6,7 @@ workload shapes.
 """
 from .gen import (  # noqa: F401
     CONFIGS,
+    STRUCTURED_LATENT,
     PlantInfo,
     planted_qkv,
     pattern_map,

@@ -16,6 +16,15 @@ vertical and slash structure:
 The vertical gain (a_v, b_v) is a calibrated knob: at the literal (1, 3) the
 planted columns add only ~0.27 nats to their logits and are not recoverable,
 so a calibrated value is used and recorded with each workload.
+
+Structured variant (locality latent, `latent=(a2, w)`): per KV group a latent
+X_i = sum of the w white-noise rows ending at i, divided by the square root of
+the number of rows summed, so every coordinate stays N(0, 1); then
+Q0 = a X + sqrt(1 - a^2) Z_q for each query head of the group and
+K = a X + sqrt(1 - a^2) Z_k, with a = sqrt(a2). Keys within w tokens of a
+query share part of its latent, which makes attention local (as the pages
+describe for real heads) while the marginals stay N(0, 1). The slash plant
+uses the pre-latent draw Z_q of the group's first head.
 """
 from __future__ import annotations
 
@@ -52,10 +61,23 @@ def _gen(device, seed: int) -> torch.Generator:
     return g
 
 
+def _latent(n: int, d: int, w: int, gen, device) -> torch.Tensor:
+    """Moving sum of the last w rows of an N(0, 1) draw, scaled back to unit variance."""
+    x = torch.randn((n, d), generator=gen, device=device, dtype=torch.float32)
+    x = torch.cumsum(x, dim=0)
+    if w < n:
+        x[w:] = x[w:] - x[:-w].clone()
+    cnt = torch.clamp(torch.arange(1, n + 1, device=device, dtype=torch.float32), max=float(w))
+    return x / cnt.sqrt()[:, None]
+
+
 def planted_qkv(n: int, hq: int, hkv: int, d: int = 128, seed: int = 1000, device="cpu",
                 vert_gain=None, n_vert: int = 8, slash_offsets=SLASH_OFFSETS,
-                slash_gain: float = 0.8, plant: bool = True):
-    """Q [hq, n, d], K/V [hkv, n, d] as bf16 on `device`, plus the PlantInfo."""
+                slash_gain: float = 0.8, plant: bool = True, latent=None):
+    """Q [hq, n, d], K/V [hkv, n, d] as bf16 on `device`, plus the PlantInfo.
+
+    latent: None (plain N(0, 1) draws) or (a2, w) for the locality latent.
+    """
     if hq % hkv:
         raise ValueError("hq must be a multiple of hkv")
     grp = hq // hkv
@@ -76,12 +98,19 @@ def planted_qkv(n: int, hq: int, hkv: int, d: int = 128, seed: int = 1000, devic
         span = max(1, n - 64)
         nv = min(n_vert, span)
         cols = torch.randperm(span, generator=gen, device=device)[:nv].sort().values
+        if latent is not None:
+            a = float(latent[0]) ** 0.5
+            b = (1.0 - float(latent[0])) ** 0.5
+            xg = _latent(n, d, int(latent[1]), gen, device)
+            kg.mul_(b).add_(xg, alpha=a)
         for t in range(grp):
             h = g * grp + t
             q0 = torch.randn((n, d), generator=gen, device=device, dtype=torch.float32)
             if plant and t == 0:
                 for o in offs:
                     kg[: n - o] += slash_gain * q0[o:]
+            if latent is not None:
+                q0.mul_(b).add_(xg, alpha=a)
             if plant:
                 q0 = q0 + a_v * u
             q[h] = q0.to(torch.bfloat16)
@@ -92,6 +121,8 @@ def planted_qkv(n: int, hq: int, hkv: int, d: int = 128, seed: int = 1000, devic
         v[g] = vg.to(torch.bfloat16)
         cols_all.append(cols.cpu().tolist())
         del kg, vg
+        if latent is not None:
+            del xg
     return q, k, v, PlantInfo(cols_all, offs, (a_v, b_v), slash_gain)
 
 
@@ -133,6 +164,9 @@ def injected_vs_index(n: int, k_v: int, k_s: int, planted_cols, planted_offsets,
     so = torch.tensor(sorted(ss)[:k_s], dtype=torch.int32)
     return sv, so
 
+
+# Locality-latent knobs of the structured track, fixed for every length.
+STRUCTURED_LATENT = (0.8, 32768)
 
 # Named workloads (seed = 1000 + index; pattern maps use seed + 7).
 CONFIGS = {
