@@ -89,6 +89,8 @@ int vs_max_chunks(int64_t n) { return (int)std::min<int64_t>(nblocks(n), 2048); 
 
 struct VsWs {
   float *part_m, *part_l, *row_m, *row_il, *vcol, *slsum, *dpart;
+  int32_t *tk_hist, *tk_state, *tk_cnt;
+  int tk_chunk, tk_nchunks;
   size_t bytes;
 };
 
@@ -105,6 +107,12 @@ VsWs carve_vs(void* base, int64_t n, int n_heads) {
   w.vcol = c.take<float>(nh * (size_t)n);
   w.slsum = c.take<float>(nh * (size_t)n);
   w.dpart = c.take<float>(nh * nt * 128);
+  // top-k scratch for the two score rows of every head
+  w.tk_chunk = topk_chunk_len((int)std::min<int64_t>(n, 1 << 30));
+  w.tk_nchunks = (int)((n + w.tk_chunk - 1) / w.tk_chunk);
+  w.tk_hist = c.take<int32_t>(2 * nh * 2048);
+  w.tk_state = c.take<int32_t>(2 * nh * 4);
+  w.tk_cnt = c.take<int32_t>(2 * nh * 2 * (size_t)w.tk_nchunks);
   w.bytes = c.off;
   return w;
 }
@@ -245,10 +253,19 @@ minf_status minf_build_vs_index(const void* q, const void* k, int64_t n, int hq,
   if (n_heads == 0) return MINF_OK;
   VsWs w = carve_vs(workspace, n, n_heads);
   if ((s = run_vs_scores(q, k, n, hq, hkv, heads, n_heads, last_q, scale, w, stream)) != MINF_OK) return s;
-  hipError_t e = hipSuccess;
-  if (kv_eff > 0) e = launch_topk_rows(w.vcol, n, n_heads, (int)n, kv_eff, v_idx, kv_eff, stream);
-  if (e == hipSuccess && ks_eff > 0) e = launch_topk_rows(w.slsum, n, n_heads, (int)n, ks_eff, s_idx, ks_eff, stream);
-  if (e != hipSuccess) return hip_fail(e, "VS top-k kernel");
+  TopkLaunch t{};
+  int ns = 0;
+  if (kv_eff > 0) t.seg[ns++] = TopkSeg{w.vcol, v_idx, n, kv_eff, n_heads, kv_eff};
+  if (ks_eff > 0) t.seg[ns++] = TopkSeg{w.slsum, s_idx, n, ks_eff, n_heads, ks_eff};
+  if (ns == 0) return MINF_OK;
+  t.n = (int)n;
+  t.chunk = w.tk_chunk;
+  t.nchunks = w.tk_nchunks;
+  t.hist = w.tk_hist;
+  t.state = w.tk_state;
+  t.cnt = w.tk_cnt;
+  hipError_t e = launch_topk(t, stream);
+  if (e != hipSuccess) return hip_fail(e, "VS top-k kernels");
   return MINF_OK;
 }
 

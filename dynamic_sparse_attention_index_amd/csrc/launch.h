@@ -59,8 +59,24 @@ struct VsLaunch {
 };
 
 hipError_t launch_vs_scores(const VsLaunch& a, hipStream_t stream);
-hipError_t launch_topk_rows(const float* src, int64_t src_stride, int rows, int n, int k, int32_t* dst,
-                            int64_t dst_stride, hipStream_t stream);
+
+// Top-k (ties to the lower index, ascending output) of every row of up to two
+// row sets with a common row length n, split over chunks of `chunk` entries.
+struct TopkSeg {
+  const float* src;  // row i at src + i * src_stride
+  int32_t* dst;      // row i at dst + i * dst_stride, k entries
+  int64_t src_stride, dst_stride;
+  int32_t rows, k;
+};
+struct TopkLaunch {
+  TopkSeg seg[2];
+  int32_t n, chunk, nchunks;
+  int32_t* hist;   // [rows][2048] scratch histograms
+  int32_t* state;  // [rows][4] prefix, prefix mask, rank left
+  int32_t* cnt;    // [rows][2][nchunks] keys above / equal to the threshold per chunk
+};
+int topk_chunk_len(int n);
+hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 
 // Pool heads[i] of x ([h][n][128] bf16) into slot slots[i] of out_rm ([slot][nb][128])
 // and/or out_t ([slot][128][nb]); either output may be null.

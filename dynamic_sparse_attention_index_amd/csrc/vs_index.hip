@@ -17,8 +17,9 @@
 //    probability tile along columns (complete column sums) and along its 127
 //    diagonals (per-tile partials; a diagonal spans at most two tiles and the
 //    two partials are added in tile order by a separate kernel);
-//  * top-k is a block-wide radix select on the sortable bit pattern, ties to
-//    the lower index, emitted in ascending index order.
+//  * top-k (topk.hip) is a radix select on the sortable bit pattern spread
+//    over many workgroups per row, ties to the lower index, emitted in
+//    ascending index order.
 #include <type_traits>
 
 #include "common.h"
@@ -232,21 +233,6 @@ __global__ __launch_bounds__(256) void vs_diag_reduce_kernel(const VsLaunch a) {
 }
 
 // Top-k of each row of a float matrix, ascending indices, ties to the lower index.
-__global__ __launch_bounds__(1024) void topk_rows_kernel(const float* src, int64_t src_stride, int n, int k,
-                                                         int32_t* dst, int64_t dst_stride) {
-  __shared__ int hist[2048];
-  __shared__ int scratch[64];
-  const float* x = src + (size_t)blockIdx.x * src_stride;
-  int32_t* out = dst + (size_t)blockIdx.x * dst_stride;
-  if (k <= 0) return;
-  if (k >= n) {
-    for (int i = threadIdx.x; i < n; i += 1024) out[i] = i;
-    return;
-  }
-  radix_topk_ordered<1024>([&](int i) { return sortable_key(x[i]); }, n, k, hist, scratch,
-                           [&](int pos, int i) { out[pos] = i; });
-}
-
 }  // namespace
 
 hipError_t launch_vs_scores(const VsLaunch& a, hipStream_t stream) {
@@ -260,14 +246,6 @@ hipError_t launch_vs_scores(const VsLaunch& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 g2((unsigned)((a.n + 255) / 256), a.n_slots);
   hipLaunchKernelGGL(vs_diag_reduce_kernel, g2, dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_rows(const float* src, int64_t src_stride, int rows, int n, int k, int32_t* dst,
-                            int64_t dst_stride, hipStream_t stream) {
-  if (rows <= 0 || k <= 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(rows), dim3(1024), 0, stream, src, src_stride, n, k, dst,
-                     dst_stride);
   return hipGetLastError();
 }
 
