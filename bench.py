@@ -77,6 +77,64 @@ def vs_work(v_idx, s_idx, n):
     return blocks, cols
 
 
+def useful_entries(plan, n):
+    """Attention entries the head's mask keeps (the exact set, not the computed tiles)."""
+    import torch
+    nb = (n + 63) // 64
+    kind = plan["kind"]
+    if kind == "dense":
+        return n * (n + 1) // 2
+    if kind == "ashape":
+        i = torch.arange(n, dtype=torch.int64)
+        win = torch.clamp(i + 1, max=plan["local"]) if plan["local"] > 0 else torch.zeros_like(i)
+        sink_only = torch.clamp(torch.clamp(i + 1 - win, min=0), max=plan["sink"])
+        return int((win + sink_only).sum())
+    rows_b = lambda b: torch.clamp(n - 64 * b, max=64)  # noqa: E731  rows of query block b
+    if kind == "block":
+        bi = plan["blk_idx"].long()
+        cnt = plan["blk_cnt"].long()
+        bq = torch.arange(bi.shape[0], device=bi.device)
+        valid = torch.arange(bi.shape[1], device=bi.device)[None, :] < cnt[:, None]
+        rb = rows_b(bq)
+        diag = ((bi == bq[:, None]) & valid).sum(1)
+        return int((rb * 64 * (cnt - diag) + diag * rb * (rb + 1) // 2).sum())
+    # VS: full blocks below the diagonal, the causal part of the diagonal block, and per gathered
+    # column the rows of its query block at or below it. Block b uses key blocks b - o for o in O;
+    # a partial last block of R rows uses its own offset set (offset q + 1 when dl % 64 > 0, offset
+    # q only when dl % 64 < R).
+    dev = plan["v_idx"].device
+    dl = plan["s_idx"].long()
+    dl = dl[(dl >= 0) & (dl < n)]
+    j = plan["v_idx"].long()
+    j = j[(j >= 0) & (j < n)]
+
+    def offsets(r_rows):
+        o = torch.zeros(nb + 1, dtype=torch.bool, device=dev)
+        o[(dl // 64)[dl % 64 < r_rows]] = True
+        o[(dl // 64 + 1)[dl % 64 > 0].clamp(max=nb)] = True
+        return o[:nb]
+
+    def block_entries(bq, off):
+        rb = rows_b(bq)
+        nblk = torch.cumsum(off.long(), 0)[bq]  # |{o in O : o <= b}|
+        has_diag = bool(off[0])
+        ent = int((rb * 64 * (nblk - int(has_diag))).sum()) + (int((rb * (rb + 1) // 2).sum()) if has_diag else 0)
+        cb = j // 64
+        for part in torch.split(bq, 2048):
+            rel = part[:, None] - cb[None, :]
+            keep = (rel >= 0) & ~off[rel.clamp(min=0)]
+            rpart = rows_b(part)[:, None]
+            rows = torch.where(rel == 0, 64 * part[:, None] + rpart - j[None, :], rpart.expand_as(rel))
+            ent += int((rows * keep).sum())
+        return ent
+
+    last_rows = n - 64 * (nb - 1)
+    if last_rows == 64:
+        return block_entries(torch.arange(nb, device=dev), offsets(64))
+    ent = block_entries(torch.arange(nb - 1, device=dev), offsets(64)) if nb > 1 else 0
+    return ent + block_entries(torch.tensor([nb - 1], device=dev), offsets(last_rows))
+
+
 def ashape_blocks(n, sink, local):
     nb = (n + 63) // 64
     sb = min((sink + 63) // 64, nb)
@@ -281,6 +339,7 @@ def main():
 
     plans_t = plans_from_state()
     blocks, cols, density, head_work = count_work(plans_t)
+    useful_flop = 512 * sum(useful_entries(p, n) for p in plans_t)  # 4 d flop per kept entry
     dense_blocks = hq * nb * (nb + 1) // 2
     flop = blocks * BLOCK_FLOP + cols * COL_FLOP
     attn_tflops = flop / (attn_ms * 1e-3) / 1e12
@@ -457,7 +516,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(args.config),
                      "kernel": "attn_kernel", "flop_per_launch": flop,
-                     "flop_rule": "4*64*64*128 per computed 64x64 block + 4*64*128 per gathered column per query block"},
+                     "flop_rule": "4*64*64*128 per computed 64x64 block + 4*64*128 per gathered column per query block",
+                     "useful_flop_per_launch": useful_flop,
+                     "useful_tflops": round(useful_flop / (attn_ms * 1e-3) / 1e12, 1)},
         "dense": dense,
         "cpu_baseline": cpu,
     }
