@@ -1,4 +1,4 @@
-"""CPU oracle for dynamic sparse attention in causal prefill (test infrastructure).
+"""CPU oracle for dynamic sparse attention in causal prefill and decoding (test infrastructure).
 
 Plain, slow NumPy fp64 statements of what the hot path computes. Only the
 test suite, the smoke check and the benchmark's CPU-baseline leg use this
@@ -26,4 +26,8 @@ from .minf_oracle import (  # noqa: F401
     build_block_index,
     sparse_attn,
     plan_mask_block,
+    decode_block_index,
+    decode_mask,
+    sparse_decode,
+    dense_decode,
 )

@@ -17,6 +17,10 @@ Sources (web pages, cited by title and section):
       patterns) and the unified three-step framework.
   [S] "MInference" abstract on the authors' page (offline pattern, online
       index, sparse kernels).
+  [D] the same talk transcript, fourth stage of the KV-cache lifecycle
+      (decoding is bound by loading the KV cache; load it sparsely) and its
+      closing part on dynamic sparsity in decoding (attention decomposes into
+      a top-k selection and attention over the selected keys).
 
 Readings where the pages are silent (each one is listed in the design notes):
   * softmax scale sigma = 1/sqrt(d), used in both the VS estimate and attention;
@@ -33,7 +37,12 @@ Readings where the pages are silent (each one is listed in the design notes):
   * A-shape is a token-level predicate: j < sink or i - j < local (window
     includes the diagonal), with j <= i;
   * a query row whose mask is empty outputs 0 with LSE = -inf;
-  * GQA: query head h reads KV head h // (hq // hkv).
+  * GQA: query head h reads KV head h // (hq // hkv);
+  * sparse decoding [D]: one new query row per head attends to the whole
+    cache of n keys (it is the last position); its keys are selected at
+    64-token block granularity by the same pooled-key estimate as
+    Block-Sparse, score(c) = q . mean(K_c), top-k_b blocks per query head,
+    ties to the lower block, with no forced blocks.
 """
 from __future__ import annotations
 
@@ -338,6 +347,64 @@ def sparse_attn(q, k, v, hq: int, hkv: int, scale: float, plans, rows=None):
             idx = [pos[i] for i in rs]
             out[h, idx] = o
             lse[h, idx] = l
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Sparse decoding with top-k block loads ([D]: the decode step is bound by
+# loading the KV cache, so only the keys of the top-k estimated blocks are
+# loaded and attended; the estimate is the pooled-key score of [A] "Method")
+# ---------------------------------------------------------------------------
+def decode_block_index(q_row, k, k_b: int):
+    """Top-k_b key blocks of one decode query: ascending block ids, and the scores.
+
+    score(c) = q . mean(K_c) over every 64-token block c of the cache (a partial
+    last block averages its own rows); ties go to the lower block.
+    """
+    s = pool_blocks(k) @ _f64(q_row)
+    return topk_lowidx(s, k_b), s
+
+
+def decode_mask(n: int, blocks) -> np.ndarray:
+    """Keys of the selected blocks (the decode query is the last position, so
+    every key of the cache is causally visible)."""
+    m = np.zeros(n, dtype=bool)
+    for c in np.asarray(blocks, dtype=np.int64).tolist():
+        m[BLOCK * c: BLOCK * c + BLOCK] = True
+    return m
+
+
+def sparse_decode(q, k, v, hq: int, hkv: int, scale: float, k_b: int):
+    """One decode step: q [hq, d] against the cache k/v [hkv, N, d].
+
+    Returns (blk_idx [hq, min(k_b, n_b)], O [hq, d], LSE [hq]). With k_b >= n_b
+    every block is selected and this is dense decoding.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n = k.shape[1]
+    kk = min(int(k_b), _nblocks(n))
+    idx = np.zeros((hq, kk), dtype=np.int64)
+    out = np.zeros((hq, q.shape[1]))
+    lse = np.zeros(hq)
+    for h in range(hq):
+        g = _kv_head(h, hq, hkv)
+        sel, _ = decode_block_index(q[h], k[g], kk)
+        idx[h] = sel
+        o, l = attend_rows(q[h][None, :], k[g], v[g], decode_mask(n, sel)[None, :], scale)
+        out[h], lse[h] = o[0], l[0]
+    return idx, out, lse
+
+
+def dense_decode(q, k, v, hq: int, hkv: int, scale: float):
+    """One decode step attending every key of the cache: O [hq, d], LSE [hq]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    n = k.shape[1]
+    out = np.zeros((hq, q.shape[1]))
+    lse = np.zeros(hq)
+    for h in range(hq):
+        g = _kv_head(h, hq, hkv)
+        o, l = attend_rows(q[h][None, :], k[g], v[g], np.ones((1, n), bool), scale)
+        out[h], lse[h] = o[0], l[0]
     return out, lse
 
 

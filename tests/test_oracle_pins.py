@@ -330,3 +330,58 @@ def test_empty_rows_give_zero_and_neg_inf():
 def test_bf16_inputs_upcast_exactly():
     x = torch.randn(16, 8).to(torch.bfloat16)
     np.testing.assert_array_equal(O.minf_oracle._f64(x.float().numpy()), x.double().numpy())
+
+
+# ---------------------------------------------------------------------------
+# sparse decoding (one query row per head against the cache)
+# ---------------------------------------------------------------------------
+def test_decode_full_budget_equals_last_row_of_causal_sdpa():
+    # a decode query is the last position: full budget must equal the last row of
+    # causal prefill attention computed by the library routine in fp64
+    rng = np.random.default_rng(11)
+    n, hq, hkv, d = 200, 4, 2, 16
+    q = rng.standard_normal((hq, n, d))
+    k = rng.standard_normal((hkv, n, d))
+    v = rng.standard_normal((hkv, n, d))
+    scale = 1 / math.sqrt(d)
+    idx, o, lse = O.sparse_decode(q[:, -1], k, v, hq, hkv, scale, k_b=10)
+    assert idx.shape == (hq, 4) and all(list(r) == [0, 1, 2, 3] for r in idx)
+    qt = torch.from_numpy(q)
+    kt = torch.from_numpy(np.repeat(k, hq // hkv, axis=0))
+    vt = torch.from_numpy(np.repeat(v, hq // hkv, axis=0))
+    want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=scale)[:, -1]
+    assert np.abs(o - want.numpy()).max() < 1e-12
+    od, ld = O.dense_decode(q[:, -1], k, v, hq, hkv, scale)
+    assert np.abs(od - o).max() < 1e-12 and np.abs(ld - lse).max() < 1e-12
+
+
+def test_decode_block_scores_equal_mean_of_raw_scores_and_selection_is_brute_force():
+    # commutativity of pooling with the product: q . mean(K_c) = mean_j (q . k_j);
+    # selection against a full sort of those raw means; mask by explicit loops
+    rng = np.random.default_rng(12)
+    n, d = 300, 8
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((n, d))
+    sel, s = O.decode_block_index(q, k, 3)
+    raw = [np.mean([q @ k[j] for j in range(64 * c, min(64 * c + 64, n))]) for c in range(5)]
+    assert np.allclose(s, raw, rtol=1e-12, atol=1e-12)
+    order = sorted(range(5), key=lambda c: (-raw[c], c))[:3]
+    assert list(sel) == sorted(order)
+    m = O.decode_mask(n, sel)
+    for j in range(n):
+        assert m[j] == (j // 64 in order)
+
+
+def test_decode_output_is_softmax_over_selected_keys_brute_force():
+    rng = np.random.default_rng(13)
+    n, d = 150, 4
+    q = rng.standard_normal((1, d))
+    k = rng.standard_normal((1, n, d))
+    v = rng.standard_normal((1, n, d))
+    idx, o, lse = O.sparse_decode(q, k, v, 1, 1, 0.5, k_b=1)
+    keys = [j for j in range(n) if j // 64 == idx[0, 0]]
+    w = [math.exp(0.5 * sum(q[0, t] * k[0, j, t] for t in range(d))) for j in keys]
+    z = sum(w)
+    want = [sum(w[a] * v[0, keys[a], t] for a in range(len(keys))) / z for t in range(d)]
+    assert np.allclose(o[0], want, rtol=1e-12, atol=1e-12)
+    assert abs(lse[0] - math.log(z)) < 1e-12
