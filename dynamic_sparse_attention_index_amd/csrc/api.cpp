@@ -483,3 +483,133 @@ minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o
 }
 
 }  // extern "C"
+
+// ---------------- decoding
+namespace {
+
+constexpr int kMaxDecodeGroup = 8;
+
+struct DecWs {
+  float* scores;
+  int32_t* blk;
+  float* part;
+  size_t bytes;
+};
+
+DecWs carve_decode(void* base, int64_t n, int hq, int kb, bool select) {
+  Carver c{(char*)base};
+  DecWs w{};
+  const size_t nb = (size_t)nblocks(n);
+  const int nsplit = (kb + decode_blocks_per_split(kb, hq) - 1) / decode_blocks_per_split(kb, hq);
+  if (select) {
+    w.scores = c.take<float>((size_t)hq * nb);
+    w.blk = c.take<int32_t>((size_t)hq * kb);
+  }
+  w.part = c.take<float>((size_t)hq * nsplit * (kHeadDim + 2));
+  w.bytes = c.off;
+  return w;
+}
+
+minf_status check_decode(const void* q, const void* k, const void* v, void* o, int64_t n, int hq, int hkv, int d,
+                         float scale) {
+  minf_status s;
+  if ((s = check_common(q, k, n, hq, hkv, d, (int64_t)kDecMaxBlocks * kBlock)) != MINF_OK) return s;
+  if (!v || !o) return fail(MINF_E_INVALID_ARG, "v and o must be non-null device pointers");
+  if (hq / hkv > kMaxDecodeGroup)
+    return fail(MINF_E_UNSUPPORTED, "decoding supports at most %d query heads per KV head", kMaxDecodeGroup);
+  return check_scale(scale);
+}
+
+minf_status run_decode(const void* q, const void* k, const void* v, const float* kbar_t, int64_t n, int hq, int hkv,
+                       float scale, int kb_eff, bool select, int32_t* blk_idx, void* o, float* lse, const DecWs& w,
+                       hipStream_t stream) {
+  DecodeLaunch a{};
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.kbar_t = kbar_t;
+  a.scores = w.scores;
+  a.blk = select ? (blk_idx ? blk_idx : w.blk) : nullptr;
+  a.part = w.part;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.n = (int)n;
+  a.nb = (int)nblocks(n);
+  a.hq = hq;
+  a.hkv = hkv;
+  a.grp = hq / hkv;
+  a.kb = kb_eff;
+  a.bps = decode_blocks_per_split(kb_eff, hq);
+  a.nsplit = (kb_eff + a.bps - 1) / a.bps;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = launch_decode(a, select, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode kernels");
+  return MINF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+minf_status minf_decode_pool_keys(const void* k, int64_t n, int hkv, int d, int first_block, float* kbar_t,
+                                  hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_common(k, k, n, hkv, hkv, d, (int64_t)kDecMaxBlocks * kBlock)) != MINF_OK) return s;
+  if (!kbar_t) return fail(MINF_E_INVALID_ARG, "kbar_t must be non-null");
+  if (first_block < 0) return fail(MINF_E_INVALID_ARG, "first_block must be >= 0");
+  if (first_block >= nblocks(n)) return MINF_OK;
+  std::vector<int32_t> heads(hkv);
+  for (int i = 0; i < hkv; ++i) heads[i] = i;
+  hipError_t e = launch_block_pool((const uint16_t*)k, (int)n, heads.data(), heads.data(), hkv, nullptr, kbar_t,
+                                   stream, first_block);
+  if (e != hipSuccess) return hip_fail(e, "key pooling kernel");
+  return MINF_OK;
+}
+
+size_t minf_decode_workspace_size(int64_t n, int hq, int k_b) {
+  if (n < 1 || hq < 1 || k_b < 1) return 0;
+  const int64_t nb = nblocks(n);
+  const bool select = k_b < nb;
+  const int kb_eff = (int)std::min<int64_t>(k_b, nb);
+  return carve_decode(nullptr, n, hq, kb_eff, select).bytes;
+}
+
+minf_status minf_sparse_decode(const void* q, const void* k, const void* v, const float* kbar_t, int64_t n, int hq,
+                               int hkv, int d, float scale, int k_b, int32_t* blk_idx, void* o, float* lse,
+                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_decode(q, k, v, o, n, hq, hkv, d, scale)) != MINF_OK) return s;
+  if (k_b < 1) return fail(MINF_E_INVALID_ARG, "k_b must be >= 1");
+  const int64_t nb = nblocks(n);
+  const bool select = k_b < nb;
+  const int kb_eff = (int)std::min<int64_t>(k_b, nb);
+  if (select && !kbar_t) return fail(MINF_E_INVALID_ARG, "kbar_t must be non-null when k_b < n_b");
+  DecWs w = carve_decode(workspace, n, hq, kb_eff, select);
+  if ((s = check_ws(workspace, ws_bytes, w.bytes)) != MINF_OK) return s;
+  w = carve_decode(workspace, n, hq, kb_eff, select);
+  if ((s = run_decode(q, k, v, kbar_t, n, hq, hkv, scale, kb_eff, select, blk_idx, o, lse, w, stream)) != MINF_OK)
+    return s;
+  if (!select && blk_idx) {
+    // full budget: every block, in order
+    hipError_t e = launch_iota_rows(blk_idx, hq, kb_eff, stream);
+    if (e != hipSuccess) return hip_fail(e, "full block list");
+  }
+  return MINF_OK;
+}
+
+minf_status minf_dense_decode(const void* q, const void* k, const void* v, int64_t n, int hq, int hkv, int d,
+                              float scale, void* o, float* lse, void* workspace, size_t ws_bytes,
+                              hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_decode(q, k, v, o, n, hq, hkv, d, scale)) != MINF_OK) return s;
+  const int kb_eff = (int)nblocks(n);
+  DecWs w = carve_decode(workspace, n, hq, kb_eff, false);
+  if ((s = check_ws(workspace, ws_bytes, w.bytes)) != MINF_OK) return s;
+  w = carve_decode(workspace, n, hq, kb_eff, false);
+  return run_decode(q, k, v, nullptr, n, hq, hkv, scale, kb_eff, false, nullptr, o, lse, w, stream);
+}
+
+}  // extern "C"

@@ -25,7 +25,7 @@ struct PoolLaunch {
   const uint16_t* x;
   float* out_rm;  // [nh][nb][128] or null
   float* out_t;   // [nh][128][nb] or null
-  int32_t n, nb, nh;
+  int32_t n, nb, nh, b0;
   int32_t heads[kMaxPoolHeads];
   int32_t slots[kMaxPoolHeads];
 };
@@ -33,7 +33,7 @@ struct PoolLaunch {
 __global__ __launch_bounds__(256) void block_pool_kernel(const PoolLaunch a) {
   __shared__ float part[16][kHeadDim];
   const int tid = threadIdx.x;
-  const int b = blockIdx.x;
+  const int b = blockIdx.x + a.b0;
   const int h = a.heads[blockIdx.y];
   const int slot = a.slots[blockIdx.y];
   const int64_t r0 = (int64_t)b * kBlock;
@@ -115,8 +115,9 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
 }  // namespace
 
 hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, const int32_t* slots, int n_heads,
-                             float* out_rm, float* out_t, hipStream_t stream) {
+                             float* out_rm, float* out_t, hipStream_t stream, int first_block) {
   const int nb = (n + kBlock - 1) / kBlock;
+  if (first_block < 0 || first_block >= nb) return hipSuccess;
   for (int base = 0; base < n_heads; base += kMaxPoolHeads) {
     const int c = n_heads - base < kMaxPoolHeads ? n_heads - base : kMaxPoolHeads;
     PoolLaunch a{};
@@ -126,11 +127,12 @@ hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, con
     a.n = n;
     a.nb = nb;
     a.nh = c;
+    a.b0 = first_block;
     for (int i = 0; i < c; ++i) {
       a.heads[i] = heads[base + i];
       a.slots[i] = slots[base + i];
     }
-    hipLaunchKernelGGL(block_pool_kernel, dim3(nb, c), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(block_pool_kernel, dim3(nb - first_block, c), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

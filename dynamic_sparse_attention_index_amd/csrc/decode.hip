@@ -1,0 +1,239 @@
+// Sparse decoding with top-k block loads for gfx950.
+//
+// What is computed ("KV-cache-centric efficient long-context methods" talk
+// transcript: in the decoding stage loading the KV cache is the bottleneck and
+// can be done sparsely, and decode attention splits into a top-k selection and
+// attention over the selected keys; MInference 1.0 article, "Method": the
+// pooled-key block estimate): one new query row per head attends to a cache
+// of n keys. Each query head scores every 64-token block c of its KV head by
+// q . mean(K_c), keeps the top-k_b blocks (ties to the lower block, ascending)
+// and attends exactly over their keys. k_b >= n_b is dense decoding.
+//
+// Layout of the work (memory bound: the point is to load few K/V rows):
+//  * scores: one thread per block, the pooled keys stored [d][n_b] so that a
+//    wave reads 64 consecutive blocks per dimension; the group's queries sit
+//    in LDS and are read by broadcast, so every pooled vector is read once per
+//    KV head;
+//  * top-k: one workgroup per head, scores as sortable keys in LDS, the shared
+//    block radix select;
+//  * attention: split over the selected blocks (flash-decoding style); a wave
+//    takes one 64-key block at a time, 16 lanes per key row with 16-byte
+//    loads, online softmax in fp32; the four waves of a workgroup merge their
+//    partials in LDS and each split writes (max, sum, o[128]);
+//  * combine: per head, the splits in a fixed order (no float atomics).
+#include "common.h"
+#include "launch.h"
+
+namespace minf {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecMaxGroup = 8;  // query heads per KV head handled by one score workgroup
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// scores[h][c] = sum_d q_h[d] * kbar_t[g][d][c], d ascending, for the heads of KV head g
+__global__ __launch_bounds__(kDecThreads) void decode_score_kernel(const DecodeLaunch a) {
+  __shared__ float qs[kHeadDim][kDecMaxGroup];
+  const int g = blockIdx.y;
+  const int h0 = g * a.grp;
+  for (int x = threadIdx.x; x < kHeadDim * kDecMaxGroup; x += kDecThreads) {
+    const int d = x / kDecMaxGroup, t = x % kDecMaxGroup;
+    qs[d][t] = t < a.grp ? __builtin_bit_cast(float, (uint32_t)a.q[(size_t)(h0 + t) * kHeadDim + d] << 16) : 0.f;
+  }
+  __syncthreads();
+  const int c = blockIdx.x * kDecThreads + threadIdx.x;
+  if (c >= a.nb) return;
+  const float* kt = a.kbar_t + (size_t)g * kHeadDim * a.nb + c;
+  float acc[kDecMaxGroup];
+#pragma unroll
+  for (int t = 0; t < kDecMaxGroup; ++t) acc[t] = 0.f;
+  for (int d = 0; d < kHeadDim; ++d) {
+    const float kv = kt[(size_t)d * a.nb];
+#pragma unroll
+    for (int t = 0; t < kDecMaxGroup; ++t) acc[t] = fmaf(qs[d][t], kv, acc[t]);
+  }
+  for (int t = 0; t < a.grp; ++t) a.scores[(size_t)(h0 + t) * a.nb + c] = acc[t];
+}
+
+// top-k_b blocks of one head (n_b <= kDecMaxBlocks), ascending
+__global__ __launch_bounds__(1024) void decode_topk_kernel(const DecodeLaunch a) {
+  __shared__ uint32_t keys[kDecMaxBlocks];
+  __shared__ int hist[2048];
+  __shared__ int scratch[64];
+  const int h = blockIdx.x;
+  const float* s = a.scores + (size_t)h * a.nb;
+  for (int c = threadIdx.x; c < a.nb; c += 1024) keys[c] = sortable_key(s[c]);
+  __syncthreads();
+  int32_t* out = a.blk + (size_t)h * a.kb;
+  radix_topk_ordered<1024>([&](int i) { return keys[i]; }, a.nb, a.kb, hist, scratch,
+                           [&](int pos, int i) { out[pos] = i; });
+}
+
+__global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(const DecodeLaunch a) {
+  __shared__ float wo[4][kHeadDim];
+  __shared__ float wm[4], wl[4];
+  const int h = blockIdx.y;
+  const int sp = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kr = lane >> 4;  // key row within a group of four
+  const int dc = lane & 15;  // 8-dim chunk
+  const int g = h / a.grp;
+  const uint16_t* kh = a.k + (size_t)g * a.n * kHeadDim;
+  const uint16_t* vh = a.v + (size_t)g * a.n * kHeadDim;
+  float qf[8];
+  {
+    const u32x4 w = *(const u32x4*)(a.q + (size_t)h * kHeadDim + 8 * dc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[2 * e] = bf16_lo(w[e]);
+      qf[2 * e + 1] = bf16_hi(w[e]);
+    }
+  }
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  const int e0 = sp * a.bps;
+  const int e1 = min(a.kb, e0 + a.bps);
+  for (int ent = e0 + wave; ent < e1; ent += 4) {
+    const int c = a.blk ? a.blk[(size_t)h * a.kb + ent] : ent;
+    const int64_t j0 = (int64_t)c * kBlock;
+    u32x4 kw[16], vw[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int64_t j = j0 + 4 * it + kr;
+      const bool ok = j < a.n;
+      kw[it] = ok ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
+      vw[it] = ok ? *(const u32x4*)(vh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
+    }
+    float s[16];
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p = fmaf(qf[2 * e], bf16_lo(kw[it][e]), p);
+        p = fmaf(qf[2 * e + 1], bf16_hi(kw[it][e]), p);
+      }
+      // the 16 lanes of a key row hold its 8-dim partials: butterfly over them
+      p += __shfl_xor(p, 8);
+      p += __shfl_xor(p, 4);
+      p += __shfl_xor(p, 2);
+      p += __shfl_xor(p, 1);
+      s[it] = (j0 + 4 * it + kr < a.n) ? p * a.scale_log2 : -INFINITY;
+    }
+    float mb = s[0];
+#pragma unroll
+    for (int it = 1; it < 16; ++it) mb = fmaxf(mb, s[it]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float m_new = fmaxf(m, mb);
+    const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const float p = fast_exp2(s[it] - m_new);
+      l += p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] = fmaf(p, bf16_lo(vw[it][e]), o[2 * e]);
+        o[2 * e + 1] = fmaf(p, bf16_hi(vw[it][e]), o[2 * e + 1]);
+      }
+    }
+    m = m_new;
+  }
+  // the four key-row groups of the wave hold disjoint keys: add them up
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    o[e] += __shfl_xor(o[e], 16);
+    o[e] += __shfl_xor(o[e], 32);
+  }
+  if (kr == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wo[wave][8 * dc + e] = o[e];
+  }
+  if (lane == 0) {
+    wm[wave] = m;
+    wl[wave] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x < kHeadDim) {
+    const int d = threadIdx.x;
+    float mm = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    float ls = 0.f, os = 0.f;
+    if (mm != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = wm[w] == -INFINITY ? 0.f : fast_exp2(wm[w] - mm);
+        ls += wl[w] * f;
+        os += wo[w][d] * f;
+      }
+    }
+    float* pp = a.part + ((size_t)h * a.nsplit + sp) * (kHeadDim + 2);
+    pp[2 + d] = os;
+    if (d == 0) {
+      pp[0] = mm;
+      pp[1] = ls;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const DecodeLaunch a) {
+  const int h = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* pp = a.part + (size_t)h * a.nsplit * (kHeadDim + 2);
+  float mm = -INFINITY;
+  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, pp[(size_t)s * (kHeadDim + 2)]);
+  float ls = 0.f, os = 0.f;
+  if (mm != -INFINITY) {
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float* x = pp + (size_t)s * (kHeadDim + 2);
+      const float f = x[0] == -INFINITY ? 0.f : fast_exp2(x[0] - mm);
+      ls += x[1] * f;
+      os += x[2 + d] * f;
+    }
+  }
+  const float out = ls > 0.f ? os / ls : 0.f;
+  a.o[(size_t)h * kHeadDim + d] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
+  if (d == 0 && a.lse) a.lse[h] = ls > 0.f ? (mm + log2f(ls)) * 0.69314718055994531f : -INFINITY;
+}
+
+__global__ __launch_bounds__(256) void iota_rows_kernel(int32_t* dst, int cols) {
+  int32_t* row = dst + (size_t)blockIdx.y * cols;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c < cols) row[c] = c;
+}
+
+}  // namespace
+
+hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(iota_rows_kernel, dim3((cols + 255) / 256, rows), dim3(256), 0, stream, dst, cols);
+  return hipGetLastError();
+}
+
+int decode_blocks_per_split(int kb, int hq) {
+  const long long want = ((long long)kb * hq + 1023) / 1024;  // about 1024 splits in total
+  int bps = (int)((want + 3) / 4 * 4);
+  return bps < 4 ? 4 : bps;
+}
+
+hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream) {
+  if (a.grp > kDecMaxGroup || a.nb > kDecMaxBlocks) return hipErrorInvalidValue;
+  if (select) {
+    hipLaunchKernelGGL(decode_score_kernel, dim3((a.nb + kDecThreads - 1) / kDecThreads, a.hkv),
+                       dim3(kDecThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_topk_kernel, dim3(a.hq), dim3(1024), 0, stream, a);
+  }
+  hipLaunchKernelGGL(decode_attn_kernel, dim3(a.nsplit, a.hq), dim3(kDecThreads), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq), dim3(kHeadDim), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace minf

@@ -79,9 +79,29 @@ int topk_chunk_len(int n);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 
 // Pool heads[i] of x ([h][n][128] bf16) into slot slots[i] of out_rm ([slot][nb][128])
-// and/or out_t ([slot][128][nb]); either output may be null.
+// and/or out_t ([slot][128][nb]); either output may be null. Blocks below
+// first_block are left untouched.
 hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, const int32_t* slots, int n_heads,
-                             float* out_rm, float* out_t, hipStream_t stream);
+                             float* out_rm, float* out_t, hipStream_t stream, int first_block = 0);
+
+// Decoding: one query row per head against a cache of n keys.
+constexpr int kDecMaxBlocks = 16384;  // n_b limit of the single-workgroup block top-k
+struct DecodeLaunch {
+  const uint16_t* q;     // [hq][128]
+  const uint16_t* k;     // [hkv][n][128]
+  const uint16_t* v;
+  const float* kbar_t;   // [hkv][128][nb] block means of K
+  float* scores;         // [hq][nb]
+  int32_t* blk;          // [hq][kb] selected blocks; null: entry e is block e (dense)
+  float* part;           // [hq][nsplit][130]: max (log2 units), sum, o[128]
+  uint16_t* o;           // [hq][128]
+  float* lse;            // [hq] or null
+  int32_t n, nb, hq, hkv, grp, kb, nsplit, bps;
+  float scale_log2;
+};
+int decode_blocks_per_split(int kb, int hq);
+hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream);
+hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream);
 // Scores and top-k for n_heads pooled query heads (qbar slots 0..n_heads-1), head i
 // reading pooled keys kbar_t slot kvslot[i]; writes blk_idx/blk_cnt slot i.
 hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,

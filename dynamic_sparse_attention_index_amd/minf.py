@@ -67,6 +67,10 @@ def _load():
         "minf_sparse_attn_workspace_size": (sz, [i64, i32]),
         "minf_sparse_attn": (i32, [vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, ctypes.POINTER(HeadPlan), vp, sz, vp]),
         "minf_dense_attn": (i32, [vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, i32, vp]),
+        "minf_decode_pool_keys": (i32, [vp, i64, i32, i32, i32, vp, vp]),
+        "minf_decode_workspace_size": (sz, [i64, i32, i32]),
+        "minf_sparse_decode": (i32, [vp, vp, vp, vp, i64, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]),
+        "minf_dense_decode": (i32, [vp, vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -243,4 +247,50 @@ def minf_dense_attn(q, k, v, scale=None, causal=True, out=None, lse=None, with_l
         lse = torch.empty((hq, n), dtype=torch.float32, device=q.device)
     _check(_lib.minf_dense_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), n, hq, hkv, d, _scale(scale, d),
                                 1 if causal else 0, _stream(stream)))
+    return o, lse
+
+
+def minf_decode_pool_keys(k, first_block=0, out=None, stream=None):
+    """Block means of K for decoding: float32 [hkv, d, n_b] (blocks >= first_block recomputed)."""
+    _need(k, torch.bfloat16, "k")
+    hkv, n, d = k.shape
+    nb = (n + 63) // 64
+    kbar_t = torch.empty((hkv, d, nb), dtype=torch.float32, device=k.device) if out is None else out
+    _check(_lib.minf_decode_pool_keys(_ptr(k), n, hkv, d, int(first_block), _ptr(kbar_t), _stream(stream)))
+    return kbar_t
+
+
+def minf_sparse_decode(q, k, v, kbar_t, k_b, scale=None, out=None, lse=None, blk_idx=None, with_index=True,
+                       workspace=None, stream=None):
+    """One decode step: q [hq, d] against the cache k/v [hkv, n, d].
+
+    Returns (o [hq, d] bf16, lse [hq] float32, blk_idx [hq, min(k_b, n_b)] int32 or None).
+    """
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, nm)
+    hq, d = q.shape
+    hkv, n, _ = k.shape
+    nb = (n + 63) // 64
+    kk = min(int(k_b), nb)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq,), dtype=torch.float32, device=q.device) if lse is None else lse
+    if blk_idx is None and with_index:
+        blk_idx = torch.empty((hq, kk), dtype=torch.int32, device=q.device)
+    ws, wsb = _workspace(_lib.minf_decode_workspace_size(n, hq, int(k_b)), q.device, workspace)
+    _check(_lib.minf_sparse_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(kbar_t), n, hq, hkv, d, _scale(scale, d),
+                                   int(k_b), _ptr(blk_idx), _ptr(o), _ptr(lse), _ptr(ws), wsb, _stream(stream)))
+    return o, lse, blk_idx
+
+
+def minf_dense_decode(q, k, v, scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Dense decoding baseline: (o [hq, d] bf16, lse [hq] float32)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, torch.bfloat16, nm)
+    hq, d = q.shape
+    hkv, n, _ = k.shape
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((hq,), dtype=torch.float32, device=q.device) if lse is None else lse
+    ws, wsb = _workspace(_lib.minf_decode_workspace_size(n, hq, (n + 63) // 64), q.device, workspace)
+    _check(_lib.minf_dense_decode(_ptr(q), _ptr(k), _ptr(v), n, hq, hkv, d, _scale(scale, d), _ptr(o), _ptr(lse),
+                                  _ptr(ws), wsb, _stream(stream)))
     return o, lse

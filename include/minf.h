@@ -177,6 +177,49 @@ minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o
                             int64_t n, int hq, int hkv, int d, float scale, int causal,
                             hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Sparse decoding with top-k block loads ("KV-cache-centric efficient
+ * long-context methods" talk transcript: in decoding, loading the KV cache is
+ * the bottleneck and can be done sparsely; decode attention splits into a
+ * top-k selection and attention over the selected keys. The block estimate is
+ * the pooled-key score of the MInference 1.0 article, "Method").
+ *
+ * One new query row per head (q: [hq][d] bf16) attends to a cache of n keys
+ * (K, V: [hkv][n][d] bf16, the new token's own key already appended at n - 1;
+ * the query is the last position, so every cached key is visible). With
+ * n_b = ceil(n / 64):
+ *   score_h(c) = q_h . Kbar_g[c], Kbar_g[c] = mean of K_g over block c (a
+ *   partial last block averages its own rows);
+ *   blocks_h = top-min(k_b, n_b) of score_h, ties to the lower c, ascending;
+ *   O_h = softmax over the keys of blocks_h of scale * q_h . k_j, applied to V
+ *   (fp32 softmax and accumulation, bf16 output); LSE_h its natural log-sum-exp.
+ * k_b >= n_b selects every block (dense decoding; kbar_t may then be NULL).
+ * n is at most 16384 * 64 and hq / hkv at most 8 (else MINF_E_UNSUPPORTED).
+ * ---------------------------------------------------------------------- */
+
+/* Block means of K for the decode estimate: kbar_t is device float
+ * [hkv][d][n_b] (dimension-major). Blocks c >= first_block are (re)computed,
+ * the others are left as they are, so after appending tokens only the last
+ * block needs first_block = n_b - 1. */
+minf_status minf_decode_pool_keys(const void* k, int64_t n, int hkv, int d, int first_block, float* kbar_t,
+                                  hipStream_t stream);
+
+/* Workspace for minf_sparse_decode with this budget (k_b >= n_b: dense). */
+size_t minf_decode_workspace_size(int64_t n, int hq, int k_b);
+
+/* blk_idx  device int32 [hq][min(k_b, n_b)] (ascending block ids) or NULL.
+ * o        device bf16 [hq][d].  lse  device float [hq] or NULL.
+ * k_b >= 1. workspace: at least minf_decode_workspace_size(n, hq, k_b). */
+minf_status minf_sparse_decode(const void* q, const void* k, const void* v, const float* kbar_t, int64_t n, int hq,
+                               int hkv, int d, float scale, int k_b, int32_t* blk_idx, void* o, float* lse,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Dense decoding baseline: every key of the cache. Workspace: at least
+ * minf_decode_workspace_size(n, hq, n_b). */
+minf_status minf_dense_decode(const void* q, const void* k, const void* v, int64_t n, int hq, int hkv, int d,
+                              float scale, void* o, float* lse, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -126,9 +126,40 @@ def test_sparse_attn_rejects():
 
 def test_python_binding_names_match_c():
     for name in ("minf_build_vs_index", "minf_build_block_index", "minf_sparse_attn", "minf_dense_attn",
-                 "minf_vs_scores", "minf_block_pool"):
+                 "minf_vs_scores", "minf_block_pool", "minf_decode_pool_keys", "minf_sparse_decode",
+                 "minf_dense_decode"):
         assert callable(getattr(minf, name))
 
 
 def test_default_scale():
     assert minf._scale(None, 128) == pytest.approx(1 / math.sqrt(128))
+
+
+def test_decode_workspace_and_rejects():
+    assert LIB.minf_decode_workspace_size(0, 32, 64) == 0
+    sparse = LIB.minf_decode_workspace_size(1 << 20, 32, 64)
+    dense = LIB.minf_decode_workspace_size(1 << 20, 32, 16384)
+    # scores [hq][n_b] + selected blocks + split partials; dense needs no scores
+    assert sparse >= 32 * 16384 * 4 + 32 * 64 * 4 and sparse % 256 == 0
+    assert 0 < dense < sparse + 32 * 1024 * 130 * 4
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, kb=FAKE, n=4096, hq=4, hkv=1, d=128, scale=0.1, k_b=8, idx=None, o=FAKE,
+                 ws=FAKE, wsb=None)
+        a.update(kw)
+        wsb = LIB.minf_decode_workspace_size(a["n"], a["hq"], a["k_b"]) if a["wsb"] is None else a["wsb"]
+        return LIB.minf_sparse_decode(a["q"], a["k"], a["v"], a["kb"], a["n"], a["hq"], a["hkv"], a["d"],
+                                      a["scale"], a["k_b"], a["idx"], a["o"], None, a["ws"], wsb, None)
+
+    assert call(k_b=0) == INVALID
+    assert call(kb=None) == INVALID          # pooled keys needed when k_b < n_b
+    assert call(o=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(wsb=64) == WORKSPACE
+    assert call(hq=16) == UNSUPPORTED        # more than 8 query heads per KV head
+    assert call(d=64) == UNSUPPORTED
+    assert call(n=16384 * 64 + 1) == UNSUPPORTED
+    assert call(scale=-1.0) == INVALID
+    assert LIB.minf_decode_pool_keys(FAKE, 4096, 1, 128, -1, FAKE, None) == INVALID
+    assert LIB.minf_decode_pool_keys(FAKE, 4096, 1, 128, 0, None, None) == INVALID
+    assert LIB.minf_dense_decode(FAKE, FAKE, None, 4096, 4, 1, 128, 0.1, FAKE, None, FAKE, 1 << 20, None) == INVALID

@@ -1,0 +1,122 @@
+"""Sparse decoding through the C ABI against the CPU oracle.
+
+The decode query of each head is the last query row of a planted workload (the
+new token), the cache is the workload's K/V. Bars: the pooled key means within
+fp32 rounding of the oracle's; block index sets exact under the margin rule;
+bf16 outputs within max-abs 2e-2 of the fp64 oracle on the selected blocks;
+LSE within 2e-3; dense and full-budget decoding identical; repeated calls
+bitwise identical.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity import check_lse, check_topk, max_abs, to_np
+from workload import planted_qkv
+
+pytestmark = pytest.mark.gpu
+SCALE = 1 / math.sqrt(128)
+
+
+def _case(n, hq, hkv, seed):
+    print(f"[case] decode n={n} hq={hq} hkv={hkv} seed={seed}", flush=True)
+    q, k, v, _ = planted_qkv(n, hq, hkv, seed=seed, device="cuda")
+    return q[:, -1].contiguous(), k, v
+
+
+def _check_selection_and_output(qd, k, v, blk, o, lse, k_b):
+    hq, hkv = qd.shape[0], k.shape[0]
+    n = k.shape[1]
+    exact = 0
+    qn = to_np(qd)
+    cache = {}
+    for h in range(hq):
+        g = h // (hq // hkv)
+        if g not in cache:
+            cache.clear()
+            cache[g] = (to_np(k[g]), to_np(v[g]))
+        kg, vg = cache[g]
+        sel, s = O.decode_block_index(qn[h], kg, k_b)
+        kbar = O.pool_blocks(kg)
+        abs_tol = 1e-5 * float(np.abs(qn[h]).astype(np.float64) @ np.abs(kbar).max(axis=0))
+        got = blk[h].cpu().numpy()
+        exact += check_topk(s, got, k_b, abs_tol=abs_tol, want=sel)
+        # attention over the GPU's (valid) selection
+        wo, wl = O.attend_rows(qn[h][None, :], kg, vg, O.decode_mask(n, got)[None, :], SCALE)
+        assert max_abs(to_np(o[h]), wo[0]) <= 2e-2, h
+        check_lse(lse[h:h + 1].cpu().numpy(), wl)
+    return exact
+
+
+@pytest.mark.parametrize("n", [700, 4096])
+def test_decode_pool_keys_and_incremental_update(gpu_lib, n):
+    _, k, _ = _case(n, 2, 2, seed=41)
+    kt = gpu_lib.minf_decode_pool_keys(k)
+    torch.cuda.synchronize()
+    for g in range(2):
+        want = O.pool_blocks(to_np(k[g]))  # [n_b, d]
+        got = kt[g].cpu().numpy().T
+        assert np.allclose(got, want, rtol=1e-5, atol=1e-6)
+    # append-style update: change the last block's rows, recompute only that block
+    nb = (n + 63) // 64
+    k2 = k.clone()
+    k2[:, 64 * (nb - 1):] = torch.randn_like(k2[:, 64 * (nb - 1):].float()).to(torch.bfloat16)
+    part = gpu_lib.minf_decode_pool_keys(k2, first_block=nb - 1, out=kt.clone())
+    full = gpu_lib.minf_decode_pool_keys(k2)
+    torch.cuda.synchronize()
+    assert torch.equal(part, full)
+
+
+@pytest.mark.parametrize("n,hq,hkv,k_b", [(700, 8, 2, 3), (4096, 8, 2, 8), (33000, 8, 2, 40), (20000, 8, 1, 1)])
+def test_sparse_decode_matches_oracle(gpu_lib, n, hq, hkv, k_b):
+    qd, k, v = _case(n, hq, hkv, seed=42 + n)
+    kt = gpu_lib.minf_decode_pool_keys(k)
+    o, lse, blk = gpu_lib.minf_sparse_decode(qd, k, v, kt, k_b, scale=SCALE)
+    torch.cuda.synchronize()
+    exact = _check_selection_and_output(qd, k, v, blk, o, lse, k_b)
+    print(f"  {exact} of {hq} block lists unambiguous", flush=True)
+    # repeated calls are bitwise identical
+    o2, lse2, blk2 = gpu_lib.minf_sparse_decode(qd, k, v, kt, k_b, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(blk, blk2) and torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+@pytest.mark.parametrize("n", [100, 5000])
+def test_dense_decode_and_full_budget(gpu_lib, n):
+    qd, k, v = _case(n, 4, 2, seed=43)
+    od, ld = gpu_lib.minf_dense_decode(qd, k, v, scale=SCALE)
+    kt = gpu_lib.minf_decode_pool_keys(k)
+    nb = (n + 63) // 64
+    of, lf, bf = gpu_lib.minf_sparse_decode(qd, k, v, kt, nb + 5, scale=SCALE)
+    torch.cuda.synchronize()
+    wo, wl = O.dense_decode(to_np(qd), to_np(k), to_np(v), 4, 2, SCALE)
+    assert max_abs(to_np(od), wo) <= 2e-2
+    check_lse(ld.cpu().numpy(), wl)
+    assert torch.equal(od, of) and torch.equal(ld, lf)
+    assert bf.shape == (4, nb) and all(bf[h].tolist() == list(range(nb)) for h in range(4))
+
+
+def test_sparse_decode_full_size_1m(gpu_lib):
+    n, hq, hkv, k_b = 1 << 20, 32, 8, 64
+    qd, k, v = _case(n, hq, hkv, seed=1004)
+    kt = gpu_lib.minf_decode_pool_keys(k)
+    o, lse, blk = gpu_lib.minf_sparse_decode(qd, k, v, kt, k_b, scale=SCALE)
+    torch.cuda.synchronize()
+    # sampled heads, each against its own KV head
+    for h in (0, 13, 31):
+        g = h // (hq // hkv)
+        kg, vg = to_np(k[g]), to_np(v[g])
+        qh = to_np(qd[h])
+        sel, s = O.decode_block_index(qh, kg, k_b)
+        kbar = O.pool_blocks(kg)
+        abs_tol = 1e-5 * float(np.abs(qh).astype(np.float64) @ np.abs(kbar).max(axis=0))
+        got = blk[h].cpu().numpy()
+        check_topk(s, got, k_b, abs_tol=abs_tol, want=sel)
+        wo, wl = O.attend_rows(qh[None, :], kg, vg, O.decode_mask(n, got)[None, :], SCALE)
+        err = max_abs(to_np(o[h]), wo[0])
+        assert err <= 2e-2, (h, err)
+        check_lse(lse[h:h + 1].cpu().numpy(), wl)
+        print(f"  head {h}: max-abs {err:.2e}", flush=True)
