@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-injected", action="store_true")
     ap.add_argument("--no-structured", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-blocks", type=int, default=64,
+                    help="decode budget in 64-token blocks (64 blocks = 4096 tokens)")
     ap.add_argument("--dense-runs", type=int, default=1)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
@@ -485,6 +488,55 @@ def main():
                 extra[trk]["speedup_step_vs_dense"] = round(dense_ms / extra[trk]["step_ms"], 2)
         print(f"[bench] dense {dense_ms:.1f} ms ({dense['tflops']} TFLOP/s), speedup {dense['speedup_step']}x",
               file=sys.stderr, flush=True)
+
+    # decoding on the same cache: the last query row of every head is the new token
+    if not args.no_decode:
+        qd = q[:, -1].contiguous()
+        kt = minf.minf_decode_pool_keys(k)
+        k_b = args.decode_blocks
+        nb_ = (n + 63) // 64
+        od = torch.empty_like(qd)
+        ld = torch.empty((hq,), dtype=torch.float32, device=dev)
+        blk = torch.empty((hq, min(k_b, nb_)), dtype=torch.int32, device=dev)
+        ws_s = torch.empty(max(1, minf.library().minf_decode_workspace_size(n, hq, k_b)), dtype=torch.uint8,
+                           device=dev)
+        ws_d = torch.empty(max(1, minf.library().minf_decode_workspace_size(n, hq, nb_)), dtype=torch.uint8,
+                           device=dev)
+
+        def timed(fn, reps=50):
+            fn()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        sparse_us = 1e3 * timed(lambda: minf.minf_sparse_decode(qd, k, v, kt, k_b, scale=scale, out=od, lse=ld,
+                                                                blk_idx=blk, workspace=ws_s))
+        dense_us = 1e3 * timed(lambda: minf.minf_dense_decode(qd, k, v, scale=scale, out=od, lse=ld, workspace=ws_d))
+        pool_us = 1e3 * timed(lambda: minf.minf_decode_pool_keys(k, first_block=nb_ - 1, out=kt))
+        row = 128 * 2 * 2  # one key row of K and V, bf16
+        dense_bytes = hkv * n * row
+        sel_rows = int(sum(min(64, n - 64 * c) for c in blk.flatten().tolist()))
+        sparse_bytes = sel_rows * row + hkv * nb_ * 128 * 4 + hq * nb_ * 4 * 2
+        extra["decode"] = {
+            "k_b": k_b, "tokens_loaded_per_head": sel_rows // hq,
+            "sparse_us": round(sparse_us, 2), "dense_us": round(dense_us, 2),
+            "speedup": round(dense_us / sparse_us, 2),
+            "dense_hbm_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+            "sparse_algorithmic_bytes": sparse_bytes,
+            "sparse_hbm_gbs": round(sparse_bytes / (sparse_us * 1e-6) / 1e9, 1),
+            "append_pool_us": round(pool_us, 2),
+            "note": "one new query row per head against the cache; top-k_b 64-token blocks by the pooled-key score; "
+                    "dense loads every K/V row of every KV head",
+        }
+        print(f"[bench] decode: sparse {sparse_us:.1f} us (k_b={k_b}), dense {dense_us:.1f} us "
+              f"({extra['decode']['dense_hbm_gbs']} GB/s), speedup {extra['decode']['speedup']}x",
+              file=sys.stderr, flush=True)
+        del kt, ws_s, ws_d
 
     cpu = None
     if not args.no_cpu:

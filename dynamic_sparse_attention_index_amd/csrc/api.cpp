@@ -496,11 +496,18 @@ struct DecWs {
   size_t bytes;
 };
 
+// Dense decoding serves up to four heads per workgroup, so it has up to four
+// times fewer workgroup rows than sparse decoding.
+int decode_split_len(int kb, int hq, bool select) {
+  return decode_blocks_per_split(kb, select ? hq : std::max(1, hq / 4));
+}
+
 DecWs carve_decode(void* base, int64_t n, int hq, int kb, bool select) {
   Carver c{(char*)base};
   DecWs w{};
   const size_t nb = (size_t)nblocks(n);
-  const int nsplit = (kb + decode_blocks_per_split(kb, hq) - 1) / decode_blocks_per_split(kb, hq);
+  const int bps = decode_split_len(kb, hq, select);
+  const int nsplit = (kb + bps - 1) / bps;
   if (select) {
     w.scores = c.take<float>((size_t)hq * nb);
     w.blk = c.take<int32_t>((size_t)hq * kb);
@@ -539,7 +546,7 @@ minf_status run_decode(const void* q, const void* k, const void* v, const float*
   a.hkv = hkv;
   a.grp = hq / hkv;
   a.kb = kb_eff;
-  a.bps = decode_blocks_per_split(kb_eff, hq);
+  a.bps = decode_split_len(kb_eff, hq, select);
   a.nsplit = (kb_eff + a.bps - 1) / a.bps;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = launch_decode(a, select, stream);

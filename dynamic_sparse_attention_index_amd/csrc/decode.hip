@@ -19,7 +19,8 @@
 //  * attention: split over the selected blocks (flash-decoding style); a wave
 //    takes one 64-key block at a time, 16 lanes per key row with 16-byte
 //    loads, online softmax in fp32; the four waves of a workgroup merge their
-//    partials in LDS and each split writes (max, sum, o[128]);
+//    partials in LDS and each split writes (max, sum, o[128]); dense decoding
+//    serves up to four heads of a GQA group from each loaded row;
 //  * combine: per head, the splits in a fixed order (no float atomics).
 #include "common.h"
 #include "launch.h"
@@ -30,6 +31,10 @@ namespace {
 constexpr int kDecThreads = 256;
 constexpr int kDecMaxGroup = 8;  // query heads per KV head handled by one score workgroup
 
+__device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float c) {
+  typedef __attribute__((__vector_size__(2 * sizeof(short)))) short s16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b), c, false);
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
@@ -71,111 +76,123 @@ __global__ __launch_bounds__(1024) void decode_topk_kernel(const DecodeLaunch a)
                            [&](int pos, int i) { out[pos] = i; });
 }
 
+// G query heads of one KV head per workgroup: G = 1 for sparse decoding (each
+// head has its own blocks), G = up to 4 heads of a GQA group for dense
+// decoding (they read the same rows, so every K/V row is loaded once for all
+// of them). A wave takes one 64-key block at a time, in two halves of 32 keys.
+template <int G>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(const DecodeLaunch a) {
-  __shared__ float wo[4][kHeadDim];
-  __shared__ float wm[4], wl[4];
-  const int h = blockIdx.y;
+  __shared__ float wo[4][G][kHeadDim];
+  __shared__ float wm[4][G], wl[4][G];
   const int sp = blockIdx.x;
+  const int h0 = blockIdx.y * G;  // first query head of this workgroup
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kr = lane >> 4;  // key row within a group of four
   const int dc = lane & 15;  // 8-dim chunk
-  const int g = h / a.grp;
+  const int g = h0 / a.grp;
   const uint16_t* kh = a.k + (size_t)g * a.n * kHeadDim;
   const uint16_t* vh = a.v + (size_t)g * a.n * kHeadDim;
-  float qf[8];
-  {
-    const u32x4 w = *(const u32x4*)(a.q + (size_t)h * kHeadDim + 8 * dc);
+  u32x4 qw[G];  // this lane's 8 dims of each head's query, bf16 pairs
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[2 * e] = bf16_lo(w[e]);
-      qf[2 * e + 1] = bf16_hi(w[e]);
-    }
+  for (int t = 0; t < G; ++t) qw[t] = *(const u32x4*)(a.q + (size_t)(h0 + t) * kHeadDim + 8 * dc);
+  float m[G], l[G], o[G][8];
+#pragma unroll
+  for (int t = 0; t < G; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[t][e] = 0.f;
   }
-  float m = -INFINITY, l = 0.f, o[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = 0.f;
   const int e0 = sp * a.bps;
   const int e1 = min(a.kb, e0 + a.bps);
   for (int ent = e0 + wave; ent < e1; ent += 4) {
-    const int c = a.blk ? a.blk[(size_t)h * a.kb + ent] : ent;
-    const int64_t j0 = (int64_t)c * kBlock;
-    u32x4 kw[16], vw[16];
+    const int c = a.blk ? a.blk[(size_t)h0 * a.kb + ent] : ent;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const int64_t j0 = (int64_t)c * kBlock + 32 * half;
+      u32x4 kw[8], vw[8];
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int64_t j = j0 + 4 * it + kr;
-      const bool ok = j < a.n;
-      kw[it] = ok ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
-      vw[it] = ok ? *(const u32x4*)(vh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
-    }
-    float s[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p = fmaf(qf[2 * e], bf16_lo(kw[it][e]), p);
-        p = fmaf(qf[2 * e + 1], bf16_hi(kw[it][e]), p);
+      for (int it = 0; it < 8; ++it) {
+        const int64_t j = j0 + 4 * it + kr;
+        const bool ok = j < a.n;
+        kw[it] = ok ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
+        vw[it] = ok ? *(const u32x4*)(vh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
       }
-      // the 16 lanes of a key row hold its 8-dim partials: butterfly over them
-      p += __shfl_xor(p, 8);
-      p += __shfl_xor(p, 4);
-      p += __shfl_xor(p, 2);
-      p += __shfl_xor(p, 1);
-      s[it] = (j0 + 4 * it + kr < a.n) ? p * a.scale_log2 : -INFINITY;
-    }
-    float mb = s[0];
 #pragma unroll
-    for (int it = 1; it < 16; ++it) mb = fmaxf(mb, s[it]);
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    const float m_new = fmaxf(m, mb);
-    const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
-    l *= alpha;
+      for (int t = 0; t < G; ++t) {
+        float s[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+        for (int it = 0; it < 8; ++it) {
+          // bf16 x bf16 products are exact in fp32; v_dot2 adds each pair in fp32
+          float p = 0.f;
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const float p = fast_exp2(s[it] - m_new);
-      l += p;
+          for (int e = 0; e < 4; ++e) p = dot_bf16x2(qw[t][e], kw[it][e], p);
+          // the 16 lanes of a key row hold its 8-dim partials: butterfly over them
+          p += __shfl_xor(p, 8);
+          p += __shfl_xor(p, 4);
+          p += __shfl_xor(p, 2);
+          p += __shfl_xor(p, 1);
+          s[it] = (j0 + 4 * it + kr < a.n) ? p * a.scale_log2 : -INFINITY;
+        }
+        float mb = s[0];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = fmaf(p, bf16_lo(vw[it][e]), o[2 * e]);
-        o[2 * e + 1] = fmaf(p, bf16_hi(vw[it][e]), o[2 * e + 1]);
+        for (int it = 1; it < 8; ++it) mb = fmaxf(mb, s[it]);
+        mb = fmaxf(mb, __shfl_xor(mb, 16));
+        mb = fmaxf(mb, __shfl_xor(mb, 32));
+        const float m_new = fmaxf(m[t], mb);
+        if (m_new == -INFINITY) continue;  // nothing visible yet (rows past n)
+        const float alpha = m[t] == -INFINITY ? 0.f : fast_exp2(m[t] - m_new);
+        l[t] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[t][e] *= alpha;
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const float p = fast_exp2(s[it] - m_new);
+          l[t] += p;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[t][2 * e] = fmaf(p, bf16_lo(vw[it][e]), o[t][2 * e]);
+            o[t][2 * e + 1] = fmaf(p, bf16_hi(vw[it][e]), o[t][2 * e + 1]);
+          }
+        }
+        m[t] = m_new;
       }
     }
-    m = m_new;
   }
-  // the four key-row groups of the wave hold disjoint keys: add them up
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    o[e] += __shfl_xor(o[e], 16);
-    o[e] += __shfl_xor(o[e], 32);
-  }
-  if (kr == 0) {
+  for (int t = 0; t < G; ++t) {
+    // the four key-row groups of the wave hold disjoint keys: add them up
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) wo[wave][8 * dc + e] = o[e];
-  }
-  if (lane == 0) {
-    wm[wave] = m;
-    wl[wave] = l;
+    for (int e = 0; e < 8; ++e) {
+      o[t][e] += __shfl_xor(o[t][e], 16);
+      o[t][e] += __shfl_xor(o[t][e], 32);
+    }
+    if (kr == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wo[wave][t][8 * dc + e] = o[t][e];
+    }
+    if (lane == 0) {
+      wm[wave][t] = m[t];
+      wl[wave][t] = l[t];
+    }
   }
   __syncthreads();
-  if (threadIdx.x < kHeadDim) {
-    const int d = threadIdx.x;
-    float mm = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  for (int x = threadIdx.x; x < G * kHeadDim; x += kDecThreads) {
+    const int t = x / kHeadDim, d = x % kHeadDim;
+    const float mm = fmaxf(fmaxf(wm[0][t], wm[1][t]), fmaxf(wm[2][t], wm[3][t]));
     float ls = 0.f, os = 0.f;
     if (mm != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float f = wm[w] == -INFINITY ? 0.f : fast_exp2(wm[w] - mm);
-        ls += wl[w] * f;
-        os += wo[w][d] * f;
+        const float f = wm[w][t] == -INFINITY ? 0.f : fast_exp2(wm[w][t] - mm);
+        ls += wl[w][t] * f;
+        os += wo[w][t][d] * f;
       }
     }
-    float* pp = a.part + ((size_t)h * a.nsplit + sp) * (kHeadDim + 2);
+    float* pp = a.part + ((size_t)(h0 + t) * a.nsplit + sp) * (kHeadDim + 2);
     pp[2 + d] = os;
     if (d == 0) {
       pp[0] = mm;
@@ -218,8 +235,11 @@ hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream
   return hipGetLastError();
 }
 
-int decode_blocks_per_split(int kb, int hq) {
-  const long long want = ((long long)kb * hq + 1023) / 1024;  // about 1024 splits in total
+// Blocks per split for `rows` workgroup rows (query heads, or head groups for
+// dense decoding): about 2048 workgroups in total, whole multiples of the 4
+// waves of a workgroup.
+int decode_blocks_per_split(int kb, int rows) {
+  const long long want = ((long long)kb * rows + 2047) / 2048;
   int bps = (int)((want + 3) / 4 * 4);
   return bps < 4 ? 4 : bps;
 }
@@ -231,7 +251,15 @@ hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream)
                        dim3(kDecThreads), 0, stream, a);
     hipLaunchKernelGGL(decode_topk_kernel, dim3(a.hq), dim3(1024), 0, stream, a);
   }
-  hipLaunchKernelGGL(decode_attn_kernel, dim3(a.nsplit, a.hq), dim3(kDecThreads), 0, stream, a);
+  if (a.blk) {
+    hipLaunchKernelGGL(decode_attn_kernel<1>, dim3(a.nsplit, a.hq), dim3(kDecThreads), 0, stream, a);
+  } else if (a.grp % 4 == 0) {
+    hipLaunchKernelGGL(decode_attn_kernel<4>, dim3(a.nsplit, a.hq / 4), dim3(kDecThreads), 0, stream, a);
+  } else if (a.grp % 2 == 0) {
+    hipLaunchKernelGGL(decode_attn_kernel<2>, dim3(a.nsplit, a.hq / 2), dim3(kDecThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(decode_attn_kernel<1>, dim3(a.nsplit, a.hq), dim3(kDecThreads), 0, stream, a);
+  }
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq), dim3(kHeadDim), 0, stream, a);
   return hipGetLastError();
 }

@@ -99,7 +99,7 @@ struct DecodeLaunch {
   int32_t n, nb, hq, hkv, grp, kb, nsplit, bps;
   float scale_log2;
 };
-int decode_blocks_per_split(int kb, int hq);
+int decode_blocks_per_split(int kb, int rows);
 hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream);
 // Scores and top-k for n_heads pooled query heads (qbar slots 0..n_heads-1), head i
