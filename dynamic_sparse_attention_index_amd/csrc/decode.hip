@@ -54,6 +54,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(const DecodeL
   float acc[kDecMaxGroup];
 #pragma unroll
   for (int t = 0; t < kDecMaxGroup; ++t) acc[t] = 0.f;
+#pragma unroll 16
   for (int d = 0; d < kHeadDim; ++d) {
     const float kv = kt[(size_t)d * a.nb];
 #pragma unroll
@@ -201,24 +202,49 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(const DecodeLa
   }
 }
 
-__global__ __launch_bounds__(kHeadDim) void decode_combine_kernel(const DecodeLaunch a) {
+// Per head: merge the splits. Thread (r, d) takes splits s = r, r + 8, ... for
+// dimension d; the eight partial sums are then added in r order.
+constexpr int kCombRows = 8;
+__global__ __launch_bounds__(kCombRows * kHeadDim) void decode_combine_kernel(const DecodeLaunch a) {
+  __shared__ float red_m[kCombRows * kHeadDim];
+  __shared__ float part_l[kCombRows], part_o[kCombRows][kHeadDim];
   const int h = blockIdx.x;
-  const int d = threadIdx.x;
-  const float* pp = a.part + (size_t)h * a.nsplit * (kHeadDim + 2);
+  const int d = threadIdx.x % kHeadDim;
+  const int r = threadIdx.x / kHeadDim;
+  const int stride = kHeadDim + 2;
+  const float* pp = a.part + (size_t)h * a.nsplit * stride;
   float mm = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, pp[(size_t)s * (kHeadDim + 2)]);
+  for (int s = threadIdx.x; s < a.nsplit; s += kCombRows * kHeadDim) mm = fmaxf(mm, pp[(size_t)s * stride]);
+  red_m[threadIdx.x] = mm;
+  __syncthreads();
+  for (int off = kCombRows * kHeadDim / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red_m[threadIdx.x] = fmaxf(red_m[threadIdx.x], red_m[threadIdx.x + off]);
+    __syncthreads();
+  }
+  mm = red_m[0];
   float ls = 0.f, os = 0.f;
   if (mm != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float* x = pp + (size_t)s * (kHeadDim + 2);
+#pragma unroll 4
+    for (int s = r; s < a.nsplit; s += kCombRows) {
+      const float* x = pp + (size_t)s * stride;
       const float f = x[0] == -INFINITY ? 0.f : fast_exp2(x[0] - mm);
       ls += x[1] * f;
       os += x[2 + d] * f;
     }
   }
-  const float out = ls > 0.f ? os / ls : 0.f;
+  part_o[r][d] = os;
+  if (d == 0) part_l[r] = ls;
+  __syncthreads();
+  if (r != 0) return;
+  float lt = 0.f, ot = 0.f;
+#pragma unroll
+  for (int q = 0; q < kCombRows; ++q) {
+    lt += part_l[q];
+    ot += part_o[q][d];
+  }
+  const float out = lt > 0.f ? ot / lt : 0.f;
   a.o[(size_t)h * kHeadDim + d] = (uint16_t)(pack_bf16x2(out, 0.f) & 0xffffu);
-  if (d == 0 && a.lse) a.lse[h] = ls > 0.f ? (mm + log2f(ls)) * 0.69314718055994531f : -INFINITY;
+  if (d == 0 && a.lse) a.lse[h] = lt > 0.f ? (mm + log2f(lt)) * 0.69314718055994531f : -INFINITY;
 }
 
 __global__ __launch_bounds__(256) void iota_rows_kernel(int32_t* dst, int cols) {
@@ -260,7 +286,7 @@ hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream)
   } else {
     hipLaunchKernelGGL(decode_attn_kernel<1>, dim3(a.nsplit, a.hq), dim3(kDecThreads), 0, stream, a);
   }
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq), dim3(kHeadDim), 0, stream, a);
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.hq), dim3(kCombRows * kHeadDim), 0, stream, a);
   return hipGetLastError();
 }
 
