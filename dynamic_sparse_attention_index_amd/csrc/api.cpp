@@ -180,7 +180,8 @@ minf_status check_vs_args(const void* q, const void* k, int64_t n, int hq, int h
 
 // ---------------- BS workspace
 struct BsWs {
-  float *qbar, *kbar_t;
+  float *qbar, *kbar_t, *scores;
+  int rows;
   size_t bytes;
 };
 
@@ -190,6 +191,8 @@ BsWs carve_bs(void* base, int64_t n, int hkv, int n_heads) {
   BsWs w;
   w.qbar = c.take<float>((size_t)std::max(n_heads, 1) * nb * kHeadDim);
   w.kbar_t = c.take<float>((size_t)std::max(std::min(hkv, std::max(n_heads, 1)), 1) * nb * kHeadDim);
+  w.rows = block_score_rows((int)nb, std::max(std::min(n_heads, 64), 1));
+  w.scores = c.take<float>((size_t)std::max(std::min(n_heads, 64), 1) * w.rows * nb);
   w.bytes = c.off;
   return w;
 }
@@ -304,7 +307,9 @@ minf_status minf_build_block_index(const void* q, const void* k, int64_t n, int 
   if (e == hipSuccess)
     e = launch_block_pool((const uint16_t*)k, (int)n, kv_heads.data(), kv_slots.data(), (int)kv_heads.size(),
                           nullptr, w.kbar_t, stream);
-  if (e == hipSuccess) e = launch_block_topk(w.qbar, w.kbar_t, kv_slot.data(), n_heads, nb, k_b, blk_idx, blk_cnt, stream);
+  if (e == hipSuccess)
+    e = launch_block_topk(w.qbar, w.kbar_t, kv_slot.data(), n_heads, nb, k_b, blk_idx, blk_cnt, w.scores, w.rows,
+                          stream);
   if (e != hipSuccess) return hip_fail(e, "block index kernels");
   return MINF_OK;
 }

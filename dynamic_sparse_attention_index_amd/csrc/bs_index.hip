@@ -10,9 +10,14 @@
 //  * pooling: one workgroup per (head, 64-row block); 16 threads span a row
 //    with 16-byte loads, fp32 sums in a fixed order. K is pooled once per KV
 //    head, into a [d][n_b] layout so that the score pass reads it coalesced.
-//  * scores + top-k: one workgroup per (head, query block); the row's scores
-//    live in LDS (up to 16384 blocks = 64 KiB), each a fixed-order fp32 dot
-//    product, followed by the shared radix select.
+//  * scores: 64 x 64 tiles of the lower triangle (query blocks x key blocks)
+//    staged through LDS, so every pooled vector is read once per tile rather
+//    than once per query block; each score is a fixed-order fp32 dot product,
+//    written to a score buffer that holds a bounded band of rows at a time;
+//  * top-k: one workgroup per (head, query block); the row's scores are copied
+//    to LDS (up to 16384 blocks = 64 KiB) for the shared radix select.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -72,22 +77,90 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const PoolLaunch a) {
 struct BsTopkLaunch {
   const float* qbar;    // [nh][nb][128]
   const float* kbar_t;  // [nkv][128][nb]
+  float* scores;        // [nh][rows][nb]: rows r0 .. r0 + rows - 1 of this round
   int32_t* blk_idx;     // [nh][nb][k_b]
   int32_t* blk_cnt;     // [nh][nb]
-  int32_t nb, k_b, nh;
+  int32_t nb, k_b, nh, r0, rows;
   int32_t kvslot[kMaxPoolHeads];
   int32_t outslot[kMaxPoolHeads];
 };
 
 constexpr int kMaxBlocks = (int)(kMaxTokens / kBlock);
+constexpr int kTile = 64;
 
+// Pooled scores of one 64 x 64 tile (query blocks x key blocks) of the lower
+// triangle: each output is a fixed-order fp32 dot product over d = 0..127.
+// Thread (ty, tx) owns query blocks 4ty..4ty+3 and key blocks 4tx..4tx+3.
+__global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) {
+  __shared__ __attribute__((aligned(16))) float qs[kHeadDim][kTile];
+  __shared__ __attribute__((aligned(16))) float ks[kHeadDim][kTile];
+  const int ct = blockIdx.x;
+  const int bt = a.r0 / kTile + (int)blockIdx.z;
+  if (ct > bt) return;  // above the block diagonal
+  const int hs = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int b0 = bt * kTile, c0 = ct * kTile;
+  {
+    // query tile, transposed into [d][row]
+    const int r = tid >> 2, dq = (tid & 3) * 32;
+    const bool ok = b0 + r < a.nb;
+    const float* src = a.qbar + ((size_t)hs * a.nb + (ok ? b0 + r : 0)) * kHeadDim + dq;
+#pragma unroll
+    for (int e = 0; e < 32; e += 4) {
+      const float4 x = ok ? *(const float4*)(src + e) : float4{0.f, 0.f, 0.f, 0.f};
+      qs[dq + e][r] = x.x;
+      qs[dq + e + 1][r] = x.y;
+      qs[dq + e + 2][r] = x.z;
+      qs[dq + e + 3][r] = x.w;
+    }
+    // key tile straight from the [d][nb] layout
+    const int d = tid >> 1, cq = (tid & 1) * 32;
+    const float* kt = a.kbar_t + ((size_t)a.kvslot[hs] * kHeadDim + d) * a.nb;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int c = c0 + cq + e;
+      ks[d][cq + e] = c < a.nb ? kt[c] : 0.f;
+    }
+  }
+  __syncthreads();
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll 8
+  for (int d = 0; d < kHeadDim; ++d) {
+    const float4 qv = *(const float4*)&qs[d][4 * ty];
+    const float4 kv = *(const float4*)&ks[d][4 * tx];
+    const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
+    const float kb[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(qa[i], kb[j], acc[i][j]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = b0 + 4 * ty + i;
+    if (b >= a.nb || b >= a.r0 + a.rows) continue;
+    float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + 4 * tx + j;
+      if (c <= b) row[c] = acc[i][j];
+    }
+  }
+}
+
+// Top-k_b key blocks of every query block of the round, from the stored scores.
 __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   __shared__ float sc[kMaxBlocks];
-  __shared__ float qb[kHeadDim];
   __shared__ int hist[2048];
   __shared__ int scratch[16];
   const int tid = threadIdx.x;
-  const int b = a.nb - 1 - (int)blockIdx.x;  // longest rows first
+  const int r_end = a.r0 + a.rows < a.nb ? a.r0 + a.rows : a.nb;
+  const int b = r_end - 1 - (int)blockIdx.x;  // longest rows first
   const int hs = blockIdx.y;
   const int slot = a.outslot[hs];
   const int kb = a.k_b;
@@ -99,14 +172,8 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
     for (int c = tid; c <= b; c += 256) out[c] = c;
     return;
   }
-  if (tid < kHeadDim) qb[tid] = a.qbar[((size_t)hs * a.nb + b) * kHeadDim + tid];
-  __syncthreads();
-  const float* kt = a.kbar_t + (size_t)a.kvslot[hs] * kHeadDim * a.nb;
-  for (int c = tid; c <= b; c += 256) {
-    float acc = 0.f;
-    for (int d = 0; d < kHeadDim; ++d) acc = fmaf(qb[d], kt[(size_t)d * a.nb + c], acc);
-    sc[c] = acc;
-  }
+  const float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
+  for (int c = tid; c <= b; c += 256) sc[c] = row[c];
   __syncthreads();
   radix_topk_ordered<256>([&](int i) { return sortable_key(sc[i]); }, b + 1, kb, hist, scratch,
                           [&](int pos, int i) { out[pos] = i; });
@@ -139,25 +206,43 @@ hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, con
   return hipSuccess;
 }
 
+int block_score_rows(int nb, int n_heads) {
+  // bound the score buffer to about 512 MiB; whole 64-row tiles
+  const long long per_row = (long long)std::max(n_heads, 1) * nb * 4;
+  long long r = (512ll << 20) / per_row / kTile * kTile;
+  if (r < kTile) r = kTile;
+  return (int)std::min<long long>(r, ((long long)nb + kTile - 1) / kTile * kTile);
+}
+
 hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
-                             int k_b, int32_t* blk_idx, int32_t* blk_cnt, hipStream_t stream) {
+                             int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
+                             hipStream_t stream) {
+  const int nbt = (nb + kTile - 1) / kTile;
   for (int base = 0; base < n_heads; base += kMaxPoolHeads) {
     const int c = n_heads - base < kMaxPoolHeads ? n_heads - base : kMaxPoolHeads;
     BsTopkLaunch a{};
     a.qbar = qbar + (size_t)base * nb * kHeadDim;
     a.kbar_t = kbar_t;
+    a.scores = scores;
     a.blk_idx = blk_idx;
     a.blk_cnt = blk_cnt;
     a.nb = nb;
     a.k_b = k_b;
     a.nh = c;
+    a.rows = rows;
     for (int i = 0; i < c; ++i) {
       a.kvslot[i] = kvslot[base + i];
       a.outslot[i] = base + i;
     }
-    hipLaunchKernelGGL(block_topk_kernel, dim3(nb, c), dim3(256), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    for (int r0 = 0; r0 < nb; r0 += rows) {
+      a.r0 = r0;
+      const int row_tiles = (std::min(nb, r0 + rows) - r0 + kTile - 1) / kTile;
+      const int col_tiles = std::min(nbt, (r0 + rows) / kTile);
+      hipLaunchKernelGGL(block_score_kernel, dim3(col_tiles, c, row_tiles), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(block_topk_kernel, dim3(std::min(rows, nb - r0), c), dim3(256), 0, stream, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

@@ -104,7 +104,9 @@ hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream
 hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream);
 // Scores and top-k for n_heads pooled query heads (qbar slots 0..n_heads-1), head i
 // reading pooled keys kbar_t slot kvslot[i]; writes blk_idx/blk_cnt slot i.
+int block_score_rows(int nb, int n_heads);
 hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
-                             int k_b, int32_t* blk_idx, int32_t* blk_cnt, hipStream_t stream);
+                             int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
+                             hipStream_t stream);
 
 }  // namespace minf

@@ -141,6 +141,14 @@ def test_c3_gqa_mixed_128k(gpu_lib):
     _check_attention(L, list(range(32)), 1, seed=6)
 
 
+def test_c4_gqa_mixed_512k(gpu_lib):
+    # 8 Block-Sparse heads at 8192 blocks: the pooled-score buffer is filled in several row bands
+    L = _run_layer(gpu_lib, "c4_gqa_512k")
+    _check_bs_index(L, [5])
+    _check_vs_index(L, [11])
+    _check_attention(L, list(range(0, 32, 5)), 1, seed=9)
+
+
 def test_c5_gqa_all_vs_1m(gpu_lib):
     L = _run_layer(gpu_lib, "c5_gqa_1m_vs")
     _check_vs_index(L, [0])
