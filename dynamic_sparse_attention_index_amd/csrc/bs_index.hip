@@ -113,14 +113,12 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
       qs[dq + e + 2][r] = x.z;
       qs[dq + e + 3][r] = x.w;
     }
-    // key tile straight from the [d][nb] layout
-    const int d = tid >> 1, cq = (tid & 1) * 32;
-    const float* kt = a.kbar_t + ((size_t)a.kvslot[hs] * kHeadDim + d) * a.nb;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int c = c0 + cq + e;
-      ks[d][cq + e] = c < a.nb ? kt[c] : 0.f;
-    }
+    // key tile straight from the [d][nb] layout: a wave reads 64 consecutive blocks of one d
+    const int cl = tid & 63, d0 = tid >> 6;
+    const float* kt = a.kbar_t + (size_t)a.kvslot[hs] * kHeadDim * a.nb + c0 + cl;
+    const bool cok = c0 + cl < a.nb;
+#pragma unroll 8
+    for (int d = d0; d < kHeadDim; d += 4) ks[d][cl] = cok ? kt[(size_t)d * a.nb] : 0.f;
   }
   __syncthreads();
   const int ty = tid >> 4, tx = tid & 15;
@@ -145,10 +143,13 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
     const int b = b0 + 4 * ty + i;
     if (b >= a.nb || b >= a.r0 + a.rows) continue;
     float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
+    const int c = c0 + 4 * tx;
+    if (c + 3 <= b && (a.nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
+      *(float4*)(row + c) = float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + 4 * tx + j;
-      if (c <= b) row[c] = acc[i][j];
+      for (int j = 0; j < 4; ++j)
+        if (c + j <= b) row[c + j] = acc[i][j];
     }
   }
 }
