@@ -30,14 +30,15 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int KSTR = 136;
-constexpr int PSTR = 65;  // floats per probability-tile row in LDS
+constexpr int PSTR = 65;   // floats per probability-tile row in LDS
+constexpr int PROWS = 32;  // query rows of the probability tile staged at a time
 
 struct VsSmem1 {
   uint16_t kt[kBlock * KSTR];
 };
 struct VsSmem2 {
   uint16_t kt[kBlock * KSTR];
-  float pt[4][kBlock * PSTR];
+  float pt[4][PROWS * PSTR];
 };
 
 template <int PASS>
@@ -81,22 +82,35 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
     }
   }
 
+  // K tiles: 16 threads per 256-byte row, rows kr + 16 i; the next tile is
+  // loaded into registers while the current one is worked on
+  const int dc = tid & 15;
+  const int kr = tid >> 4;
+  u32x4 kn[4];
+  auto load_tile = [&](int T) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t j = (int64_t)T * kBlock + kr + 16 * i;
+      kn[i] = j < n ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(sm.kt + (kr + 16 * i) * KSTR + 8 * dc) = kn[i];
+  };
+
   const int t0 = ch * a.tiles_per_chunk;
   const int t1 = t0 + a.tiles_per_chunk < a.ntiles ? t0 + a.tiles_per_chunk : a.ntiles;
+  if (t0 < t1) {
+    load_tile(t0);
+    store_tile();
+  }
+  __syncthreads();
   for (int T = t0; T < t1; ++T) {
-    // stage the K tile (16 threads per row)
-    {
-      const int dc = tid & 15;
-      const int kr = tid >> 4;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t j = (int64_t)T * kBlock + kr + 16 * i;
-        u32x4 x = j < n ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
-        *(u32x4*)(sm.kt + (kr + 16 * i) * KSTR + 8 * dc) = x;
-      }
-    }
-    __syncthreads();
-    if (active) {
+    if (T + 1 < t1) load_tile(T + 1);
+    // the causal mask only bites in tiles that reach past the first last-query row
+    const bool edge = (int64_t)T * kBlock + kBlock - 1 > (int64_t)n - r;
+    if constexpr (PASS == 1) if (active) {
       f32x16 s[2][2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -110,14 +124,12 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
           s[mt][1] = mfma32(av, qr[1][ks], s[mt][1]);
         }
       }
-      // the causal mask only bites in tiles that reach past the first last-query row
-      const bool edge = (int64_t)T * kBlock + kBlock - 1 > (int64_t)n - r;
+      {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int t = 32 * nt + r32;
-        const int64_t iq = (int64_t)n - r + t;
-        const bool row_ok = t < r;
-        if constexpr (PASS == 1) {
+        for (int nt = 0; nt < 2; ++nt) {
+          const int t = 32 * nt + r32;
+          const int64_t iq = (int64_t)n - r + t;
+          const bool row_ok = t < r;
           float mx = -INFINITY;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
@@ -138,8 +150,31 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
             for (int i = 0; i < 16; ++i) acc += fast_exp2(s[mt][nt][i] - m_use);
           run_l[nt] = run_l[nt] * fast_exp2(run_m[nt] - m_use) + acc;
           run_m[nt] = m_new;
-        } else {
-          float* pt = sm.pt[wave];
+        }
+      }
+    }
+    if constexpr (PASS == 2) {
+      // normalised probabilities, staged 32 query rows at a time; the column sum
+      // (lane = key) and the diagonal partials (lane = e, e + 64 with e = t - c + 63)
+      // run over t in ascending order across the two halves
+      float* pt = sm.pt[wave];
+      float cs = 0.f;
+      float ds[2] = {0.f, 0.f};
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (active) {
+          // scores of this half's 32 query rows (S^T = K Q^T on MFMA)
+          f32x16 s[2];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            s[mt] = f32x16{};
+            const uint16_t* kp = sm.kt + (32 * mt + r32) * KSTR + 8 * g;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) s[mt] = mfma32(*(const u32x4*)(kp + 16 * ks), qr[nt][ks], s[mt]);
+          }
+          const int t = 32 * nt + r32;
+          const int64_t iq = (int64_t)n - r + t;
+          const bool row_ok = t < r;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -147,37 +182,40 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
               const int kx = 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
               const int64_t j = (int64_t)T * kBlock + kx;
               const bool ok = row_ok && (!edge || j <= iq);
-              const float pv = ok ? fast_exp2(fmaf(s[mt][nt][i], sl2, -rm[nt])) * ril[nt] : 0.f;
-              pt[t * PSTR + kx] = pv;
+              const float pv = ok ? fast_exp2(fmaf(s[mt][i], sl2, -rm[nt])) * ril[nt] : 0.f;
+              pt[r32 * PSTR + kx] = pv;
             }
         }
+        __syncthreads();
+        if (active) {
+#pragma unroll 8
+          for (int tl = 0; tl < PROWS; ++tl) cs += pt[tl * PSTR + lane];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int e = lane + 64 * h2;
+            if (e < 127) {
+              int tlo = e - 63 > 32 * nt ? e - 63 : 32 * nt;
+              int thi = e < 32 * nt + 31 ? e : 32 * nt + 31;
+              for (int t = tlo; t <= thi; ++t) ds[h2] += pt[(t - 32 * nt) * PSTR + (t - e + 63)];
+            }
+          }
+        }
+        __syncthreads();
       }
-    }
-    if constexpr (PASS == 2) {
-      __syncthreads();
       if (active) {
-        const float* pt = sm.pt[wave];
-        // column sums over the 64 row slots, fixed order
-        float cs = 0.f;
-        for (int t = 0; t < 64; ++t) cs += pt[t * PSTR + lane];
         const int64_t j = (int64_t)T * kBlock + lane;
         if (j < n) a.vcol[(size_t)slot * n + j] = cs;
-        // diagonal partials: e = t - c + 63, lane owns e = lane and e = lane + 64
         float* dp = a.dpart + ((size_t)slot * a.ntiles + T) * 128;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int e = lane + 64 * h2;
-          float ds = 0.f;
-          if (e < 127) {
-            const int tlo = e - 63 > 0 ? e - 63 : 0;
-            const int thi = e < 63 ? e : 63;
-            for (int t = tlo; t <= thi; ++t) ds += pt[t * PSTR + (t - e + 63)];
-          }
-          dp[e] = ds;
-        }
+        dp[lane] = ds[0];
+        dp[lane + 64] = ds[1];
       }
+    } else {
+      __syncthreads();  // every wave is done with this K tile
     }
-    __syncthreads();
+    if (T + 1 < t1) {
+      store_tile();
+      __syncthreads();
+    }
   }
   if constexpr (PASS == 1) if (active) {
 #pragma unroll
