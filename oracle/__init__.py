@@ -30,4 +30,8 @@ from .minf_oracle import (  # noqa: F401
     decode_mask,
     sparse_decode,
     dense_decode,
+    plan_blocks,
+    pattern_recall,
+    candidate_plan,
+    search_head_pattern,
 )

@@ -42,7 +42,12 @@ Readings where the pages are silent (each one is listed in the design notes):
     cache of n keys (it is the last position); its keys are selected at
     64-token block granularity by the same pooled-key estimate as
     Block-Sparse, score(c) = q . mean(K_c), top-k_b blocks per query head,
-    ties to the lower block, with no forced blocks.
+    ties to the lower block, with no forced blocks;
+  * pattern search (offline): a candidate's work is the kernel's unit (key
+    blocks with a mask entry, gathered columns at 1/64 block each) on the
+    calibration input; its quality is the attention recall (the causal
+    softmax mass inside its mask, averaged over query rows); each head takes
+    the highest-recall candidate within a work budget.
 """
 from __future__ import annotations
 
@@ -406,6 +411,90 @@ def dense_decode(q, k, v, hq: int, hkv: int, scale: float):
         o, l = attend_rows(q[h][None, :], k[g], v[g], np.ones((1, n), bool), scale)
         out[h], lse[h] = o[0], l[0]
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Kernel-aware pattern search ([A] "Method": each head's pattern is chosen
+# offline by a kernel-aware sparse pattern search; [T]: offline per-head
+# pattern search, and attention recall as the share of attention an index
+# keeps)
+# ---------------------------------------------------------------------------
+def plan_blocks(plan: dict, n: int) -> float:
+    """Work of a plan in the kernel's unit, summed over query blocks: the key
+    blocks whose mask block has an entry, plus each gathered column as 1/64 of
+    a block (VS columns outside the computed blocks)."""
+    nb = _nblocks(n)
+    kind = plan["kind"]
+    if kind == "dense":
+        return nb * (nb + 1) / 2
+    if kind == "block":
+        return float(np.sum(plan["blk_cnt"]))
+    tot = 0.0
+    for b in range(nb):
+        rows = np.arange(BLOCK * b, min(BLOCK * b + BLOCK, n))
+        if kind == "vs":
+            tot += len(vs_block_set(n, plan["s_idx"], b)) + len(vs_column_set(n, plan["s_idx"], plan["v_idx"], b)) / BLOCK
+        else:
+            m = plan_mask_block(plan, n, b, rows)
+            hit = m.any(axis=0)
+            tot += len(np.unique(np.nonzero(hit)[0] // BLOCK))
+    return tot
+
+
+def pattern_recall(q, k, plan: dict, scale: float, rows=None) -> float:
+    """Mean over query rows of the causal softmax probability mass that falls
+    inside the plan's mask (1.0 for the dense plan)."""
+    q, k = _f64(q), _f64(k)
+    n = q.shape[0]
+    rows, groups = _row_blocks(n, rows)
+    tot = 0.0
+    for b, rs in groups.items():
+        s = scale * (q[rs] @ k.T)
+        causal = np.arange(n)[None, :] <= np.asarray(rs)[:, None]
+        s = np.where(causal, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        m = plan_mask_block(plan, n, b, rs)
+        tot += float((p * m).sum())
+    return tot / rows.shape[0]
+
+
+def candidate_plan(q, k, cand: dict, scale: float, last_q: int = 64) -> dict:
+    """The plan a candidate pattern gives on this head's data: its index built online."""
+    kind = cand["kind"]
+    if kind in ("dense", "ashape"):
+        return dict(cand)
+    if kind == "vs":
+        vi, si, _, _ = vs_index(q, k, last_q, int(cand["k_v"]), int(cand["k_s"]), scale)
+        return dict(kind="vs", v_idx=vi, s_idx=si)
+    if kind == "block":
+        k_b = int(cand["k_b"])
+        sel, _ = block_index(q, k, k_b)
+        idx = -np.ones((len(sel), k_b), dtype=np.int64)
+        cnt = np.zeros(len(sel), dtype=np.int64)
+        for b, cs in enumerate(sel):
+            idx[b, : len(cs)] = cs
+            cnt[b] = len(cs)
+        return dict(kind="block", blk_idx=idx, blk_cnt=cnt)
+    raise ValueError(f"unknown candidate kind {kind!r}")
+
+
+def search_head_pattern(q, k, candidates, scale: float, budget: float, last_q: int = 64, rows=None):
+    """Pick one head's pattern: among the candidates whose work on this input is
+    within `budget` blocks, the one with the highest attention recall (ties to
+    the lower work, then to the earlier candidate). Returns (index or -1, table
+    of (blocks, recall) per candidate)."""
+    table = []
+    for cand in candidates:
+        plan = candidate_plan(q, k, cand, scale, last_q)
+        table.append((plan_blocks(plan, _f64(q).shape[0]), pattern_recall(q, k, plan, scale, rows)))
+    best = -1
+    for c, (cost, rec) in enumerate(table):
+        if cost > budget:
+            continue
+        if best < 0 or rec > table[best][1] or (rec == table[best][1] and cost < table[best][0]):
+            best = c
+    return best, table
 
 
 def default_scale(d: int) -> float:

@@ -385,3 +385,77 @@ def test_decode_output_is_softmax_over_selected_keys_brute_force():
     want = [sum(w[a] * v[0, keys[a], t] for a in range(len(keys))) / z for t in range(d)]
     assert np.allclose(o[0], want, rtol=1e-12, atol=1e-12)
     assert abs(lse[0] - math.log(z)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# kernel-aware pattern search: work and recall
+# ---------------------------------------------------------------------------
+def test_pattern_recall_brute_force_and_full_budgets():
+    rng = np.random.default_rng(21)
+    n, d = 150, 8
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    scale = 0.4
+    plan = dict(kind="ashape", sink=5, local=20)
+    rows = [0, 7, 63, 64, 100, 149]
+    want = 0.0
+    for i in rows:
+        w = [math.exp(scale * sum(q[i, t] * k[j, t] for t in range(d))) for j in range(i + 1)]
+        z = sum(w)
+        want += sum(w[j] for j in range(i + 1) if j < 5 or i - j < 20) / z
+    assert abs(O.pattern_recall(q, k, plan, scale, rows) - want / len(rows)) < 1e-12
+    # every full budget keeps all of the attention
+    assert abs(O.pattern_recall(q, k, dict(kind="dense"), scale) - 1.0) < 1e-12
+    for cand in (dict(kind="vs", k_v=n, k_s=n), dict(kind="block", k_b=3), dict(kind="ashape", sink=0, local=n)):
+        plan = O.candidate_plan(q, k, cand, scale, last_q=64)
+        assert abs(O.pattern_recall(q, k, plan, scale) - 1.0) < 1e-12
+
+
+def test_plan_blocks_counts_blocks_with_mask_entries():
+    rng = np.random.default_rng(22)
+    n = 700
+    nb = (n + 63) // 64
+    assert O.plan_blocks(dict(kind="dense"), n) == nb * (nb + 1) / 2
+    for sink, local in ((0, 100), (70, 1), (64, 200), (10, 0)):
+        want = 0
+        for b in range(nb):
+            rows = np.arange(64 * b, min(64 * b + 64, n))
+            m = np.stack([O.ashape_mask_row(int(i), n, sink, local) for i in rows])
+            want += len({j // 64 for j in np.nonzero(m.any(axis=0))[0]})
+        assert O.plan_blocks(dict(kind="ashape", sink=sink, local=local), n) == want
+    cnt = rng.integers(1, 4, nb)
+    assert O.plan_blocks(dict(kind="block", blk_idx=None, blk_cnt=cnt), n) == cnt.sum()
+    s_idx = np.array([0, 130, 400])
+    v_idx = np.array([5, 300, 699])
+    want = sum(len(O.vs_block_set(n, s_idx, b)) + len(O.vs_column_set(n, s_idx, v_idx, b)) / 64 for b in range(nb))
+    assert O.plan_blocks(dict(kind="vs", s_idx=s_idx, v_idx=v_idx), n) == want
+
+
+def test_search_picks_best_recall_within_budget():
+    rng = np.random.default_rng(23)
+    n, d = 256, 8
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    cands = [dict(kind="ashape", sink=0, local=64), dict(kind="dense"), dict(kind="ashape", sink=64, local=64)]
+    best, table = O.search_head_pattern(q, k, cands, 0.3, budget=1e9)
+    assert best == 1 and abs(table[1][1] - 1.0) < 1e-12      # the dense plan keeps everything
+    best, table = O.search_head_pattern(q, k, cands, 0.3, budget=table[1][0] - 1)
+    assert best == 2                                          # sink + window beats the window alone
+    assert table[2][1] > table[0][1] and table[2][0] > table[0][0]
+    best, _ = O.search_head_pattern(q, k, cands, 0.3, budget=table[0][0])
+    assert best == 0
+    assert O.search_head_pattern(q, k, cands, 0.3, budget=0)[0] == -1
+
+
+def test_pattern_heads_favour_their_patterns():
+    from workload import pattern_heads
+    n = 2048
+    q, k, _ = pattern_heads(n)
+    qn, kn = q.float().numpy(), k.float().numpy()
+    cands = [dict(kind="ashape", sink=64, local=256), dict(kind="vs", k_v=128, k_s=4), dict(kind="vs", k_v=64, k_s=32),
+             dict(kind="block", k_b=4), dict(kind="block", k_b=8)]
+    rows = np.arange(0, n, 5)
+    picks = [O.search_head_pattern(qn[h], kn[h], cands, 1 / math.sqrt(128), budget=400, rows=rows) for h in range(3)]
+    assert cands[picks[0][0]]["kind"] == "vs"                 # vertical head
+    assert picks[1][1][picks[1][0]][1] > 0.99                 # local head: almost every candidate keeps it
+    assert cands[picks[2][0]]["kind"] == "block"              # block head

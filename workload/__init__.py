@@ -9,6 +9,7 @@ from .gen import (  # noqa: F401
     STRUCTURED_LATENT,
     PlantInfo,
     planted_qkv,
+    pattern_heads,
     pattern_map,
     injected_vs_index,
     vertical_gain_for,

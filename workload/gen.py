@@ -126,6 +126,42 @@ def planted_qkv(n: int, hq: int, hkv: int, d: int = 128, seed: int = 1000, devic
     return q, k, v, PlantInfo(cols_all, offs, (a_v, b_v), slash_gain)
 
 
+def pattern_heads(n: int, d: int = 128, seed: int = 2000, device="cpu"):
+    """Three synthetic heads (MHA: q, k, v [3, n, d] bf16), each built to favour
+    one pattern, for the offline pattern search:
+
+      head 0, vertical: 16 seeded key columns share a direction u with every
+        query (Q += 4u, K[c] += 16u, about 5.7 nats);
+      head 1, local: the locality latent with a short window (a^2 = 0.9, w = 256);
+      head 2, block: every query block b >= 1 shares a random direction u_b
+        with one seeded earlier key block c_b (Q_b += 8 u_b, K_{c_b} += 8 u_b).
+    """
+    gen = _gen(device, seed)
+    q = torch.randn((3, n, d), generator=gen, device=device, dtype=torch.float32)
+    k = torch.randn((3, n, d), generator=gen, device=device, dtype=torch.float32)
+    v = torch.randn((3, n, d), generator=gen, device=device, dtype=torch.float32)
+    # vertical head
+    u = torch.randn((d,), generator=gen, device=device)
+    u = u / u.norm()
+    cols = torch.randperm(n, generator=gen, device=device)[:16]
+    q[0] += 4.0 * u
+    k[0, cols] += 16.0 * u
+    # local head
+    a2, w = 0.9, 256
+    x = _latent(n, d, w, gen, device)
+    q[1] = (1 - a2) ** 0.5 * q[1] + a2 ** 0.5 * x
+    k[1] = (1 - a2) ** 0.5 * k[1] + a2 ** 0.5 * x
+    # block head
+    nb = (n + 63) // 64
+    for b in range(1, nb):
+        c = int(torch.randint(0, b, (1,), generator=gen, device=device))
+        ub = torch.randn((d,), generator=gen, device=device)
+        ub = ub / ub.norm()
+        q[2, 64 * b: 64 * b + 64] += 8.0 * ub
+        k[2, 64 * c: 64 * c + 64] += 8.0 * ub
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+
 def pattern_map(hq: int, n_vs: int, n_bs: int, n_a: int, seed: int) -> list:
     """Seeded per-head pattern kinds: a permutation of n_vs 'vs', n_bs 'block', n_a 'ashape'."""
     if n_vs + n_bs + n_a != hq:
