@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-injected", action="store_true")
     ap.add_argument("--no-structured", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--search", action="store_true", help="also time the offline pattern search on the input")
     ap.add_argument("--decode-blocks", type=int, default=64,
                     help="decode budget in 64-token blocks (64 blocks = 4096 tokens)")
     ap.add_argument("--dense-runs", type=int, default=1)
@@ -537,6 +538,30 @@ def main():
               f"({extra['decode']['dense_hbm_gbs']} GB/s), speedup {extra['decode']['speedup']}x",
               file=sys.stderr, flush=True)
         del kt, ws_s, ws_d
+
+    # offline pattern search on this input (optional: it re-runs attention once per candidate)
+    if args.search:
+        from dynamic_sparse_attention_index_amd import pattern_search as PS
+        cands = [dict(kind="ashape", sink=128, local=4096), dict(kind="vs", k_v=1000, k_s=6096),
+                 dict(kind="vs", k_v=1000, k_s=1024), dict(kind="block", k_b=256), dict(kind="block", k_b=64)]
+        budget = 0.1 * nb * (nb + 1) / 2
+        torch.cuda.synchronize()
+        t_s = time.perf_counter()
+        res = PS.search_patterns(q, k, v, cands, budget, scale=scale, rows=torch.arange(0, n, 97, device=dev))
+        torch.cuda.synchronize()
+        search_s = time.perf_counter() - t_s
+        picks = {}
+        for c in res["choice"]:
+            key = "none" if c < 0 else f"{cands[c]['kind']}:{','.join(str(cands[c][x]) for x in cands[c] if x != 'kind')}"
+            picks[key] = picks.get(key, 0) + 1
+        extra["pattern_search"] = {
+            "seconds": round(search_s, 2), "candidates": len(cands), "budget_blocks_per_head": budget,
+            "choices": picks, "mean_recall_of_choice": round(float(sum(
+                res["recall"][h, c] for h, c in enumerate(res["choice"]) if c >= 0) / max(1, sum(
+                    1 for c in res["choice"] if c >= 0))), 4),
+            "note": "recall over every 97th query row; work budget 10% of the causal blocks",
+        }
+        print(f"[bench] pattern search: {search_s:.2f} s, choices {picks}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
