@@ -34,4 +34,7 @@ from .minf_oracle import (  # noqa: F401
     pattern_recall,
     candidate_plan,
     search_head_pattern,
+    grid_permutation,
+    permuted_block_index,
+    permuted_block_attn,
 )

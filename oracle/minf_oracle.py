@@ -17,6 +17,8 @@ Sources (web pages, cited by title and section):
       patterns) and the unified three-step framework.
   [S] "MInference" abstract on the authors' page (offline pattern, online
       index, sparse kernels).
+  [P] the MMInference abstract on the authors' page (the Grid pattern of
+      video input and the permutation-based method).
   [D] the same talk transcript, fourth stage of the KV-cache lifecycle
       (decoding is bound by loading the KV cache; load it sparsely) and its
       closing part on dynamic sparsity in decoding (attention decomposes into
@@ -47,7 +49,13 @@ Readings where the pages are silent (each one is listed in the design notes):
     blocks with a mask entry, gathered columns at 1/64 block each) on the
     calibration input; its quality is the attention recall (the causal
     softmax mass inside its mask, averaged over query rows); each head takes
-    the highest-recall candidate within a work budget.
+    the highest-recall candidate within a work budget;
+  * grid pattern [T], [P]: a video of F frames x P patches in frame-major
+    order is permuted to patch-major order (the same permutation for rows
+    and columns), and the Block-Sparse estimate runs on the permuted
+    sequence; a key block is eligible when one of its keys precedes one of
+    the block's queries in the original order, and attention stays causal in
+    the original order.
 """
 from __future__ import annotations
 
@@ -495,6 +503,64 @@ def search_head_pattern(q, k, candidates, scale: float, budget: float, last_q: i
         if best < 0 or rec > table[best][1] or (rec == table[best][1] and cost < table[best][0]):
             best = c
     return best, table
+
+
+# ---------------------------------------------------------------------------
+# Grid pattern with permutation ([T] MMInference part: video frames and
+# patches give grid-like attention; permuting rows and columns together
+# (attention is invariant under it) turns the grid into blocks that the block
+# kernels compute densely; [P] MMInference abstract: the Grid pattern, the
+# permutation-based method, the sparse distribution built from the input)
+# ---------------------------------------------------------------------------
+def grid_permutation(frames: int, patches: int) -> np.ndarray:
+    """src[t'] = original index of permuted row t' for the patch-major order of a
+    frame-major video layout: original t = f * patches + p, permuted t' = p * frames + f."""
+    f = np.arange(frames)
+    p = np.arange(patches)
+    return (f[None, :] * patches + p[:, None]).reshape(-1).astype(np.int64)
+
+
+def permuted_block_index(q, k, src, k_b: int):
+    """Block index of a permuted head: pooled Q and K over 64-row blocks of the
+    permuted sequence (q[src], k[src]); key block c is eligible for query block b
+    when some key of c precedes some query of b in the original order
+    (min src over c <= max src over b); the top-k_b eligible blocks by the
+    pooled score, ties to the lower c, ascending. Returns (list of selections,
+    score matrix with -inf where not eligible)."""
+    src = np.asarray(src, dtype=np.int64)
+    qp, kp = _f64(q)[src], _f64(k)[src]
+    n = src.shape[0]
+    nb = _nblocks(n)
+    lo = np.array([src[BLOCK * c: BLOCK * c + BLOCK].min() for c in range(nb)])
+    hi = np.array([src[BLOCK * b: BLOCK * b + BLOCK].max() for b in range(nb)])
+    s = pool_blocks(qp) @ pool_blocks(kp).T
+    s = np.where(lo[None, :] <= hi[:, None], s, -np.inf)
+    sel = []
+    for b in range(nb):
+        ok = np.nonzero(np.isfinite(s[b]))[0]
+        pick = topk_lowidx(s[b, ok], k_b)
+        sel.append(np.sort(ok[pick]))
+    return sel, s
+
+
+def permuted_block_attn(q, k, v, src, sel, scale: float, rows=None):
+    """Attention of one head whose blocks were chosen in the permuted order,
+    evaluated in the original order: key j is in Mask(i) when j <= i and the
+    permuted block of j is selected for the permuted block of i. Returns O and
+    LSE for the original rows `rows` (all by default)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    src = np.asarray(src, dtype=np.int64)
+    n = q.shape[0]
+    inv = np.empty(n, dtype=np.int64)
+    inv[src] = np.arange(n)
+    pblk = inv // BLOCK
+    rows = np.arange(n) if rows is None else np.asarray(rows, dtype=np.int64)
+    j = np.arange(n)
+    mask = np.zeros((rows.shape[0], n), dtype=bool)
+    for t, i in enumerate(rows.tolist()):
+        allowed = np.isin(pblk, np.asarray(sel[pblk[i]], dtype=np.int64))
+        mask[t] = (j <= i) & allowed
+    return attend_rows(q[rows], k, v, mask, scale)
 
 
 def default_scale(d: int) -> float:

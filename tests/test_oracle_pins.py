@@ -459,3 +459,70 @@ def test_pattern_heads_favour_their_patterns():
     assert cands[picks[0][0]]["kind"] == "vs"                 # vertical head
     assert picks[1][1][picks[1][0]][1] > 0.99                 # local head: almost every candidate keeps it
     assert cands[picks[2][0]]["kind"] == "block"              # block head
+
+
+# ---------------------------------------------------------------------------
+# grid pattern with permutation
+# ---------------------------------------------------------------------------
+def test_grid_permutation_is_patch_major():
+    F, P = 5, 7
+    src = O.grid_permutation(F, P)
+    assert sorted(src.tolist()) == list(range(F * P))
+    for p in range(P):
+        for f in range(F):
+            assert src[p * F + f] == f * P + p
+
+
+def test_identity_permutation_reduces_to_block_sparse():
+    rng = np.random.default_rng(31)
+    n, d = 300, 8
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    sel, s = O.permuted_block_index(q, k, np.arange(n), 2)
+    want, ws = O.block_index(q, k, 2)
+    assert all(list(a) == list(b) for a, b in zip(sel, want))
+    fin = np.isfinite(ws)
+    assert np.array_equal(np.isfinite(s), fin) and np.allclose(s[fin], ws[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_permuted_eligibility_and_mask_brute_force():
+    rng = np.random.default_rng(32)
+    n, d = 200, 4
+    src = rng.permutation(n)
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    sel, s = O.permuted_block_index(q, k, src, 2)
+    nb = 4
+    for b in range(nb):
+        for c in range(nb):
+            elig = any(src[j] <= src[i] for i in range(64 * b, min(64 * b + 64, n))
+                       for j in range(64 * c, min(64 * c + 64, n)))
+            assert elig == bool(np.isfinite(s[b, c]))
+        assert len(sel[b]) == min(2, int(np.isfinite(s[b]).sum()))
+    inv = np.empty(n, dtype=np.int64)
+    inv[src] = np.arange(n)
+    o, lse = O.permuted_block_attn(q, k, v, src, sel, 0.5, rows=[0, 57, 199])
+    for t, i in enumerate([0, 57, 199]):
+        keys = [j for j in range(i + 1) if inv[j] // 64 in set(sel[inv[i] // 64].tolist())]
+        if not keys:
+            assert np.all(o[t] == 0) and np.isneginf(lse[t])
+            continue
+        w = [math.exp(0.5 * float(q[i] @ k[j])) for j in keys]
+        z = sum(w)
+        want = sum(w[a] * v[keys[a]] for a in range(len(keys))) / z
+        assert np.allclose(o[t], want, rtol=1e-12, atol=1e-12) and abs(lse[t] - math.log(z)) < 1e-12
+
+
+def test_permuted_full_budget_is_dense_causal():
+    rng = np.random.default_rng(33)
+    n, d = 260, 8
+    src = rng.permutation(n)
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    sel, _ = O.permuted_block_index(q, k, src, 10)
+    o, lse = O.permuted_block_attn(q, k, v, src, sel, 0.3)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None], is_causal=True, scale=0.3)[0]
+    assert np.abs(o - want.numpy()).max() < 1e-12

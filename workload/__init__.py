@@ -10,6 +10,7 @@ from .gen import (  # noqa: F401
     PlantInfo,
     planted_qkv,
     pattern_heads,
+    grid_qkv,
     pattern_map,
     injected_vs_index,
     vertical_gain_for,

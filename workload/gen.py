@@ -162,6 +162,34 @@ def pattern_heads(n: int, d: int = 128, seed: int = 2000, device="cpu"):
     return q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
 
 
+def grid_qkv(frames: int, patches: int, hq: int, hkv: int, d: int = 128, seed: int = 3000, gain: float = 8.0,
+             device="cpu"):
+    """Video-like inputs in frame-major order (token t = f * patches + p) whose
+    heads show the grid pattern: every KV group has a random unit direction
+    u_p per patch position p, added to the queries and keys of every frame at
+    that position (Q += gain u_p, K += gain u_p, about gain^2 / sqrt(d) nats),
+    so a query attends to the same patch in every earlier frame. Q, K, V
+    [h, F * P, d] bf16 on `device`."""
+    if hq % hkv:
+        raise ValueError("hq must be a multiple of hkv")
+    n = frames * patches
+    gen = _gen(device, seed)
+    q = torch.empty((hq, n, d), dtype=torch.bfloat16, device=device)
+    k = torch.empty((hkv, n, d), dtype=torch.bfloat16, device=device)
+    v = torch.empty((hkv, n, d), dtype=torch.bfloat16, device=device)
+    grp = hq // hkv
+    for g in range(hkv):
+        u = torch.randn((patches, d), generator=gen, device=device)
+        u = u / u.norm(dim=1, keepdim=True)
+        plant = u.repeat(frames, 1) * gain  # row f * patches + p gets u_p
+        k[g] = (torch.randn((n, d), generator=gen, device=device) + plant).to(torch.bfloat16)
+        v[g] = torch.randn((n, d), generator=gen, device=device).to(torch.bfloat16)
+        for t in range(grp):
+            q[g * grp + t] = (torch.randn((n, d), generator=gen, device=device) + plant).to(torch.bfloat16)
+        del plant
+    return q, k, v
+
+
 def pattern_map(hq: int, n_vs: int, n_bs: int, n_a: int, seed: int) -> list:
     """Seeded per-head pattern kinds: a permutation of n_vs 'vs', n_bs 'block', n_a 'ashape'."""
     if n_vs + n_bs + n_a != hq:
