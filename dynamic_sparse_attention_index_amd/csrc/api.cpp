@@ -181,6 +181,7 @@ minf_status check_vs_args(const void* q, const void* k, int64_t n, int hq, int h
 // ---------------- BS workspace
 struct BsWs {
   float *qbar, *kbar_t, *scores;
+  int32_t *blkmin, *blkmax;
   int rows;
   size_t bytes;
 };
@@ -193,6 +194,8 @@ BsWs carve_bs(void* base, int64_t n, int hkv, int n_heads) {
   w.kbar_t = c.take<float>((size_t)std::max(std::min(hkv, std::max(n_heads, 1)), 1) * nb * kHeadDim);
   w.rows = block_score_rows((int)nb, std::max(std::min(n_heads, 64), 1));
   w.scores = c.take<float>((size_t)std::max(std::min(n_heads, 64), 1) * w.rows * nb);
+  w.blkmin = c.take<int32_t>(nb);
+  w.blkmax = c.take<int32_t>(nb);
   w.bytes = c.off;
   return w;
 }
@@ -217,7 +220,7 @@ const char* minf_status_string(minf_status s) {
 
 const char* minf_last_error_detail(void) { return g_detail.c_str(); }
 
-int minf_abi_version(void) { return 1; }
+int minf_abi_version(void) { return 2; }
 
 size_t minf_vs_index_workspace_size(int64_t n, int n_heads) {
   if (n < 1 || n_heads < 0) return 0;
@@ -278,10 +281,10 @@ size_t minf_block_index_workspace_size(int64_t n, int hq, int hkv, int n_heads) 
   return carve_bs(nullptr, n, hkv, n_heads).bytes;
 }
 
-minf_status minf_build_block_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
-                                   const int32_t* heads, int n_heads, int k_b, int32_t* blk_idx, int32_t* blk_cnt,
-                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
-  g_detail.clear();
+static minf_status build_block_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                     const int32_t* heads, int n_heads, int k_b, const int32_t* pos,
+                                     int32_t* blk_idx, int32_t* blk_cnt, void* workspace, size_t ws_bytes,
+                                     hipStream_t stream) {
   minf_status s;
   if ((s = check_common(q, k, n, hq, hkv, d, kMaxTokens)) != MINF_OK) return s;
   if ((s = check_heads(heads, n_heads, hq)) != MINF_OK) return s;
@@ -307,10 +310,44 @@ minf_status minf_build_block_index(const void* q, const void* k, int64_t n, int 
   if (e == hipSuccess)
     e = launch_block_pool((const uint16_t*)k, (int)n, kv_heads.data(), kv_slots.data(), (int)kv_heads.size(),
                           nullptr, w.kbar_t, stream);
+  if (e == hipSuccess && pos) e = launch_block_minmax(pos, (int)n, w.blkmin, w.blkmax, stream);
   if (e == hipSuccess)
     e = launch_block_topk(w.qbar, w.kbar_t, kv_slot.data(), n_heads, nb, k_b, blk_idx, blk_cnt, w.scores, w.rows,
-                          stream);
+                          pos ? w.blkmin : nullptr, pos ? w.blkmax : nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "block index kernels");
+  return MINF_OK;
+}
+
+minf_status minf_build_block_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                   const int32_t* heads, int n_heads, int k_b, int32_t* blk_idx, int32_t* blk_cnt,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  g_detail.clear();
+  return build_block_index(q, k, n, hq, hkv, d, heads, n_heads, k_b, nullptr, blk_idx, blk_cnt, workspace, ws_bytes,
+                           stream);
+}
+
+minf_status minf_build_permuted_block_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                            const int32_t* heads, int n_heads, int k_b, const int32_t* pos,
+                                            int32_t* blk_idx, int32_t* blk_cnt, void* workspace, size_t ws_bytes,
+                                            hipStream_t stream) {
+  g_detail.clear();
+  if (!pos) return fail(MINF_E_INVALID_ARG, "pos must be a device array of the rows' original positions");
+  return build_block_index(q, k, n, hq, hkv, d, heads, n_heads, k_b, pos, blk_idx, blk_cnt, workspace, ws_bytes,
+                           stream);
+}
+
+minf_status minf_permute_rows(const void* x, void* out, int heads, int64_t n, int row_bytes, const int32_t* src,
+                              int scatter, hipStream_t stream) {
+  g_detail.clear();
+  if (!x || !out || !src) return fail(MINF_E_INVALID_ARG, "x, out and src must be non-null device pointers");
+  if (x == out) return fail(MINF_E_INVALID_ARG, "out must not alias x");
+  if (heads < 1 || n < 1) return fail(MINF_E_INVALID_ARG, "heads and n must be >= 1");
+  if (row_bytes < 4 || row_bytes % 4 != 0) return fail(MINF_E_INVALID_ARG, "row_bytes must be a positive multiple of 4");
+  if (n > kMaxTokens) return fail(MINF_E_UNSUPPORTED, "n = %lld exceeds the supported %lld", (long long)n,
+                                  (long long)kMaxTokens);
+  if (scatter != 0 && scatter != 1) return fail(MINF_E_INVALID_ARG, "scatter must be 0 or 1");
+  hipError_t e = launch_permute_rows(x, out, heads, n, row_bytes, src, scatter, stream);
+  if (e != hipSuccess) return hip_fail(e, "row permutation kernel");
   return MINF_OK;
 }
 
@@ -331,7 +368,10 @@ minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const 
 
 size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
   if (n < 1 || hq < 1) return 0;
-  return align_up((size_t)hq * 2 * bitmap_words(n) * sizeof(uint32_t));
+  // per head: the VS offset bitmaps, then the min / max original position of
+  // every key block for Block-Sparse heads on a permuted sequence
+  return align_up((size_t)hq * 2 * bitmap_words(n) * sizeof(uint32_t)) +
+         align_up((size_t)hq * 2 * nblocks(n) * sizeof(int32_t));
 }
 
 static minf_status check_attn_common(const void* q, const void* k, const void* v, void* o, int64_t n, int hq,
@@ -387,9 +427,12 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
   minf_status s;
   if ((s = check_attn_common(q, k, v, o, n, hq, hkv, d, scale, kMaxTokens)) != MINF_OK) return s;
   if (!plans) return fail(MINF_E_INVALID_ARG, "plans must be a host array of hq entries");
-  bool any_vs = false;
+  bool any_vs = false, any_pos = false;
   for (int h = 0; h < hq; ++h) {
     const minf_head_plan& p = plans[h];
+    if (p.pos && p.kind != MINF_KIND_BLOCK)
+      return fail(MINF_E_INVALID_ARG, "head %d: pos is only defined for Block-Sparse plans", h);
+    any_pos |= p.pos != nullptr;
     switch (p.kind) {
       case MINF_KIND_DENSE: break;
       case MINF_KIND_ASHAPE:
@@ -408,7 +451,8 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
       default: return fail(MINF_E_INVALID_ARG, "head %d: unknown plan kind %d", h, p.kind);
     }
   }
-  if (any_vs && (s = check_ws(workspace, ws_bytes, minf_sparse_attn_workspace_size(n, hq))) != MINF_OK) return s;
+  if ((any_vs || any_pos) && (s = check_ws(workspace, ws_bytes, minf_sparse_attn_workspace_size(n, hq))) != MINF_OK)
+    return s;
 
   AttnLaunch a{};
   a.q = (const uint16_t*)q;
@@ -438,6 +482,22 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
     hipError_t e = launch_vs_offset_bits(vs_s.data(), vs_k.data(), vs_bits.data(), (int)vs_s.size(), (int)n, stream);
     if (e != hipSuccess) return hip_fail(e, "VS offset bitmap kernel");
   }
+  const size_t nbk = (size_t)nblocks(n);
+  int32_t* pos_ws = (int32_t*)((char*)workspace + align_up((size_t)hq * words * sizeof(uint32_t)));
+  for (int h = 0; h < hq && any_pos; ++h) {
+    if (!plans[h].pos) continue;
+    // heads that share a position array share its block extremes
+    int first = h;
+    for (int g = 0; g < h; ++g)
+      if (plans[g].pos == plans[h].pos) {
+        first = g;
+        break;
+      }
+    if (first != h) continue;
+    hipError_t e = launch_block_minmax(plans[h].pos, (int)n, pos_ws + (size_t)h * 2 * nbk,
+                                       pos_ws + (size_t)h * 2 * nbk + nbk, stream);
+    if (e != hipSuccess) return hip_fail(e, "block position kernel");
+  }
   for (int h0 = 0; h0 < hq;) {
     int nh, hg;
     head_split(hq, a.grp, h0, false, nh, hg);
@@ -454,6 +514,16 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
       d2.obits = p.kind == MINF_KIND_VS ? (const uint32_t*)workspace + (size_t)(h0 + i) * words : nullptr;
       d2.blk_idx = p.blk_idx;
       d2.blk_cnt = p.blk_cnt;
+      if (p.pos) {
+        int first = h0 + i;
+        for (int g = 0; g < h0 + i; ++g)
+          if (plans[g].pos == p.pos) {
+            first = g;
+            break;
+          }
+        d2.pos = p.pos;
+        d2.blkmax = pos_ws + (size_t)first * 2 * nbk + nbk;
+      }
     }
     a.head0 = h0;
     a.nh = nh;

@@ -240,8 +240,10 @@ constexpr float kRescaleSlack = 0.0f;
 // One tile for one wave. MASK: 0 = every key visible; 1 = causal (j <= i);
 // 2 = general predicate (causal or j < n, plus the A-shape clause);
 // 3 = gathered columns (per-column membership flag and j <= i).
-enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_GENERAL = 2, MASK_GATHER = 3 };
+// 4 = original positions (permuted sequences): key visible iff its position <= the row's.
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_GENERAL = 2, MASK_GATHER = 3, MASK_POS = 4 };
 
+template <bool POSM>
 __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
                                              const uint16_t* vt, int MASK, int key0, const uint32_t* gcols,
                                              int qsel, int row, int n, int causal, int ashape, int sink,
@@ -282,6 +284,19 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
         const int kx0 = 32 * mt + 8 * (i >> 2) + (i & 3);
         const bool vis = kx0 <= hi && (kx0 < lo_sink || kx0 > lo_win);
         s[mt][i] = vis ? s[mt][i] : -INFINITY;
+      }
+  } else if (POSM && MASK == MASK_POS) {
+    // gcols holds the tile's key positions; `row` is this lane's query position
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x4 e4 = *(const u32x4*)(gcols + 32 * mt + 8 * q4 + 4 * g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool vis = (int)(e4[t] & 0x3fffffffu) <= row;
+          s[mt][4 * q4 + t] = vis ? s[mt][4 * q4 + t] : -INFINITY;
+        }
       }
   } else if (MASK == MASK_GATHER) {
     const uint32_t sh = 30 + qsel;
@@ -350,6 +365,9 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
   }
 }
 
+// POSM: the launch has Block-Sparse heads on permuted sequences (a separate
+// instantiation, so the common kernel carries none of that code).
+template <bool POSM>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   __shared__ Smem sm;
   __shared__ __attribute__((aligned(16))) uint16_t kt0[kTileHalves];
@@ -452,8 +470,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
     it.bits1 = (need_last && b1 == p.nb - 1) ? sm.bits[1] : sm.bits[0];
     it.base = b0 + 1;
     it.init_bitmap_cursor(it.base);
-  } else {  // KIND_BLOCK
-    const int nwords = (bmax >> 5) + 1;
+  } else {  // KIND_BLOCK (on a permuted sequence: every key block can be selected)
+    const int cmax_blk = hd.pos ? p.nb - 1 : bmax;
+    const int nwords = (cmax_blk >> 5) + 1;
     for (int i = tid; i < nwords; i += kThreads) {
       sm.bits[0][i] = 0u;
       sm.bits[1][i] = 0u;
@@ -468,12 +487,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
       const int e = x - which * kb;
       if (e < cnt) {
         int c = hd.blk_idx[(size_t)b * kb + e];
-        if (c >= 0 && c <= b) atomicOr(&sm.bits[which][c >> 5], 1u << (c & 31));
+        if (c >= 0 && c <= (hd.pos ? cmax_blk : b)) atomicOr(&sm.bits[which][c >> 5], 1u << (c & 31));
       }
     }
     __syncthreads();
-    it.cmax = bmax;
-    it.init_bitmap_cursor(bmax);
+    it.cmax = cmax_blk;
+    it.init_bitmap_cursor(cmax_blk);
+  }
+  // permuted sequences: each lane's query position and the wave's earliest one
+  const bool posm = POSM && hd.kind == KIND_BLOCK && hd.pos != nullptr;
+  int rpos = row, wminpos = 0;
+  if (posm) {
+    rpos = row < n ? hd.pos[row] : -1;
+    int mn = row < n ? rpos : 0x3fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mn = min(mn, __shfl_xor(mn, off));
+    wminpos = mn;
   }
   const int ashape = hd.kind == KIND_ASHAPE;
 
@@ -484,31 +513,46 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
     int c_cur = 0, m_cur = 0, c_nxt = 0, m_nxt = 0;
     const uint32_t lane_off = (uint32_t)tile_row_lo() * 256u + tile_chunk_byte();
     const int causal_eff = p.causal || hd.kind != KIND_DENSE;
-    auto issue_block = [&](int cblk, uint16_t* ktn, uint16_t* vtn) {
+    auto issue_block = [&](int cblk, uint16_t* ktn, uint16_t* vtn, uint32_t* psn) {
       if ((cblk + 1) * kBlock <= n) {
         const size_t base = (size_t)cblk * kBlock * (kHeadDim * 2);
         issue_contig((const char*)kh + base, (const char*)vh + base, ktn, vtn, lane_off);
+        // permuted sequences: the tile's 64 key positions go to LDS with it
+        if (posm && wave == 0)
+          __builtin_amdgcn_global_load_lds(hd.pos + (size_t)cblk * kBlock + lane, (lds_ptr)psn, 4, 0, 0);
       } else {
         // partial last block: rows past n repeat row n - 1 and are always masked
         issue_rows(kh, vh, ktn, vtn, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
+        if (posm && wave == 0) {
+          const int j = cblk * kBlock + lane;
+          psn[lane] = j < n ? (uint32_t)hd.pos[j] : 0x3fffffffu;
+        }
       }
     };
     // one pipelined step: issue the next tile into (ktn, vtn), compute the current one from (ktc, vtc)
-    auto step = [&](uint16_t* ktc, uint16_t* vtc, uint16_t* ktn, uint16_t* vtn) -> bool {
+    auto step = [&](uint16_t* ktc, uint16_t* vtc, uint32_t* psc, uint16_t* ktn, uint16_t* vtn,
+                    uint32_t* psn) -> bool {
       const bool hn = it.next(c_nxt, m_nxt);
-      if (hn) issue_block(c_nxt, ktn, vtn);
+      if (hn) issue_block(c_nxt, ktn, vtn, psn);
       if (wave_on && ((m_cur >> qsel) & 1)) {
-        int full;
-        if (causal_eff) {
-          full = c_cur < qb;
-          if (ashape && full)
-            full = ((int64_t)c_cur * kBlock + kBlock - 1 < hd.sink) ||
-                   ((int64_t)qb * kBlock + kBlock - 1 - (int64_t)c_cur * kBlock < hd.local);
+        int full, mask;
+        if (posm) {
+          full = hd.blkmax[c_cur] <= wminpos;
+          mask = full ? MASK_NONE : MASK_POS;
         } else {
-          full = (c_cur + 1) * kBlock <= n;
+          if (causal_eff) {
+            full = c_cur < qb;
+            if (ashape && full)
+              full = ((int64_t)c_cur * kBlock + kBlock - 1 < hd.sink) ||
+                     ((int64_t)qb * kBlock + kBlock - 1 - (int64_t)c_cur * kBlock < hd.local);
+          } else {
+            full = (c_cur + 1) * kBlock <= n;
+          }
+          mask = full ? MASK_NONE : ((causal_eff && !ashape) ? MASK_CAUSAL : MASK_GENERAL);
         }
-        const int mask = full ? MASK_NONE : ((causal_eff && !ashape) ? MASK_CAUSAL : MASK_GENERAL);
-        compute_tile(ws, oo, ktc, vtc, mask, c_cur * kBlock, nullptr, qsel, row, n, causal_eff, ashape, hd.sink,
+        // rpos is the query row itself unless the sequence is permuted
+        compute_tile<POSM>(ws, oo, ktc, vtc, mask, c_cur * kBlock, POSM ? psc : nullptr, qsel, rpos, n, causal_eff,
+                           ashape, hd.sink,
                      hd.local, sl2);
       }
       wait_vmem();
@@ -517,13 +561,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
       m_cur = m_nxt;
       return hn;
     };
+    // key-position slots of the two tile buffers (phase B, which uses clist, never runs on BLOCK heads)
+    uint32_t* ps0 = sm.clist;
+    uint32_t* ps1 = sm.clist + kBlock;
     bool have = it.next(c_cur, m_cur);
-    if (have) issue_block(c_cur, kt0, vt0);
+    if (have) issue_block(c_cur, kt0, vt0, ps0);
     wait_vmem();
     __syncthreads();
     while (have) {
-      if (!step(kt0, vt0, kt1, vt1)) break;
-      have = step(kt1, vt1, kt0, vt0);
+      if (!step(kt0, vt0, ps0, kt1, vt1, ps1)) break;
+      have = step(kt1, vt1, ps1, kt0, vt0, ps0);
     }
   }
 
@@ -575,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
             // (padding slots were cleared, so they never count)
             const uint32_t* gc = sm.clist + t * kBlock;
             if (__any((gc[lane] >> (30 + qsel)) & 1u))
-              compute_tile(ws, oo, ktc, vtc, MASK_GATHER, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
+              compute_tile<POSM>(ws, oo, ktc, vtc, MASK_GATHER, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
           }
           wait_vmem();
           __syncthreads();
@@ -662,7 +709,12 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   const long long chunks = (long long)((npairs + ppc - 1) / ppc) * (a.nh / a.hgroup);
   // the grid covers whole rounds of kXcds chunks so that the item map is a bijection
   const long long grid = (chunks + kXcds - 1) / kXcds * kXcds * kChunk;
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  bool posm = false;
+  for (int i = 0; i < a.nh; ++i) posm |= a.heads[i].pos != nullptr;
+  if (posm)
+    hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -80,6 +80,9 @@ struct BsTopkLaunch {
   float* scores;        // [nh][rows][nb]: rows r0 .. r0 + rows - 1 of this round
   int32_t* blk_idx;     // [nh][nb][k_b]
   int32_t* blk_cnt;     // [nh][nb]
+  // permuted sequences: per-block min / max of the original positions (null: causal c <= b)
+  const int32_t* blkmin;
+  const int32_t* blkmax;
   int32_t nb, k_b, nh, r0, rows;
   int32_t kvslot[kMaxPoolHeads];
   int32_t outslot[kMaxPoolHeads];
@@ -96,7 +99,8 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
   __shared__ __attribute__((aligned(16))) float ks[kHeadDim][kTile];
   const int ct = blockIdx.x;
   const int bt = a.r0 / kTile + (int)blockIdx.z;
-  if (ct > bt) return;  // above the block diagonal
+  const bool causal = a.blkmin == nullptr;
+  if (causal && ct > bt) return;  // above the block diagonal
   const int hs = blockIdx.y;
   const int tid = threadIdx.x;
   const int b0 = bt * kTile, c0 = ct * kTile;
@@ -144,19 +148,24 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
     if (b >= a.nb || b >= a.r0 + a.rows) continue;
     float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
     const int c = c0 + 4 * tx;
-    if (c + 3 <= b && (a.nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
+    const int clim = causal ? b : a.nb - 1;  // last column stored
+    if (c + 3 <= clim && (a.nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
       *(float4*)(row + c) = float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (c + j <= b) row[c + j] = acc[i][j];
+        if (c + j <= clim) row[c + j] = acc[i][j];
     }
   }
 }
 
 // Top-k_b key blocks of every query block of the round, from the stored scores.
+// Causal: the candidates are c <= b. Permuted: every c whose earliest original
+// position is not after the query block's latest one; the others get the
+// smallest sortable key, below every finite score, so they are never picked
+// while k does not exceed the eligible count.
 __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
-  __shared__ float sc[kMaxBlocks];
+  __shared__ uint32_t sc[kMaxBlocks];
   __shared__ int hist[2048];
   __shared__ int scratch[16];
   const int tid = threadIdx.x;
@@ -165,19 +174,84 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   const int hs = blockIdx.y;
   const int slot = a.outslot[hs];
   const int kb = a.k_b;
-  const int keep = (b + 1) < kb ? (b + 1) : kb;
+  const bool causal = a.blkmin == nullptr;
+  const int ncand = causal ? b + 1 : a.nb;
+  const float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
+  int nelig = b + 1;
+  if (!causal) {
+    const int hi = a.blkmax[b];
+    int cnt = 0;
+    for (int c = tid; c < a.nb; c += 256) {
+      const bool e = a.blkmin[c] <= hi;
+      sc[c] = e ? sortable_key(row[c]) : 0u;
+      cnt += e;
+    }
+    // block-wide count of the eligible blocks
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if ((tid & 63) == 0) scratch[8 + (tid >> 6)] = cnt;
+    __syncthreads();
+    nelig = scratch[8] + scratch[9] + scratch[10] + scratch[11];
+    __syncthreads();
+  }
+  const int keep = nelig < kb ? nelig : kb;
   int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
   if (tid == 0) a.blk_cnt[(size_t)slot * a.nb + b] = keep;
   for (int e = keep + tid; e < kb; e += 256) out[e] = -1;
-  if (b + 1 <= kb) {
-    for (int c = tid; c <= b; c += 256) out[c] = c;
+  if (keep == nelig) {
+    // every eligible block is kept: list them in order
+    if (causal) {
+      for (int c = tid; c <= b; c += 256) out[c] = c;
+    } else {
+      int written = 0;
+      for (int base = 0; base < a.nb; base += 256) {
+        const int c = base + tid;
+        const bool e = c < a.nb && sc[c] != 0u;
+        int tot;
+        const int pos = block_excl_scan_count<256>(e, scratch, tot);
+        if (e) out[written + pos] = c;
+        written += tot;
+      }
+    }
     return;
   }
-  const float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
-  for (int c = tid; c <= b; c += 256) sc[c] = row[c];
+  if (causal)
+    for (int c = tid; c <= b; c += 256) sc[c] = sortable_key(row[c]);
   __syncthreads();
-  radix_topk_ordered<256>([&](int i) { return sortable_key(sc[i]); }, b + 1, kb, hist, scratch,
+  radix_topk_ordered<256>([&](int i) { return sc[i]; }, ncand, kb, hist, scratch,
                           [&](int pos, int i) { out[pos] = i; });
+}
+
+// Per-block min and max of the original positions of a permuted sequence.
+__global__ __launch_bounds__(64) void block_minmax_kernel(const int32_t* pos, int n, int32_t* bmin, int32_t* bmax) {
+  const int c = blockIdx.x;
+  const int j = c * kBlock + threadIdx.x;
+  int lo = 0x7fffffff, hi = -1;
+  if (j < n) lo = hi = pos[j];
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off));
+    hi = max(hi, __shfl_xor(hi, off));
+  }
+  if (threadIdx.x == 0) {
+    bmin[c] = lo;
+    bmax[c] = hi;
+  }
+}
+
+// Row permutation of [heads][n] rows of row_bytes bytes (a multiple of 4):
+// gather out[h][t] = x[h][src[t]], or scatter out[h][src[t]] = x[h][t].
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint32_t* x, uint32_t* out, int64_t n,
+                                                           int words, const int32_t* src, int scatter) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int h = blockIdx.y;
+  if (idx >= n * words) return;
+  const int64_t t = idx / words;
+  const int w = (int)(idx % words);
+  const int64_t s = src[t];
+  const size_t base = (size_t)h * n * words;
+  if (scatter)
+    out[base + (size_t)s * words + w] = x[base + (size_t)t * words + w];
+  else
+    out[base + (size_t)t * words + w] = x[base + (size_t)s * words + w];
 }
 
 }  // namespace
@@ -215,9 +289,24 @@ int block_score_rows(int nb, int n_heads) {
   return (int)std::min<long long>(r, ((long long)nb + kTile - 1) / kTile * kTile);
 }
 
+hipError_t launch_block_minmax(const int32_t* pos, int n, int32_t* bmin, int32_t* bmax, hipStream_t stream) {
+  const int nb = (n + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(block_minmax_kernel, dim3(nb), dim3(64), 0, stream, pos, n, bmin, bmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_rows(const void* x, void* out, int heads, int64_t n, int row_bytes, const int32_t* src,
+                               int scatter, hipStream_t stream) {
+  const int words = row_bytes / 4;
+  const int64_t total = n * words;
+  hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((total + 255) / 256), heads), dim3(256), 0, stream,
+                     (const uint32_t*)x, (uint32_t*)out, n, words, src, scatter);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
                              int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
-                             hipStream_t stream) {
+                             const int32_t* blkmin, const int32_t* blkmax, hipStream_t stream) {
   const int nbt = (nb + kTile - 1) / kTile;
   for (int base = 0; base < n_heads; base += kMaxPoolHeads) {
     const int c = n_heads - base < kMaxPoolHeads ? n_heads - base : kMaxPoolHeads;
@@ -231,6 +320,8 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32
     a.k_b = k_b;
     a.nh = c;
     a.rows = rows;
+    a.blkmin = blkmin;
+    a.blkmax = blkmax;
     for (int i = 0; i < c; ++i) {
       a.kvslot[i] = kvslot[base + i];
       a.outslot[i] = base + i;
@@ -238,7 +329,7 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32
     for (int r0 = 0; r0 < nb; r0 += rows) {
       a.r0 = r0;
       const int row_tiles = (std::min(nb, r0 + rows) - r0 + kTile - 1) / kTile;
-      const int col_tiles = std::min(nbt, (r0 + rows) / kTile);
+      const int col_tiles = blkmin ? nbt : std::min(nbt, (r0 + rows) / kTile);
       hipLaunchKernelGGL(block_score_kernel, dim3(col_tiles, c, row_tiles), dim3(256), 0, stream, a);
       hipLaunchKernelGGL(block_topk_kernel, dim3(std::min(rows, nb - r0), c), dim3(256), 0, stream, a);
       hipError_t e = hipGetLastError();

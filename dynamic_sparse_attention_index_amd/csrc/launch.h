@@ -17,6 +17,8 @@ struct AttnHead {
   const uint32_t* obits;   // VS: bitmap of block offsets covered by the slashes
   const int32_t* blk_idx;  // BLOCK
   const int32_t* blk_cnt;  // BLOCK
+  const int32_t* pos;      // BLOCK on a permuted sequence: original position of every row (else null)
+  const int32_t* blkmax;   // with pos: latest original position in every key block
 };
 
 struct AttnLaunch {
@@ -107,6 +109,11 @@ hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream)
 int block_score_rows(int nb, int n_heads);
 hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
                              int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
-                             hipStream_t stream);
+                             const int32_t* blkmin, const int32_t* blkmax, hipStream_t stream);
+// Per-block min / max of the original positions of a permuted sequence.
+hipError_t launch_block_minmax(const int32_t* pos, int n, int32_t* bmin, int32_t* bmax, hipStream_t stream);
+// Gather (scatter = 0) or scatter (1) rows of row_bytes bytes of [heads][n] data by src.
+hipError_t launch_permute_rows(const void* x, void* out, int heads, int64_t n, int row_bytes, const int32_t* src,
+                               int scatter, hipStream_t stream);
 
 }  // namespace minf

@@ -45,6 +45,7 @@ class HeadPlan(ctypes.Structure):
         ("s_idx", ctypes.c_void_p),
         ("blk_idx", ctypes.c_void_p),
         ("blk_cnt", ctypes.c_void_p),
+        ("pos", ctypes.c_void_p),
     ]
 
 
@@ -67,6 +68,8 @@ def _load():
         "minf_sparse_attn_workspace_size": (sz, [i64, i32]),
         "minf_sparse_attn": (i32, [vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, ctypes.POINTER(HeadPlan), vp, sz, vp]),
         "minf_dense_attn": (i32, [vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, i32, vp]),
+        "minf_build_permuted_block_index": (i32, [vp, vp, i64, i32, i32, i32, ip, i32, i32, vp, vp, vp, vp, sz, vp]),
+        "minf_permute_rows": (i32, [vp, vp, i32, i64, i32, vp, i32, vp]),
         "minf_decode_pool_keys": (i32, [vp, i64, i32, i32, i32, vp, vp]),
         "minf_decode_workspace_size": (sz, [i64, i32, i32]),
         "minf_sparse_decode": (i32, [vp, vp, vp, vp, i64, i32, i32, i32, f32, i32, vp, vp, vp, vp, sz, vp]),
@@ -178,6 +181,40 @@ def minf_build_block_index(q, k, heads, k_b=256, workspace=None, stream=None):
     return blk_idx, blk_cnt
 
 
+def minf_build_permuted_block_index(q, k, heads, pos, k_b=256, workspace=None, stream=None):
+    """Block index of a permuted sequence (q, k in permuted order, pos[t] = original position of row t).
+
+    Returns (blk_idx [n_heads, n_b, k_b] int32, blk_cnt [n_heads, n_b] int32).
+    """
+    _need(q, torch.bfloat16, "q")
+    _need(k, torch.bfloat16, "k")
+    _need(pos, torch.int32, "pos")
+    hq, n, d = q.shape
+    hkv = k.shape[0]
+    arr, nh = _heads_arr(heads)
+    nb = (n + 63) // 64
+    bi = torch.empty((nh, nb, k_b), dtype=torch.int32, device=q.device)
+    bc = torch.empty((nh, nb), dtype=torch.int32, device=q.device)
+    ws, wsb = _workspace(_lib.minf_block_index_workspace_size(n, hq, hkv, nh), q.device, workspace)
+    _check(_lib.minf_build_permuted_block_index(_ptr(q), _ptr(k), n, hq, hkv, d, arr, nh, int(k_b), _ptr(pos),
+                                                _ptr(bi), _ptr(bc), _ptr(ws), wsb, _stream(stream)))
+    return bi, bc
+
+
+def minf_permute_rows(x, src, scatter=False, out=None, stream=None):
+    """Rows of x [h, n, ...] (contiguous) permuted by src: gather out[:, t] = x[:, src[t]], or scatter
+    out[:, src[t]] = x[:, t]."""
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous GPU tensor")
+    _need(src, torch.int32, "src")
+    h, n = x.shape[0], x.shape[1]
+    row_bytes = x[0, 0].numel() * x.element_size()
+    out = torch.empty_like(x) if out is None else out
+    _check(_lib.minf_permute_rows(_ptr(x), _ptr(out), h, n, row_bytes, _ptr(src), 1 if scatter else 0,
+                                  _stream(stream)))
+    return out
+
+
 def minf_block_pool(x, heads, stream=None):
     """64-row block means of x [h, n, d] for the listed heads: [n_heads, n_b, d] float32."""
     _need(x, torch.bfloat16, "x")
@@ -212,6 +249,10 @@ def make_plans(plans):
             e.k_b = bi.shape[-1]
             e.blk_idx, e.blk_cnt = bi.data_ptr(), bc.data_ptr()
             keep += [bi, bc]
+            if p.get("pos") is not None:
+                _need(p["pos"], torch.int32, "pos")
+                e.pos = p["pos"].data_ptr()
+                keep.append(p["pos"])
         elif kind != "dense":
             raise ValueError(f"unknown plan kind {kind!r}")
     return arr, keep

@@ -115,6 +115,36 @@ minf_status minf_build_block_index(const void* q, const void* k, int64_t n, int 
                                    int32_t* blk_cnt, void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Grid pattern with permutation (talk transcript, MMInference part: video
+ * frames and patches give grid-like attention, and permuting rows and
+ * columns together maps the grid onto blocks; MMInference abstract on the
+ * authors' page: the Grid pattern and the permutation-based method).
+ *
+ * The caller permutes Q, K and V (minf_permute_rows, gather) into an order
+ * where the grid becomes blocks (for a frame-major video, patch-major order)
+ * and keeps pos[t] = the original position of permuted row t. The index is
+ * the Block-Sparse estimate on the permuted sequence: pooled means over its
+ * 64-row blocks; key block c is eligible for query block b when
+ * min(pos over c) <= max(pos over b); score(b, c) = Qbar[b] . Kbar[c] over
+ * eligible c; row b keeps the top-min(k_b, #eligible), ties to the lower c,
+ * ascending, padded with -1; blk_cnt[b] = that count. Attention then runs
+ * with BLOCK plans carrying pos, and the output rows are scattered back.
+ * Same arguments, workspace size and errors as minf_build_block_index, plus
+ * pos (device int32 [n], a permutation of 0..n-1; non-null).
+ * ---------------------------------------------------------------------- */
+minf_status minf_build_permuted_block_index(const void* q, const void* k, int64_t n, int hq, int hkv, int d,
+                                            const int32_t* heads, int n_heads, int k_b, const int32_t* pos,
+                                            int32_t* blk_idx, int32_t* blk_cnt, void* workspace, size_t ws_bytes,
+                                            hipStream_t stream);
+
+/* Row permutation of [heads][n] rows of row_bytes bytes (a multiple of 4):
+ * scatter == 0 gathers out[h][t] = x[h][src[t]]; scatter == 1 scatters
+ * out[h][src[t]] = x[h][t]. src: device int32 [n], a permutation of 0..n-1
+ * (not checked). out must not alias x. */
+minf_status minf_permute_rows(const void* x, void* out, int heads, int64_t n, int row_bytes, const int32_t* src,
+                              int scatter, hipStream_t stream);
+
 /* Debug export of the pooling step: out is device float [n_heads][n_b][d],
  * the 64-row block means of x ([h_total][n][d] bf16) for the listed heads. */
 minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const int32_t* heads,
@@ -162,6 +192,8 @@ typedef struct minf_head_plan {
   const int32_t* s_idx;   /* VS: device, diagonal offsets */
   const int32_t* blk_idx; /* BLOCK: device [n_b][k_b] */
   const int32_t* blk_cnt; /* BLOCK: device [n_b] */
+  const int32_t* pos;     /* BLOCK on a permuted sequence: device [n] original position of
+                             every row (see minf_build_permuted_block_index), else NULL */
 } minf_head_plan;
 
 size_t minf_sparse_attn_workspace_size(int64_t n, int hq);
@@ -169,6 +201,13 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
                              int64_t n, int hq, int hkv, int d, float scale,
                              const minf_head_plan* plans, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
+
+/* A BLOCK plan with pos != NULL describes a permuted sequence (q, k, v, o
+ * and lse are all in the permuted row order): key block c may appear in any
+ * row of blk_idx, and row i attends to key j when block(j) is listed for
+ * block(i) and pos[j] <= pos[i] (causal in the original order). Only BLOCK
+ * plans may carry pos (else MINF_E_INVALID_ARG); the workspace is then
+ * required as for VS plans. */
 
 /* Dense FlashAttention baseline (the comparison kernel of Fig. 3).
  * causal != 0: row i attends to j <= i; causal == 0: to every j < n.

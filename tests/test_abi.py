@@ -31,7 +31,7 @@ def test_status_strings():
     assert LIB.minf_status_string(WORKSPACE) == b"MINF_E_WORKSPACE"
     assert LIB.minf_status_string(HIP) == b"MINF_E_HIP"
     assert LIB.minf_status_string(99) == b"MINF_E_UNKNOWN"
-    assert LIB.minf_abi_version() == 1
+    assert LIB.minf_abi_version() == 2
 
 
 def test_workspace_sizes():
@@ -163,3 +163,18 @@ def test_decode_workspace_and_rejects():
     assert LIB.minf_decode_pool_keys(FAKE, 4096, 1, 128, -1, FAKE, None) == INVALID
     assert LIB.minf_decode_pool_keys(FAKE, 4096, 1, 128, 0, None, None) == INVALID
     assert LIB.minf_dense_decode(FAKE, FAKE, None, 4096, 4, 1, 128, 0.1, FAKE, None, FAKE, 1 << 20, None) == INVALID
+
+
+def test_permutation_entry_points_reject():
+    assert LIB.minf_permute_rows(FAKE, FAKE, 1, 64, 256, FAKE, 0, None) == INVALID      # out aliases x
+    assert LIB.minf_permute_rows(FAKE, ctypes.c_void_p(0x20000), 1, 64, 6, FAKE, 0, None) == INVALID
+    assert LIB.minf_permute_rows(FAKE, ctypes.c_void_p(0x20000), 1, 64, 256, None, 0, None) == INVALID
+    assert LIB.minf_permute_rows(FAKE, ctypes.c_void_p(0x20000), 1, 64, 256, FAKE, 2, None) == INVALID
+    arr, nh = _heads(0)
+    ws = LIB.minf_block_index_workspace_size(4096, 2, 1, 1)
+    assert LIB.minf_build_permuted_block_index(FAKE, FAKE, 4096, 2, 1, 128, arr, nh, 4, None, FAKE, FAKE, FAKE, ws,
+                                               None) == INVALID
+    # pos is only defined for Block-Sparse plans
+    plans = _plans(dict(kind=0, pos=0x10000), dict(kind=0))
+    assert _sparse(plans) == INVALID
+    assert LIB.minf_sparse_attn_workspace_size(4096, 2) >= 2 * 2 * 64 * 4
