@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-injected", action="store_true")
     ap.add_argument("--no-structured", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-grid", action="store_true")
+    ap.add_argument("--grid-blocks", type=int, default=64, help="block budget of the grid track")
     ap.add_argument("--search", action="store_true", help="also time the offline pattern search on the input")
     ap.add_argument("--decode-blocks", type=int, default=64,
                     help="decode budget in 64-token blocks (64 blocks = 4096 tokens)")
@@ -489,6 +491,91 @@ def main():
                 extra[trk]["speedup_step_vs_dense"] = round(dense_ms / extra[trk]["step_ms"], 2)
         print(f"[bench] dense {dense_ms:.1f} ms ({dense['tflops']} TFLOP/s), speedup {dense['speedup_step']}x",
               file=sys.stderr, flush=True)
+
+    # grid track: a video-like input (frames x 256 patches) with grid-planted heads, permuted to
+    # patch-major order, Block-Sparse index and attention in that order, output scattered back;
+    # beside it the same block budget without the permutation, and dense attention on the same data
+    if not args.no_grid and n % 256 == 0:
+        from workload import grid_qkv
+        patches = 256
+        frames = n // patches
+        k_b = args.grid_blocks
+        t1 = time.perf_counter()
+        qg, kg, vg = grid_qkv(frames, patches, hq, hkv, device="cuda")
+        # patch-major order: permuted row p * frames + f holds original row f * patches + p
+        fr = torch.arange(frames, device=dev, dtype=torch.int32)
+        pa = torch.arange(patches, device=dev, dtype=torch.int32)
+        src = (fr[None, :] * patches + pa[:, None]).reshape(-1).contiguous()
+        torch.cuda.synchronize()
+        print(f"[bench] grid inputs: {frames} frames x {patches} patches ({time.perf_counter() - t1:.1f} s)",
+              file=sys.stderr, flush=True)
+        heads_all = list(range(hq))
+        og = torch.empty_like(qg)
+        lg = torch.empty((hq, n), dtype=torch.float32, device=dev)
+
+        def grid_step(record=None):
+            e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+            e0.record(stream)
+            qp = minf.minf_permute_rows(qg, src)
+            kp = minf.minf_permute_rows(kg, src)
+            vp = minf.minf_permute_rows(vg, src)
+            bi, bc = minf.minf_build_permuted_block_index(qp, kp, heads_all, src, k_b=k_b)
+            e1.record(stream)
+            plans_g = minf.make_plans([dict(kind="block", blk_idx=bi[h], blk_cnt=bc[h], pos=src) for h in heads_all])
+            op, lp = minf.minf_sparse_attn(qp, kp, vp, plans_g, scale=scale, workspace=ws_at)
+            e2.record(stream)
+            minf.minf_permute_rows(op, src, scatter=True, out=og)
+            minf.minf_permute_rows(lp.unsqueeze(-1).contiguous(), src, scatter=True, out=lg.unsqueeze(-1))
+            e3.record(stream)
+            if record is not None:
+                record.append((e0, e1, e2, e3))
+            return bc
+
+        grid_step()
+        torch.cuda.synchronize()
+        recs_g = []
+        for _ in range(max(2, args.steps)):
+            bc_g = grid_step(recs_g)
+        torch.cuda.synchronize()
+        g_step = sum(a.elapsed_time(d_) for a, _, _, d_ in recs_g) / len(recs_g)
+        g_attn = sum(b.elapsed_time(c) for _, b, c, _ in recs_g) / len(recs_g)
+        g_pre = sum(a.elapsed_time(b) for a, b, _, _ in recs_g) / len(recs_g)
+        g_blocks = int(bc_g.long().sum())
+        lse_perm = lg.clone()
+        # the same budget in the original order
+        bj, bd = minf.minf_build_block_index(qg, kg, heads_all, k_b=k_b)
+        plans_b = minf.make_plans([dict(kind="block", blk_idx=bj[h], blk_cnt=bd[h]) for h in heads_all])
+        a_, b_ = ev(), ev()
+        a_.record(stream)
+        _, lse_plain = minf.minf_sparse_attn(qg, kg, vg, plans_b, scale=scale, workspace=ws_at)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        plain_ms = a_.elapsed_time(b_)
+        rows_s = torch.arange(0, n, 4099, device=dev)
+        grid = {
+            "frames": frames, "patches": patches, "k_b": k_b,
+            "step_ms": round(g_step, 3), "permute_and_index_ms": round(g_pre, 3), "attn_ms": round(g_attn, 3),
+            "computed_blocks": g_blocks, "density": round(g_blocks / dense_blocks, 5),
+            "attn_tflops": round(g_blocks * BLOCK_FLOP / (g_attn * 1e-3) / 1e12, 1),
+            "unpermuted_same_budget_attn_ms": round(plain_ms, 3),
+        }
+        if not args.no_dense:
+            a_, b_ = ev(), ev()
+            a_.record(stream)
+            _, lse_d = minf.minf_dense_attn(qg, kg, vg, scale=scale)
+            b_.record(stream)
+            torch.cuda.synchronize()
+            grid["dense_ms"] = round(a_.elapsed_time(b_), 2)
+            grid["speedup_step_vs_dense"] = round(grid["dense_ms"] / g_step, 2)
+            rec = lambda l_: float(torch.exp(l_[:, rows_s].double() - lse_d[:, rows_s].double()).mean())  # noqa: E731
+            grid["recall_permuted"] = round(rec(lse_perm), 4)
+            grid["recall_unpermuted_same_budget"] = round(rec(lse_plain), 4)
+            del lse_d
+        extra["grid_track"] = grid
+        print(f"[bench] grid track: step {g_step:.2f} ms (permute + index {g_pre:.2f}, attention {g_attn:.2f}), "
+              f"density {grid['density']}, recall {grid.get('recall_permuted')} vs unpermuted "
+              f"{grid.get('recall_unpermuted_same_budget')}", file=sys.stderr, flush=True)
+        del qg, kg, vg, og, lg, lse_perm
 
     # decoding on the same cache: the last query row of every head is the new token
     if not args.no_decode:
