@@ -89,14 +89,17 @@ struct BsTopkLaunch {
 };
 
 constexpr int kMaxBlocks = (int)(kMaxTokens / kBlock);
-constexpr int kTile = 64;
+constexpr int kTile = 128;  // query blocks x key blocks per score workgroup
+constexpr int kDChunk = 32;  // pooled dimensions staged in LDS at a time
 
-// Pooled scores of one 64 x 64 tile (query blocks x key blocks) of the lower
-// triangle: each output is a fixed-order fp32 dot product over d = 0..127.
-// Thread (ty, tx) owns query blocks 4ty..4ty+3 and key blocks 4tx..4tx+3.
+// Pooled scores of one 128 x 128 tile (query blocks x key blocks): each output
+// is a fixed-order fp32 dot product over d = 0..127 (d ascending across the
+// staged chunks). Thread (ty, tx) owns query blocks {4ty + i, 64 + 4ty + i}
+// and key blocks {4tx + j, 64 + 4tx + j}, i, j < 4: 64 accumulators, and the
+// four float4 LDS reads per d hit consecutive addresses across the wave.
 __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) {
-  __shared__ __attribute__((aligned(16))) float qs[kHeadDim][kTile];
-  __shared__ __attribute__((aligned(16))) float ks[kHeadDim][kTile];
+  __shared__ __attribute__((aligned(16))) float qs[kDChunk][kTile];
+  __shared__ __attribute__((aligned(16))) float ks[kDChunk][kTile];
   const int ct = blockIdx.x;
   const int bt = a.r0 / kTile + (int)blockIdx.z;
   const bool causal = a.blkmin == nullptr;
@@ -104,57 +107,62 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
   const int hs = blockIdx.y;
   const int tid = threadIdx.x;
   const int b0 = bt * kTile, c0 = ct * kTile;
-  {
-    // query tile, transposed into [d][row]
-    const int r = tid >> 2, dq = (tid & 3) * 32;
-    const bool ok = b0 + r < a.nb;
-    const float* src = a.qbar + ((size_t)hs * a.nb + (ok ? b0 + r : 0)) * kHeadDim + dq;
-#pragma unroll
-    for (int e = 0; e < 32; e += 4) {
-      const float4 x = ok ? *(const float4*)(src + e) : float4{0.f, 0.f, 0.f, 0.f};
-      qs[dq + e][r] = x.x;
-      qs[dq + e + 1][r] = x.y;
-      qs[dq + e + 2][r] = x.z;
-      qs[dq + e + 3][r] = x.w;
-    }
-    // key tile straight from the [d][nb] layout: a wave reads 64 consecutive blocks of one d
-    const int cl = tid & 63, d0 = tid >> 6;
-    const float* kt = a.kbar_t + (size_t)a.kvslot[hs] * kHeadDim * a.nb + c0 + cl;
-    const bool cok = c0 + cl < a.nb;
-#pragma unroll 8
-    for (int d = d0; d < kHeadDim; d += 4) ks[d][cl] = cok ? kt[(size_t)d * a.nb] : 0.f;
-  }
-  __syncthreads();
   const int ty = tid >> 4, tx = tid & 15;
-  float acc[4][4];
+  float acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-#pragma unroll 8
-  for (int d = 0; d < kHeadDim; ++d) {
-    const float4 qv = *(const float4*)&qs[d][4 * ty];
-    const float4 kv = *(const float4*)&ks[d][4 * tx];
-    const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
-    const float kb[4] = {kv.x, kv.y, kv.z, kv.w};
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  // staging roles: query row r = tid / 2 (16 dims each), key dim kd = tid / 8 (16 blocks each)
+  const int qr = tid >> 1, qpart = (tid & 1) * 16;
+  const bool qok = b0 + qr < a.nb;
+  const float* qsrc = a.qbar + ((size_t)hs * a.nb + (qok ? b0 + qr : 0)) * kHeadDim + qpart;
+  const int kd = tid >> 3, kc = (tid & 7) * 16;
+  const float* ksrc = a.kbar_t + (size_t)a.kvslot[hs] * kHeadDim * a.nb + c0 + kc;
+  for (int dc = 0; dc < kHeadDim; dc += kDChunk) {
+    if (dc) __syncthreads();  // the previous chunk has been read
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int e = 0; e < 16; e += 4) {
+      const float4 x = qok ? *(const float4*)(qsrc + dc + e) : float4{0.f, 0.f, 0.f, 0.f};
+      qs[qpart + e][qr] = x.x;
+      qs[qpart + e + 1][qr] = x.y;
+      qs[qpart + e + 2][qr] = x.z;
+      qs[qpart + e + 3][qr] = x.w;
+    }
+    const float* kp = ksrc + (size_t)(dc + kd) * a.nb;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(qa[i], kb[j], acc[i][j]);
+    for (int e = 0; e < 16; ++e) ks[kd][kc + e] = c0 + kc + e < a.nb ? kp[e] : 0.f;
+    __syncthreads();
+#pragma unroll 4
+    for (int d = 0; d < kDChunk; ++d) {
+      const float4 q0 = *(const float4*)&qs[d][4 * ty];
+      const float4 q1 = *(const float4*)&qs[d][64 + 4 * ty];
+      const float4 k0 = *(const float4*)&ks[d][4 * tx];
+      const float4 k1 = *(const float4*)&ks[d][64 + 4 * tx];
+      const float qa[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      const float kb[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(qa[i], kb[j], acc[i][j]);
+    }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int b = b0 + 4 * ty + i;
+  for (int i = 0; i < 8; ++i) {
+    const int b = b0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + i - 4);
     if (b >= a.nb || b >= a.r0 + a.rows) continue;
     float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
-    const int c = c0 + 4 * tx;
     const int clim = causal ? b : a.nb - 1;  // last column stored
-    if (c + 3 <= clim && (a.nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
-      *(float4*)(row + c) = float4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
-    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (c + j <= clim) row[c + j] = acc[i][j];
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + 64 * h + 4 * tx;
+      if (c + 3 <= clim && (a.nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
+        *(float4*)(row + c) = float4{acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c + j <= clim) row[c + j] = acc[i][4 * h + j];
+      }
     }
   }
 }
