@@ -17,6 +17,8 @@ from .minf_oracle import (  # noqa: F401
     vs_block_set,
     vs_column_set,
     vs_mask_block,
+    vs_window_set,
+    vsw_mask_block,
     pool_blocks,
     block_scores,
     block_index,

@@ -55,7 +55,13 @@ Readings where the pages are silent (each one is listed in the design notes):
     and columns), and the Block-Sparse estimate runs on the permuted
     sequence; a key block is eligible when one of its keys precedes one of
     the block's queries in the original order, and attention stays causal in
-    the original order.
+    the original order;
+  * VS with slash-aligned windows (the index-shifting alternative): for
+    query block b each selected slash delta keeps the 64 keys starting at
+    64b - delta, so row 64b + r meets its slash key at window position r;
+    Mask(i) = j <= i and (j in one of b's windows or j in V). It contains
+    every exact slash entry and, for full query blocks, lies inside the
+    64x64-block reading.
 """
 from __future__ import annotations
 
@@ -247,6 +253,35 @@ def vs_mask_block(n: int, s_idx, v_idx, b: int, rows) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# VS index with slash-aligned windows ([T] MMInference part: index shifting,
+# i.e. reading keys at a row-dependent offset, lines slashes up into dense
+# pieces; the reading here keeps, for query block b and each selected slash
+# delta, the 64 consecutive keys that start at 64b - delta: row 64b + r finds
+# its slash key at window position r, so one 64x64 product per slash covers
+# the slash inside the block)
+# ---------------------------------------------------------------------------
+def vs_window_set(n: int, s_idx, b: int) -> np.ndarray:
+    """Keys of query block b's slash windows: union over delta in D with
+    64b + 63 - delta >= 0 of [64b - delta, 64b - delta + 64), clipped to [0, n)."""
+    keys = set()
+    for dl in np.asarray(s_idx, dtype=np.int64).tolist():
+        lo = BLOCK * b - dl
+        if lo + BLOCK - 1 < 0:
+            continue
+        keys.update(range(max(0, lo), min(n, lo + BLOCK)))
+    return np.array(sorted(keys), dtype=np.int64)
+
+
+def vsw_mask_block(n: int, s_idx, v_idx, b: int, rows) -> np.ndarray:
+    """Mask rows of block b for the window reading: j <= i and (j in a slash
+    window of b or j in V)."""
+    j = np.arange(n)
+    sel = np.isin(j, vs_window_set(n, s_idx, b)) | np.isin(j, np.asarray(v_idx, dtype=np.int64))
+    rows = np.asarray(rows, dtype=np.int64)
+    return (j[None, :] <= rows[:, None]) & sel[None, :]
+
+
+# ---------------------------------------------------------------------------
 # Block-Sparse online estimate ([A] "Method": mean pooling of Q and K, and the
 # commutativity of mean pooling with the matrix product, give the block index)
 # ---------------------------------------------------------------------------
@@ -324,7 +359,8 @@ def plan_mask_block(plan: dict, n: int, b: int, rows) -> np.ndarray:
     """Boolean mask [len(rows), N] of one head's plan for rows inside query block b.
 
     plan kinds: "dense" (causal), "ashape" (sink, local), "vs" (v_idx, s_idx),
-    "block" (blk_idx [n_b, k_b] padded with -1 and blk_cnt [n_b]).
+    "vs_window" (v_idx, s_idx; slash-aligned windows), "block" (blk_idx
+    [n_b, k_b] padded with -1 and blk_cnt [n_b]).
     """
     kind = plan["kind"]
     rows = np.asarray(rows, dtype=np.int64)
@@ -334,6 +370,8 @@ def plan_mask_block(plan: dict, n: int, b: int, rows) -> np.ndarray:
         return ashape_mask_block(n, int(plan["sink"]), int(plan["local"]), rows)
     if kind == "vs":
         return vs_mask_block(n, plan["s_idx"], plan["v_idx"], b, rows)
+    if kind == "vs_window":
+        return vsw_mask_block(n, plan["s_idx"], plan["v_idx"], b, rows)
     if kind == "block":
         c = int(plan["blk_cnt"][b])
         return bs_mask_block(n, np.asarray(plan["blk_idx"][b])[:c], b, rows)

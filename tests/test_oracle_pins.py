@@ -526,3 +526,42 @@ def test_permuted_full_budget_is_dense_causal():
     want = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None], is_causal=True, scale=0.3)[0]
     assert np.abs(o - want.numpy()).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# VS with slash-aligned windows
+# ---------------------------------------------------------------------------
+def test_vs_window_contains_exact_slashes_and_lies_inside_block_reading():
+    rng = np.random.default_rng(41)
+    n = 640
+    s_idx = np.sort(rng.choice(n, 9, replace=False))
+    v_idx = np.sort(rng.choice(n, 7, replace=False))
+    for b in range(n // 64):
+        rows = np.arange(64 * b, 64 * b + 64)
+        mw = O.vsw_mask_block(n, s_idx, v_idx, b, rows)
+        mb = O.vs_mask_block(n, s_idx, v_idx, b, rows)
+        assert not (mw & ~mb).any()          # inside the 64x64-block reading (full blocks)
+        for t, i in enumerate(rows):
+            for dl in s_idx:
+                if i - dl >= 0:
+                    assert mw[t, i - dl]       # every exact slash entry
+            for c in v_idx:
+                assert mw[t, c] == (c <= i)    # every vertical column up to the row
+
+
+def test_vs_window_brute_force_and_full_budget():
+    n = 150
+    s_idx = np.array([0, 5, 70, 149])
+    v_idx = np.array([3, 100])
+    for b in range(3):
+        want = set()
+        for dl in s_idx:
+            lo = 64 * b - dl
+            if lo + 63 >= 0:
+                want |= {j for j in range(lo, lo + 64) if 0 <= j < n}
+        assert O.vs_window_set(n, s_idx, b).tolist() == sorted(want)
+    # every offset selected: the windows cover every key up to the row
+    full = np.arange(n)
+    for b in range(3):
+        rows = np.arange(64 * b, min(64 * b + 64, n))
+        assert np.array_equal(O.vsw_mask_block(n, full, [], b, rows), np.arange(n)[None, :] <= rows[:, None])
