@@ -29,6 +29,14 @@
 //    accumulator to MFMA operand without any cross-lane movement.
 //  * tiles are double-buffered in LDS; the next tile's loads are in flight
 //    while the current tile is computed (one barrier per tile).
+//  * every kind walks its key tiles in ascending key order, and the work map
+//    gives each XCD whole chunks of 64 workgroups (one head x 64 pairs for
+//    sparse plans, one GQA group x 16 pairs for dense) that move through the
+//    keys together and share the tiles in that XCD's L2.
+//  * Block-Sparse plans on a permuted sequence (the grid pattern) carry the
+//    original position of every row; a tile that is not entirely earlier than
+//    the wave's earliest query is masked by comparing positions, which the
+//    separate attn_kernel<true> instantiation handles.
 #include "common.h"
 #include "launch.h"
 
