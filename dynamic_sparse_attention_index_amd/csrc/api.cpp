@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -371,7 +372,26 @@ size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
   // per head: the VS offset bitmaps, then the min / max original position of
   // every key block for Block-Sparse heads on a permuted sequence
   return align_up((size_t)hq * 2 * bitmap_words(n) * sizeof(uint32_t)) +
-         align_up((size_t)hq * 2 * nblocks(n) * sizeof(int32_t));
+         align_up((size_t)hq * 2 * nblocks(n) * sizeof(int32_t)) + kAlign;  // + per-XCD counters and a flag
+}
+
+// Launches with Vertical-Slash heads at long lengths queue two launches of
+// the same work: a cooperative one in which the 64 workgroups of an XCD run
+// their items in rounds that start together, and an ordinary one. A flag
+// computed on the device from the offset bitmaps, without a host round trip,
+// lets exactly one of them work: rounds when the items are long (thousands of
+// key tiles), because workgroups that stay at the same key position keep
+// sharing K/V tiles through L2 (at 1M tokens on literal data this cuts the
+// attention's HBM reads from ~35 TB to ~2 TB); the ordinary launch when they
+// are short, because its hardware dispatch balances the load better.
+// MINF_ATTN_ROUNDS=0 in the environment (read on every call) keeps the
+// ordinary launch only; both give bitwise-identical results.
+constexpr int64_t kRoundsMinTokens = 1 << 19;
+constexpr int kRoundsMinTiles = 1024;
+
+static bool rounds_enabled() {
+  const char* e = getenv("MINF_ATTN_ROUNDS");
+  return e == nullptr || e[0] != '0';
 }
 
 static minf_status check_attn_common(const void* q, const void* k, const void* v, void* o, int64_t n, int hq,
@@ -484,6 +504,7 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
   }
   const size_t nbk = (size_t)nblocks(n);
   int32_t* pos_ws = (int32_t*)((char*)workspace + align_up((size_t)hq * words * sizeof(uint32_t)));
+  int32_t* sync_ws = (int32_t*)((char*)pos_ws + align_up((size_t)hq * 2 * nbk * sizeof(int32_t)));
   for (int h = 0; h < hq && any_pos; ++h) {
     if (!plans[h].pos) continue;
     // heads that share a position array share its block extremes
@@ -525,9 +546,22 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
         d2.blkmax = pos_ws + (size_t)first * 2 * nbk + nbk;
       }
     }
+    std::vector<uint32_t*> launch_bits;
+    for (int i = 0; i < nh; ++i)
+      if (plans[h0 + i].kind == MINF_KIND_VS) launch_bits.push_back((uint32_t*)workspace + (size_t)(h0 + i) * words);
     a.head0 = h0;
     a.nh = nh;
     a.hgroup = hg;
+    a.xcd_sync = nullptr;
+    a.rounds_flag = nullptr;
+    if (!launch_bits.empty() && n >= kRoundsMinTokens && rounds_enabled()) {
+      int32_t* flag = sync_ws + 8;
+      hipError_t e = launch_rounds_flag(launch_bits.data(), (int)launch_bits.size(), (int)n, kRoundsMinTiles, flag,
+                                        stream);
+      if (e != hipSuccess) return hip_fail(e, "rounds flag kernel");
+      a.xcd_sync = sync_ws;
+      a.rounds_flag = flag;
+    }
     hipError_t e = launch_attn(a, stream);
     if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
     h0 += nh;

@@ -375,26 +375,17 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
 
 // POSM: the launch has Block-Sparse heads on permuted sequences (a separate
 // instantiation, so the common kernel carries none of that code).
+// One work item: a head and a pair of query blocks. Item i is the (i % C)-th
+// member of chunk i / C; a chunk is one group of hg heads sharing a KV head
+// times C / hg consecutive query-block pairs (C = 64), and chunks go heaviest
+// pair block first.
 template <bool POSM>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
-  __shared__ Smem sm;
-  __shared__ __attribute__((aligned(16))) uint16_t kt0[kTileHalves];
-  __shared__ __attribute__((aligned(16))) uint16_t kt1[kTileHalves];
-  __shared__ __attribute__((aligned(16))) uint16_t vt0[kTileHalves];
-  __shared__ __attribute__((aligned(16))) uint16_t vt1[kTileHalves];
+__device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, Smem& sm, uint16_t* kt0,
+                                          uint16_t* kt1, uint16_t* vt0, uint16_t* vt1) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int npairs = (p.nb + 1) >> 1;
-  // XCD-aware work order. Workgroup L runs on XCD L % 8; that XCD's k-th
-  // workgroup takes item (k / C * 8 + L % 8) * C + k % C, so each XCD works
-  // through whole chunks of C consecutive items. A chunk is one group of hg
-  // heads sharing a KV head times C / hg consecutive query-block pairs, and
-  // C = 64 is what one XCD holds at once (32 CUs x 2 workgroups): the
-  // workgroups resident on an XCD stream the same K/V tiles through its L2.
-  // Chunks go heaviest pair block first.
-  const int slot = blockIdx.x >> 3;
-  const int item = ((slot / kChunk) * kXcds + (int)(blockIdx.x & (kXcds - 1))) * kChunk + slot % kChunk;
   const int hg = p.hgroup;
   const int ppc = kChunk / hg;                  // pairs per chunk
   const int npb = (npairs + ppc - 1) / ppc;     // pair blocks
@@ -669,6 +660,71 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   }
 }
 
+// The 64 workgroups of one XCD wait for each other between rounds: a counter
+// per XCD, raised once per workgroup and round. The wait is bounded, so the
+// kernel ends even if the group were not resident together (only the L2
+// sharing would suffer).
+constexpr int kSpinLimit = 1 << 22;
+__device__ __forceinline__ void xcd_barrier(int32_t* ctr, int target) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(ctr, 1);
+    int spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target && spins < kSpinLimit) {
+      __builtin_amdgcn_s_sleep(4);
+      ++spins;
+    }
+  }
+  __syncthreads();
+}
+
+// XCD-aware work order. Workgroup L runs on XCD L % 8; that XCD's k-th
+// workgroup takes item (k / C * 8 + L % 8) * C + k % C, so each XCD works
+// through whole chunks of C consecutive items, C = 64 being what one XCD holds
+// at once (32 CUs x 2 workgroups): the workgroups resident on an XCD stream
+// the same K/V tiles through its L2.
+template <bool POSM>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
+  __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t vt0[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t vt1[kTileHalves];
+  // when a rounds launch of the same work was queued beside this one, only one of them works
+  if (p.rounds_flag != nullptr && *p.rounds_flag != 0) return;
+  const int slot = blockIdx.x >> 3;
+  const int xcd = (int)(blockIdx.x & (kXcds - 1));
+  attn_item<POSM>(p, ((slot / kChunk) * kXcds + xcd) * kChunk + slot % kChunk, sm, kt0, kt1, vt0, vt1);
+}
+
+// Rounds variant: exactly 8 x 64 workgroups, launched cooperatively so that
+// they are resident together. In round r workgroup L takes item
+// (r * 8 + L % 8) * C + L / 8, and the 64 workgroups of an XCD start every
+// round together: long items (thousands of key tiles) then stay near the same
+// key position and keep sharing K/V tiles in that XCD's L2. It works only
+// when *p.rounds_flag is set (the flag is computed on the device from the
+// offset bitmaps); otherwise the ordinary launch queued after it does.
+template <bool POSM>
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel_rounds(const AttnLaunch p) {
+  __shared__ Smem sm;
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t kt1[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t vt0[kTileHalves];
+  __shared__ __attribute__((aligned(16))) uint16_t vt1[kTileHalves];
+  if (*p.rounds_flag == 0) return;
+  const int slot = blockIdx.x >> 3;
+  const int xcd = (int)(blockIdx.x & (kXcds - 1));
+  for (int r = 0; r < p.rounds; ++r) {
+    attn_item<POSM>(p, (r * kXcds + xcd) * kChunk + slot, sm, kt0, kt1, vt0, vt1);
+    xcd_barrier(p.xcd_sync + xcd, kChunk * (r + 1));
+  }
+}
+
+__global__ void zero_counters_kernel(int32_t* c, int n) {
+  if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+}
+
+
 // Block offsets covered by a VS head's slash lines. For a full query block b,
 // offset dl = 64q + rho (0 <= rho < 64) meets key block b - q (rows with
 // t >= rho) and, when rho > 0, key block b - q - 1 (rows with t < rho); so
@@ -709,6 +765,27 @@ __global__ __launch_bounds__(256) void vs_offset_bits_kernel(const OffBitsLaunch
 
 }  // namespace
 
+// Whether this device keeps all 8 x 64 workgroups of a rounds launch resident
+// together (cooperative launches are supported and two workgroups fit per CU
+// on at least 256 CUs). Asked once per device and instantiation.
+static bool rounds_supported(bool posm) {
+  static int cache[2][64] = {};  // 0 unknown, 1 yes, 2 no
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  int& c = cache[posm][dev];
+  if (c == 0) {
+    int coop = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, posm ? (const void*)attn_kernel_rounds<true> : (const void*)attn_kernel_rounds<false>,
+          kThreads, 0);
+    c = (e == hipSuccess && coop && (long long)cus * per_cu >= kXcds * kChunk) ? 1 : 2;
+  }
+  return c == 1;
+}
+
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   const int npairs = (a.nb + 1) / 2;
   if (npairs <= 0 || a.nh <= 0 || a.hgroup <= 0 || a.nh % a.hgroup != 0 || kChunk % a.hgroup != 0)
@@ -719,10 +796,61 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   const long long grid = (chunks + kXcds - 1) / kXcds * kXcds * kChunk;
   bool posm = false;
   for (int i = 0; i < a.nh; ++i) posm |= a.heads[i].pos != nullptr;
+  AttnLaunch c = a;
+  c.xcd_sync = nullptr;
+  c.rounds_flag = nullptr;
+  if (a.xcd_sync != nullptr && a.rounds_flag != nullptr && rounds_supported(posm)) {
+    // the rounds launch, then the ordinary one; the device-side flag lets exactly one of them work
+    AttnLaunch b = a;
+    b.rounds = (int)((chunks + kXcds - 1) / kXcds);
+    hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, b.xcd_sync, kXcds);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    void* args[] = {&b};
+    const void* fn = posm ? (const void*)attn_kernel_rounds<true> : (const void*)attn_kernel_rounds<false>;
+    e = hipLaunchCooperativeKernel(fn, dim3(kXcds * kChunk), dim3(kThreads), args, 0, stream);
+    if (e == hipSuccess)
+      c.rounds_flag = a.rounds_flag;
+    else
+      (void)hipGetLastError();  // not launchable cooperatively here: the ordinary launch does all the work
+  }
   if (posm)
-    hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, c);
   else
-    hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, c);
+  return hipGetLastError();
+}
+
+// Rounds pay off when the work items are long: flag = 1 when the listed VS
+// heads' offset sets O u (O + 1) hold on average at least `min_tiles` block
+// offsets (the tile count of the longest query-block pairs).
+__global__ __launch_bounds__(256) void rounds_flag_kernel(const OffBitsLaunch a, int count, int min_tiles,
+                                                          int32_t* flag) {
+  __shared__ unsigned long long tot;
+  if (threadIdx.x == 0) tot = 0;
+  __syncthreads();
+  const int nwords = (a.nb >> 5) + 1;
+  unsigned long long mine = 0;
+  for (int h = 0; h < count; ++h) {
+    const uint32_t* w = a.bits[h];
+    for (int i = threadIdx.x; i < nwords; i += 256) {
+      const uint32_t prev = i > 0 ? w[i - 1] : 0u;
+      mine += (unsigned long long)__popc(w[i] | (w[i] << 1) | (prev >> 31));
+    }
+  }
+  atomicAdd(&tot, mine);
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = (count > 0 && tot >= (unsigned long long)min_tiles * count) ? 1 : 0;
+}
+
+hipError_t launch_rounds_flag(uint32_t* const* bits, int count, int n, int min_tiles, int32_t* flag,
+                              hipStream_t stream) {
+  OffBitsLaunch a{};
+  const int c = count < kMaxLaunchHeads ? count : kMaxLaunchHeads;
+  for (int i = 0; i < c; ++i) a.bits[i] = bits[i];
+  a.n = n;
+  a.nb = (n + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(rounds_flag_kernel, dim3(1), dim3(256), 0, stream, a, c, min_tiles, flag);
   return hipGetLastError();
 }
 

@@ -31,12 +31,18 @@ struct AttnLaunch {
   int32_t hgroup;  // heads per work chunk: divides nh and 64; consecutive heads (they share K/V when
                    // they fall in one GQA group)
   float scale_log2;
+  int32_t* xcd_sync;          // per-XCD barrier counters (8 ints) for a rounds launch, else null
+  const int32_t* rounds_flag;  // device flag: 1 = the rounds launch works, 0 = the ordinary launch does
+  int32_t rounds;              // set by launch_attn
   AttnHead heads[kMaxLaunchHeads];
 };
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_vs_offset_bits(const int32_t* const* s_idx, const int32_t* k_s, uint32_t* const* bits,
                                  int count, int n, hipStream_t stream);
+// flag = 1 when the VS heads' offset bitmaps (up to 32) average at least min_tiles tiles per item
+hipError_t launch_rounds_flag(uint32_t* const* bits, int count, int n, int min_tiles, int32_t* flag,
+                              hipStream_t stream);
 
 struct VsGroup {
   int32_t kv;        // KV head of the group

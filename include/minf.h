@@ -202,6 +202,14 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
                              const minf_head_plan* plans, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* Launch order: with Vertical-Slash heads and n >= 2^19, the heads' offset
+ * sets decide on the device whether the workgroups of each XCD take their
+ * work items in rounds that start together (long items share K/V tiles in
+ * L2) or as one ordinary launch; results are bitwise identical either way.
+ * The environment variable MINF_ATTN_ROUNDS=0 (read on every call) keeps the
+ * ordinary launch only. The rounds launch is cooperative; where the device
+ * refuses it, the ordinary launch does the work. */
+
 /* A BLOCK plan with pos != NULL describes a permuted sequence (q, k, v, o
  * and lse are all in the permuted row order): key block c may appear in any
  * row of blk_idx, and row i attends to key j when block(j) is listed for

@@ -236,3 +236,33 @@ def test_mixed_heads_gqa_and_determinism(gpu_lib):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(vi, vi2) and torch.equal(si, si2) and torch.equal(bi, bi2) and torch.equal(bc, bc2)
+
+
+def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch):
+    # 2^19 tokens, scattered slash offsets: long work items, so the XCD-round
+    # launch takes the work; MINF_ATTN_ROUNDS=0 forces the ordinary launch
+    n, hq = 1 << 19, 4
+    q, k, v, _ = _qkv(n, hq, 1, 25)
+    g = torch.Generator().manual_seed(26)
+    plans = []
+    for h in range(hq):
+        si = torch.randperm(n, generator=g)[:3000 + 500 * h].sort().values.to(torch.int32)
+        vi = torch.randperm(n, generator=g)[:400].sort().values.to(torch.int32)
+        plans.append(dict(kind="vs", v_idx=vi.cuda(), s_idx=si.cuda()))
+    monkeypatch.delenv("MINF_ATTN_ROUNDS", raising=False)
+    o1, l1 = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    monkeypatch.setenv("MINF_ATTN_ROUNDS", "0")
+    o2, l2 = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # sampled rows of one head against the oracle: the first block, a middle one and the last
+    rows = np.concatenate([np.arange(0, 64), np.arange(n // 2, n // 2 + 64), np.arange(n - 64, n)])
+    h = 2
+    qh = np.zeros((1, n, 128), np.float32)
+    qh[0, rows] = to_np(q[h][torch.as_tensor(rows, device="cuda")])
+    wo, wl = O.sparse_attn(qh, to_np(k), to_np(v), 1, 1, SCALE, _np_plans([plans[h]]), rows=rows)
+    t = torch.as_tensor(rows, device="cuda")
+    err = max_abs(to_np(o1[h][t]), wo[0])
+    print(f"  rounds launch: max-abs err {err:.3e}", flush=True)
+    assert err <= OUT_TOL
+    check_lse(l1[h][t].cpu().numpy(), wl[0])
