@@ -679,7 +679,7 @@ def main():
         "density": density,
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": profiled_traffic(args.config),
-                     "kernel": "attn_kernel", "flop_per_launch": flop,
+                     "kernel": "attn_kernel_rounds or attn_kernel (one sparse attention launch)", "flop_per_launch": flop,
                      "flop_rule": "4*64*64*128 per computed 64x64 block + 4*64*128 per gathered column per query block",
                      "useful_flop_per_launch": useful_flop,
                      "useful_tflops": round(useful_flop / (attn_ms * 1e-3) / 1e12, 1)},

@@ -14,8 +14,8 @@
 //    staged through LDS, so every pooled vector is read once per tile rather
 //    than once per query block; each score is a fixed-order fp32 dot product,
 //    written to a score buffer that holds a bounded band of rows at a time;
-//  * top-k: one workgroup per (head, query block); the row's scores are copied
-//    to LDS (up to 16384 blocks = 64 KiB) for the shared radix select.
+//  * top-k: one workgroup per (head, query block); the row's scores are held
+//    in registers (up to 64 per thread) for an exact bitwise search.
 #include <algorithm>
 
 #include "common.h"
@@ -88,7 +88,7 @@ struct BsTopkLaunch {
   int32_t outslot[kMaxPoolHeads];
 };
 
-constexpr int kMaxBlocks = (int)(kMaxTokens / kBlock);
+static_assert(kMaxTokens / kBlock <= 256 * 64, "the top-k holds at most 64 candidates per thread");
 constexpr int kTile = 128;  // query blocks x key blocks per score workgroup
 constexpr int kDChunk = 32;  // pooled dimensions staged in LDS at a time
 
@@ -167,16 +167,56 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
   }
 }
 
+// Sum over the 4 waves of a wave-uniform value; `red` is LDS of 8 ints used
+// as two alternating halves (a wave can only overwrite a half again after
+// every wave has passed the next call's barrier, i.e. has read it).
+__device__ __forceinline__ int block_sum4(int v, int* red, int& half) {
+  if ((threadIdx.x & 63) == 0) red[4 * half + (threadIdx.x >> 6)] = v;
+  __syncthreads();
+  const int s = red[4 * half] + red[4 * half + 1] + red[4 * half + 2] + red[4 * half + 3];
+  half ^= 1;
+  return s;
+}
+
+// Exclusive prefix sum over the 256 threads of one int each; wsum: 4 ints of LDS.
+__device__ __forceinline__ int block_excl_scan256(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) before += w < wave ? wsum[w] : 0;
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return before + incl - v;
+}
+
 // Top-k_b key blocks of every query block of the round, from the stored scores.
 // Causal: the candidates are c <= b. Permuted: every c whose earliest original
-// position is not after the query block's latest one; the others get the
-// smallest sortable key, below every finite score, so they are never picked
-// while k does not exceed the eligible count.
+// position is not after the query block's latest one. One workgroup per row;
+// candidate c = 256 i + tid is held as sortable key k[i] in registers, 0 for
+// an ineligible block (eligible keys are at least 1).
+//  * the k-th largest key t is found bit by bit from the top: t | bit is kept
+//    while at least k keys are >= it (counted with wave ballots and one
+//    cross-wave sum per bit); a count of exactly k ends the search early;
+//  * selected: every key > t, then the lowest-id keys == t until k are taken;
+//  * the waves' ballots give the selected set as 64-bit words of consecutive
+//    block ids, and a scan of their popcounts writes the ids in ascending order.
+// There are no atomics, so skewed score distributions cost nothing extra.
+template <int PER>
 __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
-  __shared__ uint32_t sc[kMaxBlocks];
-  __shared__ int hist[2048];
-  __shared__ int scratch[16];
+  __shared__ uint64_t gmask[4 * PER];
+  __shared__ uint64_t emask[4 * PER];
+  __shared__ int red[8];
+  __shared__ int wsum[4];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int r_end = a.r0 + a.rows < a.nb ? a.r0 + a.rows : a.nb;
   const int b = r_end - 1 - (int)blockIdx.x;  // longest rows first
   const int hs = blockIdx.y;
@@ -185,48 +225,99 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   const bool causal = a.blkmin == nullptr;
   const int ncand = causal ? b + 1 : a.nb;
   const float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
-  int nelig = b + 1;
-  if (!causal) {
-    const int hi = a.blkmax[b];
-    int cnt = 0;
-    for (int c = tid; c < a.nb; c += 256) {
-      const bool e = a.blkmin[c] <= hi;
-      sc[c] = e ? sortable_key(row[c]) : 0u;
-      cnt += e;
+  const int hi = causal ? 0 : a.blkmax[b];
+  // all loads first (addresses clamped into the row), then the keys
+  float sv[PER];
+  int mv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = 256 * i + tid < a.nb ? 256 * i + tid : a.nb - 1;
+    sv[i] = 0.f;
+    mv[i] = 0;
+    if (256 * i < ncand) {
+      sv[i] = row[c];
+      if (!causal) mv[i] = a.blkmin[c];
     }
-    // block-wide count of the eligible blocks
-    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
-    if ((tid & 63) == 0) scratch[8 + (tid >> 6)] = cnt;
-    __syncthreads();
-    nelig = scratch[8] + scratch[9] + scratch[10] + scratch[11];
-    __syncthreads();
   }
+  uint32_t key[PER];
+  int wc = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = 256 * i + tid;
+    const bool e = c < ncand && (causal || mv[i] <= hi);
+    const uint32_t u = sortable_key(sv[i]);
+    key[i] = e ? (u > 0u ? u : 1u) : 0u;  // an eligible key is never 0, even for a NaN score
+    if (256 * i < ncand) wc += (int)__popcll(__ballot(e));
+  }
+  int half = 0;
+  const int nelig = block_sum4(wc, red, half);
   const int keep = nelig < kb ? nelig : kb;
-  int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
-  if (tid == 0) a.blk_cnt[(size_t)slot * a.nb + b] = keep;
-  for (int e = keep + tid; e < kb; e += 256) out[e] = -1;
-  if (keep == nelig) {
-    // every eligible block is kept: list them in order
-    if (causal) {
-      for (int c = tid; c <= b; c += 256) out[c] = c;
-    } else {
-      int written = 0;
-      for (int base = 0; base < a.nb; base += 256) {
-        const int c = base + tid;
-        const bool e = c < a.nb && sc[c] != 0u;
-        int tot;
-        const int pos = block_excl_scan_count<256>(e, scratch, tot);
-        if (e) out[written + pos] = c;
-        written += tot;
+  // selection rule: key > thr, plus the `need` lowest-id keys == thr
+  uint32_t thr = 0u;
+  int need = 0;
+  if (keep < nelig) {
+    uint32_t t = 0u;
+    bool exact = false;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (256 * i < ncand) c += (int)__popcll(__ballot(key[i] >= cand));
+      c = block_sum4(c, red, half);
+      if (c >= kb) {
+        t = cand;
+        if (c == kb) {
+          exact = true;
+          break;
+        }
       }
     }
-    return;
+    if (exact) {
+      thr = t - 1u;  // exactly k keys are >= t
+    } else {
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (256 * i < ncand) c += (int)__popcll(__ballot(key[i] > t));
+      thr = t;
+      need = kb - block_sum4(c, red, half);
+    }
   }
-  if (causal)
-    for (int c = tid; c <= b; c += 256) sc[c] = sortable_key(row[c]);
+  // word 4 i + wave holds blocks 256 i + 64 wave .. + 63, bit = lane
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint64_t g = __ballot(key[i] > thr);
+    const uint64_t e = __ballot(need > 0 && key[i] == thr);
+    if (lane == 0) {
+      gmask[4 * i + wave] = g;
+      emask[4 * i + wave] = e;
+    }
+  }
   __syncthreads();
-  radix_topk_ordered<256>([&](int i) { return sc[i]; }, ncand, kb, hist, scratch,
-                          [&](int pos, int i) { out[pos] = i; });
+  uint64_t sel = 0ull, eq = 0ull;
+  if (tid < 4 * PER) {
+    sel = gmask[tid];
+    eq = emask[tid];
+  }
+  int tot;
+  if (need > 0) {
+    int m = need - block_excl_scan256((int)__popcll(eq), wsum, tot);  // equal keys this word may take
+    while (m > 0 && eq != 0ull) {
+      const uint64_t low = eq & (~eq + 1ull);
+      sel |= low;
+      eq ^= low;
+      --m;
+    }
+  }
+  int pos = block_excl_scan256((int)__popcll(sel), wsum, tot);
+  int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
+  while (sel != 0ull) {
+    out[pos++] = 64 * tid + __builtin_ctzll(sel);
+    sel &= sel - 1ull;
+  }
+  for (int e = keep + tid; e < kb; e += 256) out[e] = -1;
+  if (tid == 0) a.blk_cnt[(size_t)slot * a.nb + b] = keep;
 }
 
 // Per-block min and max of the original positions of a permuted sequence.
@@ -247,8 +338,10 @@ __global__ __launch_bounds__(64) void block_minmax_kernel(const int32_t* pos, in
 
 // Row permutation of [heads][n] rows of row_bytes bytes (a multiple of 4):
 // gather out[h][t] = x[h][src[t]], or scatter out[h][src[t]] = x[h][t].
-__global__ __launch_bounds__(256) void permute_rows_kernel(const uint32_t* x, uint32_t* out, int64_t n,
-                                                           int words, const int32_t* src, int scatter) {
+// W is the access unit (16 bytes when the row size allows, else 4).
+template <typename W>
+__global__ __launch_bounds__(256) void permute_rows_kernel(const W* x, W* out, int64_t n, int words,
+                                                           const int32_t* src, int scatter) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int h = blockIdx.y;
   if (idx >= n * words) return;
@@ -305,10 +398,16 @@ hipError_t launch_block_minmax(const int32_t* pos, int n, int32_t* bmin, int32_t
 
 hipError_t launch_permute_rows(const void* x, void* out, int heads, int64_t n, int row_bytes, const int32_t* src,
                                int scatter, hipStream_t stream) {
-  const int words = row_bytes / 4;
+  const bool wide = row_bytes % 16 == 0 && ((uintptr_t)x | (uintptr_t)out) % 16 == 0;
+  const int words = wide ? row_bytes / 16 : row_bytes / 4;
   const int64_t total = n * words;
-  hipLaunchKernelGGL(permute_rows_kernel, dim3((unsigned)((total + 255) / 256), heads), dim3(256), 0, stream,
-                     (const uint32_t*)x, (uint32_t*)out, n, words, src, scatter);
+  const dim3 grid((unsigned)((total + 255) / 256), heads);
+  if (wide)
+    hipLaunchKernelGGL(permute_rows_kernel<u32x4>, grid, dim3(256), 0, stream, (const u32x4*)x, (u32x4*)out, n,
+                       words, src, scatter);
+  else
+    hipLaunchKernelGGL(permute_rows_kernel<uint32_t>, grid, dim3(256), 0, stream, (const uint32_t*)x,
+                       (uint32_t*)out, n, words, src, scatter);
   return hipGetLastError();
 }
 
@@ -339,7 +438,15 @@ hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32
       const int row_tiles = (std::min(nb, r0 + rows) - r0 + kTile - 1) / kTile;
       const int col_tiles = blkmin ? nbt : std::min(nbt, (r0 + rows) / kTile);
       hipLaunchKernelGGL(block_score_kernel, dim3(col_tiles, c, row_tiles), dim3(256), 0, stream, a);
-      hipLaunchKernelGGL(block_topk_kernel, dim3(std::min(rows, nb - r0), c), dim3(256), 0, stream, a);
+      const dim3 tg(std::min(rows, nb - r0), c);
+      if (nb <= 256)
+        hipLaunchKernelGGL(block_topk_kernel<1>, tg, dim3(256), 0, stream, a);
+      else if (nb <= 1024)
+        hipLaunchKernelGGL(block_topk_kernel<4>, tg, dim3(256), 0, stream, a);
+      else if (nb <= 4096)
+        hipLaunchKernelGGL(block_topk_kernel<16>, tg, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL(block_topk_kernel<64>, tg, dim3(256), 0, stream, a);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
