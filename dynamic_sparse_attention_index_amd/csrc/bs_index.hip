@@ -167,48 +167,11 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
   }
 }
 
-// Sum over the 4 waves of a wave-uniform value; `red` is LDS of 8 ints used
-// as two alternating halves (a wave can only overwrite a half again after
-// every wave has passed the next call's barrier, i.e. has read it).
-__device__ __forceinline__ int block_sum4(int v, int* red, int& half) {
-  if ((threadIdx.x & 63) == 0) red[4 * half + (threadIdx.x >> 6)] = v;
-  __syncthreads();
-  const int s = red[4 * half] + red[4 * half + 1] + red[4 * half + 2] + red[4 * half + 3];
-  half ^= 1;
-  return s;
-}
-
-// Exclusive prefix sum over the 256 threads of one int each; wsum: 4 ints of LDS.
-__device__ __forceinline__ int block_excl_scan256(int v, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) before += w < wave ? wsum[w] : 0;
-  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-  __syncthreads();
-  return before + incl - v;
-}
-
 // Top-k_b key blocks of every query block of the round, from the stored scores.
 // Causal: the candidates are c <= b. Permuted: every c whose earliest original
 // position is not after the query block's latest one. One workgroup per row;
-// candidate c = 256 i + tid is held as sortable key k[i] in registers, 0 for
-// an ineligible block (eligible keys are at least 1).
-//  * the k-th largest key t is found bit by bit from the top: t | bit is kept
-//    while at least k keys are >= it (counted with wave ballots and one
-//    cross-wave sum per bit); a count of exactly k ends the search early;
-//  * selected: every key > t, then the lowest-id keys == t until k are taken;
-//  * the waves' ballots give the selected set as 64-bit words of consecutive
-//    block ids, and a scan of their popcounts writes the ids in ascending order.
-// There are no atomics, so skewed score distributions cost nothing extra.
+// candidate c = 256 i + tid is held as sortable key k[i] in registers (0 for
+// an ineligible block) for the exact register top-k (ties to the lower id).
 template <int PER>
 __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   __shared__ uint64_t gmask[4 * PER];
@@ -216,7 +179,6 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   __shared__ int red[8];
   __shared__ int wsum[4];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const int r_end = a.r0 + a.rows < a.nb ? a.r0 + a.rows : a.nb;
   const int b = r_end - 1 - (int)blockIdx.x;  // longest rows first
   const int hs = blockIdx.y;
@@ -240,82 +202,16 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
     }
   }
   uint32_t key[PER];
-  int wc = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = 256 * i + tid;
     const bool e = c < ncand && (causal || mv[i] <= hi);
     const uint32_t u = sortable_key(sv[i]);
     key[i] = e ? (u > 0u ? u : 1u) : 0u;  // an eligible key is never 0, even for a NaN score
-    if (256 * i < ncand) wc += (int)__popcll(__ballot(e));
   }
-  int half = 0;
-  const int nelig = block_sum4(wc, red, half);
-  const int keep = nelig < kb ? nelig : kb;
-  // selection rule: key > thr, plus the `need` lowest-id keys == thr
-  uint32_t thr = 0u;
-  int need = 0;
-  if (keep < nelig) {
-    uint32_t t = 0u;
-    bool exact = false;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = t | (1u << bit);
-      int c = 0;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (256 * i < ncand) c += (int)__popcll(__ballot(key[i] >= cand));
-      c = block_sum4(c, red, half);
-      if (c >= kb) {
-        t = cand;
-        if (c == kb) {
-          exact = true;
-          break;
-        }
-      }
-    }
-    if (exact) {
-      thr = t - 1u;  // exactly k keys are >= t
-    } else {
-      int c = 0;
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (256 * i < ncand) c += (int)__popcll(__ballot(key[i] > t));
-      thr = t;
-      need = kb - block_sum4(c, red, half);
-    }
-  }
-  // word 4 i + wave holds blocks 256 i + 64 wave .. + 63, bit = lane
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const uint64_t g = __ballot(key[i] > thr);
-    const uint64_t e = __ballot(need > 0 && key[i] == thr);
-    if (lane == 0) {
-      gmask[4 * i + wave] = g;
-      emask[4 * i + wave] = e;
-    }
-  }
-  __syncthreads();
-  uint64_t sel = 0ull, eq = 0ull;
-  if (tid < 4 * PER) {
-    sel = gmask[tid];
-    eq = emask[tid];
-  }
-  int tot;
-  if (need > 0) {
-    int m = need - block_excl_scan256((int)__popcll(eq), wsum, tot);  // equal keys this word may take
-    while (m > 0 && eq != 0ull) {
-      const uint64_t low = eq & (~eq + 1ull);
-      sel |= low;
-      eq ^= low;
-      --m;
-    }
-  }
-  int pos = block_excl_scan256((int)__popcll(sel), wsum, tot);
   int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
-  while (sel != 0ull) {
-    out[pos++] = 64 * tid + __builtin_ctzll(sel);
-    sel &= sel - 1ull;
-  }
+  const int keep = reg_topk_ordered<256, PER>(key, ncand, kb, gmask, emask, red, wsum,
+                                              [&](int pos, int c) { out[pos] = c; });
   for (int e = keep + tid; e < kb; e += 256) out[e] = -1;
   if (tid == 0) a.blk_cnt[(size_t)slot * a.nb + b] = keep;
 }

@@ -72,15 +72,8 @@ __host__ __device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
   return (a % b != 0 && ((a < 0) != (b < 0))) ? q - 1 : q;
 }
 
-// ---------------------------------------------------------------------------
-// Block-wide radix select of the k largest keys (ties to the lower index),
-// written out in ascending index order. Used by the VS top-k (keys in global
-// memory) and the Block-Sparse row top-k (keys in LDS).
-//   KeyFn(i) -> uint32 sortable key of element i, i in [0, n).
-//   0 < k < n is assumed; callers handle k == 0 and k >= n themselves.
-// NT threads (a multiple of 64, at most 1024). `hist` is LDS of 2048 ints,
-// `scratch` LDS of at least 2 * (NT / 64) + 8 ints.
-// ---------------------------------------------------------------------------
+// Exclusive count of set flags over the NT threads of a block, in thread
+// order; `wsum`: NT / 64 ints of LDS; `total` gets the block's count.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan_count(bool flag, int* wsum, int& total) {
   const int lane = threadIdx.x & 63;
@@ -102,76 +95,135 @@ __device__ __forceinline__ int block_excl_scan_count(bool flag, int* wsum, int& 
   return before + in_wave;
 }
 
-template <int NT, class KeyFn, class OutFn>
-__device__ void radix_topk_ordered(KeyFn key_of, int n, int k, int* hist, int* scratch, OutFn out) {
+// ---------------------------------------------------------------------------
+// Block-wide exact top-k of register-held keys. Element c = NT * i + tid of
+// the block's candidate list is key[i] of thread tid: 0 marks a non-candidate,
+// candidates carry keys >= 1. Only i with NT * i < n are looked at. Writes
+// the ids of the min(k, candidates) largest keys, ties to the lower id, in
+// ascending order through out(pos, c), and returns their number.
+//  * the k-th largest key t is built bit by bit from the top: t | bit is kept
+//    while at least k keys are >= it, counted with wave ballots and one
+//    cross-wave sum per bit; a count of exactly k ends the search early;
+//  * the selected set (every key > t, then the lowest-id keys == t until k
+//    are taken) is formed as 64-bit ballot words of consecutive ids and
+//    written in ascending order through a popcount scan.
+// No atomics, so skewed key distributions cost nothing extra.
+// LDS: gmask and emask of NT / 64 * PER words each, red of 2 * NT / 64 ints,
+// wsum of NT / 64 ints. Every thread of the block must call it.
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ int block_sum_waves(int v, int* red, int& half) {
+  // v is uniform within each wave; `red` alternates halves, so one barrier per call suffices
+  constexpr int NW = NT / 64;
+  if ((threadIdx.x & 63) == 0) red[NW * half + (threadIdx.x >> 6)] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[NW * half + w];
+  half ^= 1;
+  return s;
+}
+
+template <int NT>
+__device__ __forceinline__ int block_excl_scan_int(int v, int* wsum, int& total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = wsum[w];
+    before += w < wave ? c : 0;
+    tot += c;
+  }
+  total = tot;
+  __syncthreads();
+  return before + incl - v;
+}
+
+template <int NT, int PER, class OutFn>
+__device__ int reg_topk_ordered(const uint32_t (&key)[PER], int n, int k, uint64_t* gmask, uint64_t* emask,
+                                int* red, int* wsum, OutFn out) {
+  constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-  int krem = k;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const int nbins = 1 << widths[pass];
-    for (int i = tid; i < nbins; i += NT) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      uint32_t u = key_of(i);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nbins - 1)], 1);
-    }
-    __syncthreads();
-    // wave 0 finds the digit holding the krem-th largest key (searching from the top bin)
-    if (tid < 64) {
-      const int per = nbins / 64;  // 32 or 16 bins per lane, lane 0 owns the top bins
-      const int hi = nbins - per * tid;  // bins [hi - per, hi)
-      int s = 0;
-      for (int b = hi - 1; b >= hi - per; --b) s += hist[b];
-      // inclusive scan over lanes (lane 0 = top chunk)
-      int incl = s;
-      for (int off = 1; off < 64; off <<= 1) {
-        int o = __shfl_up(incl, off);
-        if (tid >= off) incl += o;
-      }
-      int excl = incl - s;
-      if (excl < krem && krem <= incl) {
-        int cum = excl;
-        for (int b = hi - 1; b >= hi - per; --b) {
-          int h = hist[b];
-          if (cum + h >= krem) {
-            scratch[0] = b;
-            scratch[1] = krem - cum;
-            break;
-          }
-          cum += h;
+  const int lane = tid & 63, wave = tid >> 6;
+  int half = 0;
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (NT * i < n) c += (int)__popcll(__ballot(key[i] > 0u));
+  const int ncand = block_sum_waves<NT>(c, red, half);
+  const int keep = ncand < k ? ncand : k;
+  uint32_t thr = 0u;  // selected: key > thr, then `need` lowest-id keys == thr
+  int need = 0;
+  if (keep < ncand) {
+    uint32_t t = 0u;
+    bool exact = false;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = t | (1u << bit);
+      c = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (NT * i < n) c += (int)__popcll(__ballot(key[i] >= cand));
+      c = block_sum_waves<NT>(c, red, half);
+      if (c >= k) {
+        t = cand;
+        if (c == k) {
+          exact = true;
+          break;
         }
       }
     }
-    __syncthreads();
-    const int digit = scratch[0];
-    krem = scratch[1];
-    prefix |= (uint32_t)digit << shift;
-    pmask |= (uint32_t)(nbins - 1) << shift;
-    __syncthreads();
+    if (exact) {
+      thr = t - 1u;  // exactly k keys are >= t
+    } else {
+      c = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (NT * i < n) c += (int)__popcll(__ballot(key[i] > t));
+      thr = t;
+      need = k - block_sum_waves<NT>(c, red, half);
+    }
   }
-  // prefix is now the exact key of the k-th largest element; krem of the keys
-  // equal to it are taken, lowest indices first.
-  const uint32_t thr = prefix;
-  const int need_eq = krem;
-  int eq_seen = 0, written = 0;
-  int* wsum = scratch + 4;
-  for (int base = 0; base < n && written < k; base += NT) {
-    const int i = base + tid;
-    uint32_t u = (i < n) ? key_of(i) : 0u;
-    bool gt = (i < n) && (u > thr);
-    bool eq = (i < n) && (u == thr);
-    int eq_tot;
-    int eq_rank = block_excl_scan_count<NT>(eq, wsum, eq_tot);
-    bool sel = gt || (eq && (eq_seen + eq_rank < need_eq));
-    int sel_tot;
-    int pos = block_excl_scan_count<NT>(sel, wsum, sel_tot);
-    if (sel) out(written + pos, i);
-    eq_seen += eq_tot;
-    written += sel_tot;
+  // word NW * i + wave holds ids NT * i + 64 * wave .. + 63, bit = lane
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint64_t g = __ballot(key[i] > thr);
+    const uint64_t e = __ballot(need > 0 && key[i] == thr);
+    if (lane == 0) {
+      gmask[NW * i + wave] = g;
+      emask[NW * i + wave] = e;
+    }
   }
+  __syncthreads();
+  uint64_t sel = 0ull, eq = 0ull;
+  if (tid < NW * PER) {
+    sel = gmask[tid];
+    eq = emask[tid];
+  }
+  int tot;
+  if (need > 0) {
+    int m = need - block_excl_scan_int<NT>((int)__popcll(eq), wsum, tot);  // equal keys this word may take
+    while (m > 0 && eq != 0ull) {
+      const uint64_t low = eq & (~eq + 1ull);
+      sel |= low;
+      eq ^= low;
+      --m;
+    }
+  }
+  int pos = block_excl_scan_int<NT>((int)__popcll(sel), wsum, tot);
+  while (sel != 0ull) {
+    out(pos++, 64 * tid + __builtin_ctzll(sel));
+    sel &= sel - 1ull;
+  }
+  return keep;
 }
 
 }  // namespace minf

@@ -14,8 +14,8 @@
 //    wave reads 64 consecutive blocks per dimension; the group's queries sit
 //    in LDS and are read by broadcast, so every pooled vector is read once per
 //    KV head;
-//  * top-k: one workgroup per head, scores as sortable keys in LDS, the shared
-//    block radix select;
+//  * top-k: one workgroup per head, scores as sortable keys in registers, the
+//    exact register top-k (bitwise search, ballot counts, no atomics);
 //  * attention: split over the selected blocks (flash-decoding style); a wave
 //    takes one 64-key block at a time, 16 lanes per key row with 16-byte
 //    loads, online softmax in fp32; the four waves of a workgroup merge their
@@ -63,18 +63,30 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(const DecodeL
   for (int t = 0; t < a.grp; ++t) a.scores[(size_t)(h0 + t) * a.nb + c] = acc[t];
 }
 
-// top-k_b blocks of one head (n_b <= kDecMaxBlocks), ascending
+static_assert(kDecMaxBlocks <= 1024 * 16, "the decode top-k holds at most 16 blocks per thread");
+
+// top-k_b blocks of one head (n_b <= kDecMaxBlocks), ascending: block
+// c = 1024 i + tid is key[i] of thread tid, for the exact register top-k
+template <int PER>
 __global__ __launch_bounds__(1024) void decode_topk_kernel(const DecodeLaunch a) {
-  __shared__ uint32_t keys[kDecMaxBlocks];
-  __shared__ int hist[2048];
-  __shared__ int scratch[64];
+  __shared__ uint64_t gmask[16 * PER];
+  __shared__ uint64_t emask[16 * PER];
+  __shared__ int red[32];
+  __shared__ int wsum[16];
   const int h = blockIdx.x;
+  const int tid = threadIdx.x;
   const float* s = a.scores + (size_t)h * a.nb;
-  for (int c = threadIdx.x; c < a.nb; c += 1024) keys[c] = sortable_key(s[c]);
-  __syncthreads();
+  float sv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sv[i] = s[1024 * i + tid < a.nb ? 1024 * i + tid : a.nb - 1];
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t u = sortable_key(sv[i]);
+    key[i] = 1024 * i + tid < a.nb ? (u > 0u ? u : 1u) : 0u;
+  }
   int32_t* out = a.blk + (size_t)h * a.kb;
-  radix_topk_ordered<1024>([&](int i) { return keys[i]; }, a.nb, a.kb, hist, scratch,
-                           [&](int pos, int i) { out[pos] = i; });
+  reg_topk_ordered<1024, PER>(key, a.nb, a.kb, gmask, emask, red, wsum, [&](int pos, int c) { out[pos] = c; });
 }
 
 // G query heads of one KV head per workgroup: G = 1 for sparse decoding (each
@@ -275,7 +287,12 @@ hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream)
   if (select) {
     hipLaunchKernelGGL(decode_score_kernel, dim3((a.nb + kDecThreads - 1) / kDecThreads, a.hkv),
                        dim3(kDecThreads), 0, stream, a);
-    hipLaunchKernelGGL(decode_topk_kernel, dim3(a.hq), dim3(1024), 0, stream, a);
+    if (a.nb <= 1024)
+      hipLaunchKernelGGL(decode_topk_kernel<1>, dim3(a.hq), dim3(1024), 0, stream, a);
+    else if (a.nb <= 4096)
+      hipLaunchKernelGGL(decode_topk_kernel<4>, dim3(a.hq), dim3(1024), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_topk_kernel<16>, dim3(a.hq), dim3(1024), 0, stream, a);
   }
   if (a.blk) {
     hipLaunchKernelGGL(decode_attn_kernel<1>, dim3(a.nsplit, a.hq), dim3(kDecThreads), 0, stream, a);
