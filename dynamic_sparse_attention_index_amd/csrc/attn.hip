@@ -85,20 +85,25 @@ struct BlockIter {
   int sb, wlo0, wlo1;  // A-shape
   int w, wmax, base;   // VS / BLOCK bitmap cursor
   uint32_t rem;
+  uint32_t mw0, mw1;   // membership of b0 / b1 for the bits of the current word
   // BLOCK: membership bitmaps over key blocks c of b0 and b1.
   // VS: block-offset bitmaps of b0 and b1 (they differ only for a partial last block).
   const uint32_t* bits0;
   const uint32_t* bits1;
 
-  __device__ uint32_t union_word(int ww) const {
+  // Reads word ww of both memberships from LDS (kept in registers until the
+  // cursor leaves the word) and returns their union.
+  __device__ uint32_t union_word(int ww) {
     if (kind == KIND_VS) {
-      uint32_t bw = bits0[ww];
-      uint32_t prev = ww > 0 ? bits0[ww - 1] : 0u;
-      uint32_t u = (bw << 1) | (prev >> 31);  // offsets v with v - 1 in b0's set
-      if (has_b1) u |= bits1[ww];             // offsets v in b1's set
-      return u;
+      const uint32_t bw = bits0[ww];
+      const uint32_t prev = ww > 0 ? bits0[ww - 1] : 0u;
+      mw0 = (bw << 1) | (prev >> 31);      // offsets v with v - 1 in b0's set
+      mw1 = has_b1 ? bits1[ww] : 0u;       // offsets v in b1's set
+    } else {
+      mw0 = bits0[ww];
+      mw1 = bits1[ww];
     }
-    return bits0[ww] | bits1[ww];
+    return mw0 | mw1;
   }
 
   // Bitmap cursor over offsets/blocks [0, vmax]. VS walks its offsets
@@ -145,9 +150,7 @@ struct BlockIter {
       rem ^= 1u << bit;
       const int v = (w << 5) + bit;
       cout = base - v;
-      const int m1 = has_b1 && bit_at(bits1, v);
-      const int m0 = v >= 1 && bit_at(bits0, v - 1);
-      mem = m0 | (m1 << 1);
+      mem = (int)((mw0 >> bit) & 1u) | ((int)((mw1 >> bit) & 1u) << 1);
       return true;
     }
     // bitmap kinds: iterate set bits of the union word by word
@@ -160,10 +163,10 @@ struct BlockIter {
       }
       rem = u;
     }
-    const int v = (w << 5) + __builtin_ctz(rem);
+    const int bit = __builtin_ctz(rem);
     rem &= rem - 1u;
-    cout = v;
-    mem = (int)bit_at(bits0, v) | ((int)bit_at(bits1, v) << 1);
+    cout = (w << 5) + bit;
+    mem = (int)((mw0 >> bit) & 1u) | ((int)((mw1 >> bit) & 1u) << 1);
     return true;
   }
 };
