@@ -77,6 +77,10 @@ enum : int { KIND_DENSE = 0, KIND_ASHAPE = 1, KIND_VS = 2, KIND_BLOCK = 3 };
 
 __device__ __forceinline__ uint32_t bit_at(const uint32_t* w, int v) { return (w[v >> 5] >> (v & 31)) & 1u; }
 
+// A value that is the same in every lane of the wave, as a scalar.
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // Tile sequence over the key blocks of the pair (b0, b1). Every thread runs
 // the same sequence (it only reads kernel arguments and LDS).
 struct BlockIter {
@@ -92,16 +96,18 @@ struct BlockIter {
   const uint32_t* bits1;
 
   // Reads word ww of both memberships from LDS (kept in registers until the
-  // cursor leaves the word) and returns their union.
+  // cursor leaves the word) and returns their union. The words are the same
+  // in every lane; taking them as wave-uniform keeps the tile index and the
+  // copy addresses derived from it in scalar registers.
   __device__ uint32_t union_word(int ww) {
     if (kind == KIND_VS) {
-      const uint32_t bw = bits0[ww];
-      const uint32_t prev = ww > 0 ? bits0[ww - 1] : 0u;
-      mw0 = (bw << 1) | (prev >> 31);      // offsets v with v - 1 in b0's set
-      mw1 = has_b1 ? bits1[ww] : 0u;       // offsets v in b1's set
+      const uint32_t bw = uniform_u32(bits0[ww]);
+      const uint32_t prev = ww > 0 ? uniform_u32(bits0[ww - 1]) : 0u;
+      mw0 = (bw << 1) | (prev >> 31);                  // offsets v with v - 1 in b0's set
+      mw1 = has_b1 ? uniform_u32(bits1[ww]) : 0u;     // offsets v in b1's set
     } else {
-      mw0 = bits0[ww];
-      mw1 = bits1[ww];
+      mw0 = uniform_u32(bits0[ww]);
+      mw1 = uniform_u32(bits1[ww]);
     }
     return mw0 | mw1;
   }
@@ -183,7 +189,7 @@ __device__ __forceinline__ uint32_t tile_chunk_byte() {
 // uniform base pointers and per-lane 32-bit offsets.
 __device__ __forceinline__ void issue_contig(const char* kbase, const char* vbase, uint16_t* kt, uint16_t* vt,
                                              uint32_t lane_off) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_index();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t off = lane_off + (uint32_t)i * 16 * 256;
