@@ -602,6 +602,10 @@ struct DecWs {
   float* scores;
   int32_t* blk;
   float* part;
+  uint32_t* seg_key;
+  int32_t* seg_id;
+  int32_t* seg_cnt;
+  int nseg;
   size_t bytes;
 };
 
@@ -620,6 +624,12 @@ DecWs carve_decode(void* base, int64_t n, int hq, int kb, bool select) {
   if (select) {
     w.scores = c.take<float>((size_t)hq * nb);
     w.blk = c.take<int32_t>((size_t)hq * kb);
+    w.nseg = decode_topk_segments((int)nb, kb);
+    if (w.nseg > 1) {
+      w.seg_key = c.take<uint32_t>((size_t)hq * w.nseg * kb);
+      w.seg_id = c.take<int32_t>((size_t)hq * w.nseg * kb);
+      w.seg_cnt = c.take<int32_t>((size_t)hq * w.nseg);
+    }
   }
   w.part = c.take<float>((size_t)hq * nsplit * (kHeadDim + 2));
   w.bytes = c.off;
@@ -647,6 +657,10 @@ minf_status run_decode(const void* q, const void* k, const void* v, const float*
   a.scores = w.scores;
   a.blk = select ? (blk_idx ? blk_idx : w.blk) : nullptr;
   a.part = w.part;
+  a.seg_key = w.seg_key;
+  a.seg_id = w.seg_id;
+  a.seg_cnt = w.seg_cnt;
+  a.nseg = w.nseg;
   a.o = (uint16_t*)o;
   a.lse = lse;
   a.n = (int)n;

@@ -10,12 +10,15 @@
 // and attends exactly over their keys. k_b >= n_b is dense decoding.
 //
 // Layout of the work (memory bound: the point is to load few K/V rows):
-//  * scores: one thread per block, the pooled keys stored [d][n_b] so that a
+//  * scores: 64 blocks per workgroup, one lane per block and one wave per
+//    quarter of the dimensions, the pooled keys stored [d][n_b] so that a
 //    wave reads 64 consecutive blocks per dimension; the group's queries sit
 //    in LDS and are read by broadcast, so every pooled vector is read once per
 //    KV head;
-//  * top-k: one workgroup per head, scores as sortable keys in registers, the
-//    exact register top-k (bitwise search, ballot counts, no atomics);
+//  * top-k: the exact register top-k (bitwise search, ballot counts); for
+//    k_b <= 256 over more than 2048 blocks, 2048-block segments are selected
+//    by separate workgroups and a second kernel merges each head's segment
+//    winners, else one 1024-thread workgroup per head;
 //  * attention: split over the selected blocks (flash-decoding style); a wave
 //    takes one 64-key block at a time, 16 lanes per key row with 16-byte
 //    loads, online softmax in fp32; the four waves of a workgroup merge their
@@ -38,9 +41,14 @@ __device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float c) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// scores[h][c] = sum_d q_h[d] * kbar_t[g][d][c], d ascending, for the heads of KV head g
+// scores[h][c] = sum_d q_h[d] * kbar_t[g][d][c] for the heads of KV head g.
+// A workgroup takes 64 blocks; wave w sums d = 32 w .. 32 w + 31 in ascending
+// order and the four partials are added in wave order (a fixed order, so the
+// scores are reproducible), which gives four times the loads in flight of one
+// thread walking all 128 dimensions.
 __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(const DecodeLaunch a) {
   __shared__ float qs[kHeadDim][kDecMaxGroup];
+  __shared__ float part[3][kDecMaxGroup][64];
   const int g = blockIdx.y;
   const int h0 = g * a.grp;
   for (int x = threadIdx.x; x < kHeadDim * kDecMaxGroup; x += kDecThreads) {
@@ -48,19 +56,29 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(const DecodeL
     qs[d][t] = t < a.grp ? __builtin_bit_cast(float, (uint32_t)a.q[(size_t)(h0 + t) * kHeadDim + d] << 16) : 0.f;
   }
   __syncthreads();
-  const int c = blockIdx.x * kDecThreads + threadIdx.x;
-  if (c >= a.nb) return;
-  const float* kt = a.kbar_t + (size_t)g * kHeadDim * a.nb + c;
+  const int lane = threadIdx.x & 63;
+  const int wq = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
   float acc[kDecMaxGroup];
 #pragma unroll
   for (int t = 0; t < kDecMaxGroup; ++t) acc[t] = 0.f;
-#pragma unroll 16
-  for (int d = 0; d < kHeadDim; ++d) {
-    const float kv = kt[(size_t)d * a.nb];
+  if (c < a.nb) {
+    const float* kt = a.kbar_t + ((size_t)g * kHeadDim + 32 * wq) * a.nb + c;
+#pragma unroll 8
+    for (int d = 0; d < 32; ++d) {
+      const float kv = kt[(size_t)d * a.nb];
 #pragma unroll
-    for (int t = 0; t < kDecMaxGroup; ++t) acc[t] = fmaf(qs[d][t], kv, acc[t]);
+      for (int t = 0; t < kDecMaxGroup; ++t) acc[t] = fmaf(qs[32 * wq + d][t], kv, acc[t]);
+    }
   }
-  for (int t = 0; t < a.grp; ++t) a.scores[(size_t)(h0 + t) * a.nb + c] = acc[t];
+  if (wq > 0) {
+#pragma unroll
+    for (int t = 0; t < kDecMaxGroup; ++t) part[wq - 1][t][lane] = acc[t];
+  }
+  __syncthreads();
+  if (wq == 0 && c < a.nb)
+    for (int t = 0; t < a.grp; ++t)
+      a.scores[(size_t)(h0 + t) * a.nb + c] = ((acc[t] + part[0][t][lane]) + part[1][t][lane]) + part[2][t][lane];
 }
 
 static_assert(kDecMaxBlocks <= 1024 * 16, "the decode top-k holds at most 16 blocks per thread");
@@ -87,6 +105,72 @@ __global__ __launch_bounds__(1024) void decode_topk_kernel(const DecodeLaunch a)
   }
   int32_t* out = a.blk + (size_t)h * a.kb;
   reg_topk_ordered<1024, PER>(key, a.nb, a.kb, gmask, emask, red, wsum, [&](int pos, int c) { out[pos] = c; });
+}
+
+// Segmented top-k_b of one head (k_b <= kDecSegMaxK), step 1: workgroup
+// (seg, h) selects the top-k_b of blocks [2048 seg, 2048 seg + 2048) with the
+// register top-k and stores their keys and ids (ascending ids).
+__global__ __launch_bounds__(256) void decode_topk_seg_kernel(const DecodeLaunch a) {
+  constexpr int PER = kDecSeg / 256;
+  __shared__ uint64_t gmask[4 * PER];
+  __shared__ uint64_t emask[4 * PER];
+  __shared__ int red[8];
+  __shared__ int wsum[4];
+  const int seg = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int c0 = seg * kDecSeg;
+  const int ns = a.nb - c0 < kDecSeg ? a.nb - c0 : kDecSeg;
+  const float* s = a.scores + (size_t)h * a.nb + c0;
+  float sv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) sv[i] = s[256 * i + tid < ns ? 256 * i + tid : ns - 1];
+  uint32_t key[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const uint32_t u = sortable_key(sv[i]);
+    key[i] = 256 * i + tid < ns ? (u > 0u ? u : 1u) : 0u;
+  }
+  const size_t so = ((size_t)h * a.nseg + seg) * a.kb;
+  uint32_t* sk = a.seg_key + so;
+  int32_t* si = a.seg_id + so;
+  const int keep = reg_topk_ordered<256, PER>(key, ns, a.kb, gmask, emask, red, wsum, [&](int pos, int c) {
+    const uint32_t u = sortable_key(s[c]);
+    sk[pos] = u > 0u ? u : 1u;
+    si[pos] = c0 + c;
+  });
+  if (tid == 0) a.seg_cnt[(size_t)h * a.nseg + seg] = keep;
+}
+
+// Step 2, one workgroup per head: the global top-k_b is contained in the union
+// of the segments' top-k_b under the same order (key descending, lower id
+// first). Candidate x = seg * k_b + slot lists the segments in id order, so the
+// lowest candidate index is the lowest id among equal keys.
+template <int PER2>
+__global__ __launch_bounds__(256) void decode_topk_merge_kernel(const DecodeLaunch a) {
+  __shared__ uint64_t gmask[4 * PER2];
+  __shared__ uint64_t emask[4 * PER2];
+  __shared__ int red[8];
+  __shared__ int wsum[4];
+  const int h = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ncand = a.nseg * a.kb;
+  const uint32_t* hk = a.seg_key + (size_t)h * a.nseg * a.kb;
+  const int32_t* hid = a.seg_id + (size_t)h * a.nseg * a.kb;
+  const int32_t* hcnt = a.seg_cnt + (size_t)h * a.nseg;
+  uint32_t key2[PER2];
+#pragma unroll
+  for (int i = 0; i < PER2; ++i) {
+    const int x = 256 * i + tid;
+    key2[i] = 0u;
+    if (x < ncand) {
+      const int sg = x / a.kb;
+      if (x - sg * a.kb < hcnt[sg]) key2[i] = hk[x];
+    }
+  }
+  int32_t* out = a.blk + (size_t)h * a.kb;
+  reg_topk_ordered<256, PER2>(key2, ncand, a.kb, gmask, emask, red, wsum,
+                              [&](int pos, int x) { out[pos] = hid[x]; });
 }
 
 // G query heads of one KV head per workgroup: G = 1 for sparse decoding (each
@@ -285,9 +369,20 @@ int decode_blocks_per_split(int kb, int rows) {
 hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream) {
   if (a.grp > kDecMaxGroup || a.nb > kDecMaxBlocks) return hipErrorInvalidValue;
   if (select) {
-    hipLaunchKernelGGL(decode_score_kernel, dim3((a.nb + kDecThreads - 1) / kDecThreads, a.hkv),
+    hipLaunchKernelGGL(decode_score_kernel, dim3((a.nb + 63) / 64, a.hkv),
                        dim3(kDecThreads), 0, stream, a);
-    if (a.nb <= 1024)
+    if (a.seg_key && a.nseg > 1) {
+      hipLaunchKernelGGL(decode_topk_seg_kernel, dim3(a.nseg, a.hq), dim3(256), 0, stream, a);
+      const int per2 = (a.nseg * a.kb + 255) / 256;
+      if (per2 <= 1)
+        hipLaunchKernelGGL(decode_topk_merge_kernel<1>, dim3(a.hq), dim3(256), 0, stream, a);
+      else if (per2 <= 2)
+        hipLaunchKernelGGL(decode_topk_merge_kernel<2>, dim3(a.hq), dim3(256), 0, stream, a);
+      else if (per2 <= 4)
+        hipLaunchKernelGGL(decode_topk_merge_kernel<4>, dim3(a.hq), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL(decode_topk_merge_kernel<8>, dim3(a.hq), dim3(256), 0, stream, a);
+    } else if (a.nb <= 1024)
       hipLaunchKernelGGL(decode_topk_kernel<1>, dim3(a.hq), dim3(1024), 0, stream, a);
     else if (a.nb <= 4096)
       hipLaunchKernelGGL(decode_topk_kernel<4>, dim3(a.hq), dim3(1024), 0, stream, a);

@@ -104,9 +104,20 @@ struct DecodeLaunch {
   float* part;           // [hq][nsplit][130]: max (log2 units), sum, o[128]
   uint16_t* o;           // [hq][128]
   float* lse;            // [hq] or null
-  int32_t n, nb, hq, hkv, grp, kb, nsplit, bps;
+  // segmented top-k (null when a single workgroup per head selects): per head
+  // and segment the segment's top-kb keys and block ids, and their count
+  uint32_t* seg_key;     // [hq][nseg][kb]
+  int32_t* seg_id;       // [hq][nseg][kb]
+  int32_t* seg_cnt;      // [hq][nseg]
+  int32_t n, nb, hq, hkv, grp, kb, nsplit, bps, nseg;
   float scale_log2;
 };
+constexpr int kDecSeg = 2048;      // candidate blocks per top-k segment
+constexpr int kDecSegMaxK = 256;   // largest k_b served by the segmented top-k
+// Segments of the segmented decode top-k for n_b blocks and k_b (0: one workgroup per head).
+inline int decode_topk_segments(int nb, int kb) {
+  return (nb > kDecSeg && kb <= kDecSegMaxK) ? (nb + kDecSeg - 1) / kDecSeg : 0;
+}
 int decode_blocks_per_split(int kb, int rows);
 hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream);
