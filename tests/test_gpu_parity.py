@@ -238,10 +238,11 @@ def test_mixed_heads_gqa_and_determinism(gpu_lib):
     assert torch.equal(vi, vi2) and torch.equal(si, si2) and torch.equal(bi, bi2) and torch.equal(bc, bc2)
 
 
-def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch):
-    # 2^19 tokens, scattered slash offsets: long work items, so the XCD-round
-    # launch takes the work; MINF_ATTN_ROUNDS=0 forces the ordinary launch
-    n, hq = 1 << 19, 4
+@pytest.mark.parametrize("n", [1 << 19, (1 << 19) + 37])
+def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch, n):
+    # 2^19 tokens (and a ragged length), scattered slash offsets: long work items,
+    # so the XCD-round launch takes the work; MINF_ATTN_ROUNDS=0 forces the ordinary launch
+    hq = 4
     q, k, v, _ = _qkv(n, hq, 1, 25)
     g = torch.Generator().manual_seed(26)
     plans = []
@@ -256,7 +257,7 @@ def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     # sampled rows of one head against the oracle: the first block, a middle one and the last
-    rows = np.concatenate([np.arange(0, 64), np.arange(n // 2, n // 2 + 64), np.arange(n - 64, n)])
+    rows = np.concatenate([np.arange(0, 64), np.arange(n // 2, n // 2 + 64), np.arange(64 * ((n - 1) // 64) - 64, n)])
     h = 2
     qh = np.zeros((1, n, 128), np.float32)
     qh[0, rows] = to_np(q[h][torch.as_tensor(rows, device="cuda")])
