@@ -167,18 +167,30 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
   }
 }
 
+constexpr int kTopkCap = 1024;  // compacted candidates of the pre-filtered top-k
+
 // Top-k_b key blocks of every query block of the round, from the stored scores.
 // Causal: the candidates are c <= b. Permuted: every c whose earliest original
 // position is not after the query block's latest one. One workgroup per row;
 // candidate c = 256 i + tid is held as sortable key k[i] in registers (0 for
 // an ineligible block) for the exact register top-k (ties to the lower id).
+// Long rows (PER >= 16, k_b <= 256) are first narrowed: each wave takes the
+// ceil(k_b / 4)-th largest of its 64 threads' maxima (a wave-only bitwise
+// search), and the smallest of the four, t0, has at least k_b keys >= it
+// (each wave has ceil(k_b / 4) threads whose maximum is >= t0). The keys >= t0
+// (typically ~2 k_b) are compacted into LDS in block order and the register
+// top-k runs over them; when they exceed kTopkCap the whole row is searched.
 template <int PER>
 __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   __shared__ uint64_t gmask[4 * PER];
   __shared__ uint64_t emask[4 * PER];
   __shared__ int red[8];
   __shared__ int wsum[4];
+  __shared__ uint32_t ckey[PER >= 16 ? kTopkCap : 1];
+  __shared__ int32_t cid[PER >= 16 ? kTopkCap : 1];
+  __shared__ int coff[PER >= 16 ? 4 * PER : 1];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int r_end = a.r0 + a.rows < a.nb ? a.r0 + a.rows : a.nb;
   const int b = r_end - 1 - (int)blockIdx.x;  // longest rows first
   const int hs = blockIdx.y;
@@ -210,8 +222,60 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
     key[i] = e ? (u > 0u ? u : 1u) : 0u;  // an eligible key is never 0, even for a NaN score
   }
   int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
-  const int keep = reg_topk_ordered<256, PER>(key, ncand, kb, gmask, emask, red, wsum,
-                                              [&](int pos, int c) { out[pos] = c; });
+  int keep = -1;
+  if constexpr (PER >= 16) {
+    if (kb <= 256 && ncand > kTopkCap) {
+      // t0: the smallest of the waves' ceil(kb / 4)-th largest thread maxima
+      uint32_t tm = 0u;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) tm = key[i] > tm ? key[i] : tm;
+      const int kq = (kb + 3) >> 2;
+      uint32_t tw = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = tw | (1u << bit);
+        if ((int)__popcll(__ballot(tm >= cand)) >= kq) tw = cand;
+      }
+      if (lane == 0) red[wave] = (int)tw;
+      __syncthreads();
+      uint32_t t0 = (uint32_t)red[0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) t0 = (uint32_t)red[w] < t0 ? (uint32_t)red[w] : t0;
+      if (t0 == 0u) t0 = 1u;  // never ineligible blocks
+      // per (i, wave) counts of keys >= t0, then their offsets in block order
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int cnt = (int)__popcll(__ballot(key[i] >= t0));
+        if (lane == 0) coff[4 * i + wave] = cnt;
+      }
+      __syncthreads();
+      int tot;
+      const int myoff = block_excl_scan_int<256>(tid < 4 * PER ? coff[tid] : 0, wsum, tot);
+      if (tot <= kTopkCap) {
+        if (tid < 4 * PER) coff[tid] = myoff;
+        __syncthreads();
+        const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const uint64_t bal = __ballot(key[i] >= t0);
+          if (key[i] >= t0) {
+            const int pos = coff[4 * i + wave] + (int)__popcll(bal & lt);
+            ckey[pos] = key[i];
+            cid[pos] = 256 * i + tid;
+          }
+        }
+        __syncthreads();
+        uint32_t k2[kTopkCap / 256];
+#pragma unroll
+        for (int j = 0; j < kTopkCap / 256; ++j) k2[j] = 256 * j + tid < tot ? ckey[256 * j + tid] : 0u;
+        keep = reg_topk_ordered<256, kTopkCap / 256>(k2, tot, kb, gmask, emask, red, wsum,
+                                                     [&](int pos, int x) { out[pos] = cid[x]; });
+      }
+      __syncthreads();  // red / wsum / coff are reused below
+    }
+  }
+  if (keep < 0)
+    keep = reg_topk_ordered<256, PER>(key, ncand, kb, gmask, emask, red, wsum,
+                                      [&](int pos, int c) { out[pos] = c; });
   for (int e = keep + tid; e < kb; e += 256) out[e] = -1;
   if (tid == 0) a.blk_cnt[(size_t)slot * a.nb + b] = keep;
 }
