@@ -832,20 +832,23 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
 
 // Rounds pay off when the work items are long: flag = 1 when the listed VS
 // heads' offset sets O u (O + 1) hold on average at least `min_tiles` block
-// offsets (the tile count of the longest query-block pairs).
-__global__ __launch_bounds__(256) void rounds_flag_kernel(const OffBitsLaunch a, int count, int min_tiles,
-                                                          int32_t* flag) {
+// offsets (the tile count of the longest query-block pairs). One workgroup of
+// 1024 threads walks every head's bitmap words as one flat index space.
+__global__ __launch_bounds__(1024) void rounds_flag_kernel(const OffBitsLaunch a, int count, int min_tiles,
+                                                           int32_t* flag) {
   __shared__ unsigned long long tot;
   if (threadIdx.x == 0) tot = 0;
   __syncthreads();
   const int nwords = (a.nb >> 5) + 1;
+  const int total = count * nwords;
   unsigned long long mine = 0;
-  for (int h = 0; h < count; ++h) {
+#pragma unroll 4
+  for (int x = threadIdx.x; x < total; x += 1024) {
+    const int h = x / nwords;
+    const int i = x - h * nwords;
     const uint32_t* w = a.bits[h];
-    for (int i = threadIdx.x; i < nwords; i += 256) {
-      const uint32_t prev = i > 0 ? w[i - 1] : 0u;
-      mine += (unsigned long long)__popc(w[i] | (w[i] << 1) | (prev >> 31));
-    }
+    const uint32_t prev = i > 0 ? w[i - 1] : 0u;
+    mine += (unsigned long long)__popc(w[i] | (w[i] << 1) | (prev >> 31));
   }
   atomicAdd(&tot, mine);
   __syncthreads();
@@ -859,7 +862,7 @@ hipError_t launch_rounds_flag(uint32_t* const* bits, int count, int n, int min_t
   for (int i = 0; i < c; ++i) a.bits[i] = bits[i];
   a.n = n;
   a.nb = (n + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(rounds_flag_kernel, dim3(1), dim3(256), 0, stream, a, c, min_tiles, flag);
+  hipLaunchKernelGGL(rounds_flag_kernel, dim3(1), dim3(1024), 0, stream, a, c, min_tiles, flag);
   return hipGetLastError();
 }
 
