@@ -382,7 +382,7 @@ size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
 // lets exactly one of them work: rounds when the items are long (thousands of
 // key tiles), because workgroups that stay at the same key position keep
 // sharing K/V tiles through L2 (at 1M tokens on literal data this cuts the
-// attention's HBM reads from ~35 TB to ~2 TB); the ordinary launch when they
+// attention's HBM reads from ~34 TB to ~3 TB); the ordinary launch when they
 // are short, because its hardware dispatch balances the load better.
 // MINF_ATTN_ROUNDS=0 in the environment (read on every call) keeps the
 // ordinary launch only; both give bitwise-identical results.
