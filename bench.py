@@ -602,8 +602,33 @@ def main():
             torch.cuda.synchronize()
             return a.elapsed_time(b) / reps
 
-        sparse_us = 1e3 * timed(lambda: minf.minf_sparse_decode(qd, k, v, kt, k_b, scale=scale, out=od, lse=ld,
-                                                                blk_idx=blk, workspace=ws_s))
+        def sparse_step():
+            minf.minf_sparse_decode(qd, k, v, kt, k_b, scale=scale, out=od, lse=ld, blk_idx=blk, workspace=ws_s)
+
+        sparse_us = 1e3 * timed(sparse_step)
+        # the same step captured once into a HIP graph and replayed (one launch per step)
+        sparse_step()
+        torch.cuda.synchronize()
+        ref = (od.clone(), ld.clone(), blk.clone())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sparse_step()
+        torch.cuda.synchronize()
+        graph_us = 1e3 * timed(graph.replay)
+        graph_ok = torch.equal(od, ref[0]) and torch.equal(ld, ref[1]) and torch.equal(blk, ref[2])
+
+        def latency_us(fn, reps=50):
+            # one step at a time, each waited for: what a token-by-token decoder sees
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+                torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / reps * 1e6
+
+        lat_eager_us = latency_us(sparse_step)
+        lat_graph_us = latency_us(graph.replay)
         dense_us = 1e3 * timed(lambda: minf.minf_dense_decode(qd, k, v, scale=scale, out=od, lse=ld, workspace=ws_d))
         pool_us = 1e3 * timed(lambda: minf.minf_decode_pool_keys(k, first_block=nb_ - 1, out=kt))
         row = 128 * 2 * 2  # one key row of K and V, bf16
@@ -612,7 +637,9 @@ def main():
         sparse_bytes = sel_rows * row + hkv * nb_ * 128 * 4 + hq * nb_ * 4 * 2
         extra["decode"] = {
             "k_b": k_b, "tokens_loaded_per_head": sel_rows // hq,
-            "sparse_us": round(sparse_us, 2), "dense_us": round(dense_us, 2),
+            "sparse_us": round(sparse_us, 2), "sparse_graph_us": round(graph_us, 2),
+            "step_latency_us": {"eager": round(lat_eager_us, 1), "graph": round(lat_graph_us, 1)},
+            "graph_replay_matches_eager": graph_ok, "dense_us": round(dense_us, 2),
             "speedup": round(dense_us / sparse_us, 2),
             "dense_hbm_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
             "sparse_algorithmic_bytes": sparse_bytes,
@@ -621,10 +648,12 @@ def main():
             "note": "one new query row per head against the cache; top-k_b 64-token blocks by the pooled-key score; "
                     "dense loads every K/V row of every KV head",
         }
-        print(f"[bench] decode: sparse {sparse_us:.1f} us (k_b={k_b}), dense {dense_us:.1f} us "
+        print(f"[bench] decode: sparse {sparse_us:.1f} us (k_b={k_b}; {graph_us:.1f} us replayed from a graph; "
+              f"one step waited for: {lat_eager_us:.1f} us eager, {lat_graph_us:.1f} us graph), "
+              f"dense {dense_us:.1f} us "
               f"({extra['decode']['dense_hbm_gbs']} GB/s), speedup {extra['decode']['speedup']}x",
               file=sys.stderr, flush=True)
-        del kt, ws_s, ws_d
+        del kt, ws_s, ws_d, graph
 
     # offline pattern search on this input (optional: it re-runs attention once per candidate)
     if args.search:

@@ -126,6 +126,11 @@ def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
+def _need_out(t, shape, name):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected a contiguous int32 device tensor of shape {tuple(shape)}")
+
+
 def _workspace(nbytes, device, workspace):
     if nbytes == 0:
         return None, 0
@@ -134,16 +139,25 @@ def _workspace(nbytes, device, workspace):
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
-def minf_build_vs_index(q, k, heads, last_q=64, k_v=1000, k_s=6096, scale=None, workspace=None, stream=None):
-    """VS index for query heads `heads`: (v_idx [n_heads, min(k_v, n)], s_idx [n_heads, min(k_s, n)])."""
+def minf_build_vs_index(q, k, heads, last_q=64, k_v=1000, k_s=6096, scale=None, workspace=None, stream=None,
+                        out=None):
+    """VS index for query heads `heads`: (v_idx [n_heads, min(k_v, n)], s_idx [n_heads, min(k_s, n)]).
+
+    out: optional preallocated (v_idx, s_idx) of those shapes, contiguous int32.
+    """
     _need(q, torch.bfloat16, "q")
     _need(k, torch.bfloat16, "k")
     hq, n, d = q.shape
     hkv = k.shape[0]
     arr, nh = _heads_arr(heads)
     kv_eff, ks_eff = min(k_v, n), min(k_s, n)
-    v_idx = torch.empty((nh, kv_eff), dtype=torch.int32, device=q.device)
-    s_idx = torch.empty((nh, ks_eff), dtype=torch.int32, device=q.device)
+    if out is None:
+        v_idx = torch.empty((nh, kv_eff), dtype=torch.int32, device=q.device)
+        s_idx = torch.empty((nh, ks_eff), dtype=torch.int32, device=q.device)
+    else:
+        v_idx, s_idx = out
+        _need_out(v_idx, (nh, kv_eff), "v_idx")
+        _need_out(s_idx, (nh, ks_eff), "s_idx")
     ws, wsb = _workspace(_lib.minf_vs_index_workspace_size(n, nh), q.device, workspace)
     _check(_lib.minf_build_vs_index(_ptr(q), _ptr(k), n, hq, hkv, d, arr, nh, last_q, k_v, k_s, _scale(scale, d),
                                     _ptr(v_idx), _ptr(s_idx), _ptr(ws), wsb, _stream(stream)))
@@ -165,26 +179,35 @@ def minf_vs_scores(q, k, heads, last_q=64, scale=None, workspace=None, stream=No
     return v, sl
 
 
-def minf_build_block_index(q, k, heads, k_b=256, workspace=None, stream=None):
-    """Block index: (blk_idx [n_heads, n_b, k_b] padded with -1, blk_cnt [n_heads, n_b])."""
+def minf_build_block_index(q, k, heads, k_b=256, workspace=None, stream=None, out=None):
+    """Block index: (blk_idx [n_heads, n_b, k_b] padded with -1, blk_cnt [n_heads, n_b]).
+
+    out: optional preallocated (blk_idx, blk_cnt) of those shapes, contiguous int32.
+    """
     _need(q, torch.bfloat16, "q")
     _need(k, torch.bfloat16, "k")
     hq, n, d = q.shape
     hkv = k.shape[0]
     arr, nh = _heads_arr(heads)
     nb = (n + 63) // 64
-    blk_idx = torch.empty((nh, nb, k_b), dtype=torch.int32, device=q.device)
-    blk_cnt = torch.empty((nh, nb), dtype=torch.int32, device=q.device)
+    if out is None:
+        blk_idx = torch.empty((nh, nb, k_b), dtype=torch.int32, device=q.device)
+        blk_cnt = torch.empty((nh, nb), dtype=torch.int32, device=q.device)
+    else:
+        blk_idx, blk_cnt = out
+        _need_out(blk_idx, (nh, nb, k_b), "blk_idx")
+        _need_out(blk_cnt, (nh, nb), "blk_cnt")
     ws, wsb = _workspace(_lib.minf_block_index_workspace_size(n, hq, hkv, nh), q.device, workspace)
     _check(_lib.minf_build_block_index(_ptr(q), _ptr(k), n, hq, hkv, d, arr, nh, k_b, _ptr(blk_idx), _ptr(blk_cnt),
                                        _ptr(ws), wsb, _stream(stream)))
     return blk_idx, blk_cnt
 
 
-def minf_build_permuted_block_index(q, k, heads, pos, k_b=256, workspace=None, stream=None):
+def minf_build_permuted_block_index(q, k, heads, pos, k_b=256, workspace=None, stream=None, out=None):
     """Block index of a permuted sequence (q, k in permuted order, pos[t] = original position of row t).
 
-    Returns (blk_idx [n_heads, n_b, k_b] int32, blk_cnt [n_heads, n_b] int32).
+    Returns (blk_idx [n_heads, n_b, k_b] int32, blk_cnt [n_heads, n_b] int32); out: optional
+    preallocated pair of those shapes.
     """
     _need(q, torch.bfloat16, "q")
     _need(k, torch.bfloat16, "k")
@@ -193,8 +216,13 @@ def minf_build_permuted_block_index(q, k, heads, pos, k_b=256, workspace=None, s
     hkv = k.shape[0]
     arr, nh = _heads_arr(heads)
     nb = (n + 63) // 64
-    bi = torch.empty((nh, nb, k_b), dtype=torch.int32, device=q.device)
-    bc = torch.empty((nh, nb), dtype=torch.int32, device=q.device)
+    if out is None:
+        bi = torch.empty((nh, nb, k_b), dtype=torch.int32, device=q.device)
+        bc = torch.empty((nh, nb), dtype=torch.int32, device=q.device)
+    else:
+        bi, bc = out
+        _need_out(bi, (nh, nb, k_b), "blk_idx")
+        _need_out(bc, (nh, nb), "blk_cnt")
     ws, wsb = _workspace(_lib.minf_block_index_workspace_size(n, hq, hkv, nh), q.device, workspace)
     _check(_lib.minf_build_permuted_block_index(_ptr(q), _ptr(k), n, hq, hkv, d, arr, nh, int(k_b), _ptr(pos),
                                                 _ptr(bi), _ptr(bc), _ptr(ws), wsb, _stream(stream)))
