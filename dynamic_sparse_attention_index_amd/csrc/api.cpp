@@ -221,7 +221,7 @@ const char* minf_status_string(minf_status s) {
 
 const char* minf_last_error_detail(void) { return g_detail.c_str(); }
 
-int minf_abi_version(void) { return 2; }
+int minf_abi_version(void) { return 3; }
 
 size_t minf_vs_index_workspace_size(int64_t n, int n_heads) {
   if (n < 1 || n_heads < 0) return 0;
@@ -367,12 +367,20 @@ minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const 
   return MINF_OK;
 }
 
+// Per-head window area of VS window heads: the offset bitmap over [0, n), the
+// tile cover, its tile count.
+static size_t vsw_head_bytes(int64_t n) {
+  return align_up((size_t)((n + 31) / 32) * sizeof(uint32_t)) +
+         align_up((size_t)vsw_tile_capacity((int)n) * sizeof(int2)) + kAlign;
+}
+
 size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
   if (n < 1 || hq < 1) return 0;
   // per head: the VS offset bitmaps, then the min / max original position of
-  // every key block for Block-Sparse heads on a permuted sequence
+  // every key block for Block-Sparse heads on a permuted sequence; per-XCD
+  // counters and a flag; then the window areas of VS window heads
   return align_up((size_t)hq * 2 * bitmap_words(n) * sizeof(uint32_t)) +
-         align_up((size_t)hq * 2 * nblocks(n) * sizeof(int32_t)) + kAlign;  // + per-XCD counters and a flag
+         align_up((size_t)hq * 2 * nblocks(n) * sizeof(int32_t)) + kAlign + (size_t)hq * vsw_head_bytes(n);
 }
 
 // Launches with Vertical-Slash heads at long lengths queue two launches of
@@ -447,7 +455,7 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
   minf_status s;
   if ((s = check_attn_common(q, k, v, o, n, hq, hkv, d, scale, kMaxTokens)) != MINF_OK) return s;
   if (!plans) return fail(MINF_E_INVALID_ARG, "plans must be a host array of hq entries");
-  bool any_vs = false, any_pos = false;
+  bool any_vs = false, any_pos = false, any_vsw = false;
   for (int h = 0; h < hq; ++h) {
     const minf_head_plan& p = plans[h];
     if (p.pos && p.kind != MINF_KIND_BLOCK)
@@ -459,10 +467,11 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
         if (p.sink < 0 || p.local < 0) return fail(MINF_E_INVALID_ARG, "head %d: sink and local must be >= 0", h);
         break;
       case MINF_KIND_VS:
+      case MINF_KIND_VS_WINDOW:
         if (p.k_v < 0 || p.k_s < 0) return fail(MINF_E_INVALID_ARG, "head %d: k_v and k_s must be >= 0", h);
         if ((p.k_v > 0 && !p.v_idx) || (p.k_s > 0 && !p.s_idx))
           return fail(MINF_E_INVALID_ARG, "head %d: v_idx / s_idx null with a positive count", h);
-        any_vs = true;
+        (p.kind == MINF_KIND_VS ? any_vs : any_vsw) = true;
         break;
       case MINF_KIND_BLOCK:
         if (p.k_b < 1) return fail(MINF_E_INVALID_ARG, "head %d: k_b must be >= 1", h);
@@ -471,7 +480,8 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
       default: return fail(MINF_E_INVALID_ARG, "head %d: unknown plan kind %d", h, p.kind);
     }
   }
-  if ((any_vs || any_pos) && (s = check_ws(workspace, ws_bytes, minf_sparse_attn_workspace_size(n, hq))) != MINF_OK)
+  if ((any_vs || any_pos || any_vsw) &&
+      (s = check_ws(workspace, ws_bytes, minf_sparse_attn_workspace_size(n, hq))) != MINF_OK)
     return s;
 
   AttnLaunch a{};
@@ -505,6 +515,35 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
   const size_t nbk = (size_t)nblocks(n);
   int32_t* pos_ws = (int32_t*)((char*)workspace + align_up((size_t)hq * words * sizeof(uint32_t)));
   int32_t* sync_ws = (int32_t*)((char*)pos_ws + align_up((size_t)hq * 2 * nbk * sizeof(int32_t)));
+  char* vsw_ws = (char*)sync_ws + kAlign;
+  const int vsw_cap = vsw_tile_capacity((int)n);
+  auto vsw_area = [&](int h, uint32_t*& dbits, int2*& tiles, int32_t*& count) {
+    char* base = vsw_ws + (size_t)h * vsw_head_bytes(n);
+    dbits = (uint32_t*)base;
+    tiles = (int2*)(base + align_up((size_t)((n + 31) / 32) * sizeof(uint32_t)));
+    count = (int32_t*)((char*)tiles + align_up((size_t)vsw_cap * sizeof(int2)));
+  };
+  if (any_vsw) {
+    // offset bitmaps and window tile covers of the VS window heads
+    VswLaunch w{};
+    int cnt = 0, max_ks = 0;
+    for (int h = 0; h <= hq; ++h) {
+      if (cnt == kMaxLaunchHeads || (h == hq && cnt > 0)) {
+        w.n = (int)n;
+        w.cap = vsw_cap;
+        hipError_t e = launch_vsw_prepare(w, cnt, max_ks, stream);
+        if (e != hipSuccess) return hip_fail(e, "VS window preparation kernels");
+        w = VswLaunch{};
+        cnt = max_ks = 0;
+      }
+      if (h == hq || plans[h].kind != MINF_KIND_VS_WINDOW) continue;
+      w.s_idx[cnt] = plans[h].s_idx;
+      w.k_s[cnt] = plans[h].k_s;
+      max_ks = std::max(max_ks, plans[h].k_s);
+      vsw_area(h, w.dbits[cnt], w.tiles[cnt], w.count[cnt]);
+      ++cnt;
+    }
+  }
   for (int h = 0; h < hq && any_pos; ++h) {
     if (!plans[h].pos) continue;
     // heads that share a position array share its block extremes
@@ -529,7 +568,16 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
       d2.kind = p.kind;
       d2.sink = p.sink;
       d2.local = p.local;
-      d2.k_v = p.kind == MINF_KIND_VS ? p.k_v : 0;
+      d2.k_v = (p.kind == MINF_KIND_VS || p.kind == MINF_KIND_VS_WINDOW) ? p.k_v : 0;
+      if (p.kind == MINF_KIND_VS_WINDOW) {
+        uint32_t* db;
+        int2* wt;
+        int32_t* wc;
+        vsw_area(h0 + i, db, wt, wc);
+        d2.dbits = db;
+        d2.wtiles = wt;
+        d2.wcount = wc;
+      }
       d2.k_b = p.k_b;
       d2.v_idx = p.v_idx;
       d2.obits = p.kind == MINF_KIND_VS ? (const uint32_t*)workspace + (size_t)(h0 + i) * words : nullptr;

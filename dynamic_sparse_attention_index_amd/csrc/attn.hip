@@ -73,9 +73,23 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-enum : int { KIND_DENSE = 0, KIND_ASHAPE = 1, KIND_VS = 2, KIND_BLOCK = 3 };
+enum : int { KIND_DENSE = 0, KIND_ASHAPE = 1, KIND_VS = 2, KIND_BLOCK = 3, KIND_VSW = 4 };
 
 __device__ __forceinline__ uint32_t bit_at(const uint32_t* w, int v) { return (w[v >> 5] >> (v & 31)) & 1u; }
+
+// Whether the offset bitmap w over [0, n) has a set bit in [x, x + 63].
+__device__ __forceinline__ bool any_offset(const uint32_t* w, int x, int n) {
+  const int lo = x > 0 ? x : 0;
+  const int hi = x + 63 < n - 1 ? x + 63 : n - 1;
+  if (lo > hi) return false;
+  for (int ww = lo >> 5; ww <= (hi >> 5); ++ww) {
+    uint32_t m = w[ww];
+    if (ww == (lo >> 5)) m &= 0xffffffffu << (lo & 31);
+    if (ww == (hi >> 5)) m &= 0xffffffffu >> (31 - (hi & 31));
+    if (m != 0u) return true;
+  }
+  return false;
+}
 
 // A value that is the same in every lane of the wave, as a scalar.
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
@@ -90,6 +104,10 @@ struct BlockIter {
   int w, wmax, base;   // VS / BLOCK bitmap cursor
   uint32_t rem;
   uint32_t mw0, mw1;   // membership of b0 / b1 for the bits of the current word
+  // VS windows: the head's tile cover (relative to a block's first row), the
+  // next tile of b0 and of b1, and the blocks' first rows
+  const int2* wt;
+  int nwt, i0, i1, wb0, wb1;
   // BLOCK: membership bitmaps over key blocks c of b0 and b1.
   // VS: block-offset bitmaps of b0 and b1 (they differ only for a partial last block).
   const uint32_t* bits0;
@@ -121,6 +139,24 @@ struct BlockIter {
     uint32_t u = union_word(w);
     if (w == wmax) u &= (vmax & 31) == 31 ? 0xffffffffu : ((1u << ((vmax & 31) + 1)) - 1u);
     rem = u;
+  }
+
+  // VS windows: the next tile of the pair in key order. b1's tiles are b0's
+  // shifted by 64 keys; a tile both blocks have is visited once. t is the
+  // tile's first key (may be negative near the start), e0 / e1 the end of the
+  // tile's interval for b0 / b1.
+  __device__ bool next_window(int& t, int& mem, int& e0, int& e1) {
+    const int s0 = i0 < nwt ? wb0 + wt[i0].x : 0x7fffffff;
+    const int s1 = i1 < nwt ? wb1 + wt[i1].x : 0x7fffffff;
+    if (s0 == 0x7fffffff && s1 == 0x7fffffff) return false;
+    t = s0 < s1 ? s0 : s1;
+    const int m0 = s0 == t, m1 = s1 == t;
+    e0 = m0 ? wb0 + wt[i0].y : 0;
+    e1 = m1 ? wb1 + wt[i1].y : 0;
+    i0 += m0;
+    i1 += m1;
+    mem = m0 | (m1 << 1);
+    return true;
   }
 
   // Next tile: key block c and membership (bit 0: block b0 uses it, bit 1: b1).
@@ -258,7 +294,7 @@ constexpr float kRescaleSlack = 0.0f;
 // 2 = general predicate (causal or j < n, plus the A-shape clause);
 // 3 = gathered columns (per-column membership flag and j <= i).
 // 4 = original positions (permuted sequences): key visible iff its position <= the row's.
-enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_GENERAL = 2, MASK_GATHER = 3, MASK_POS = 4 };
+enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_GENERAL = 2, MASK_GATHER = 3, MASK_POS = 4, MASK_WIN = 5 };
 
 template <bool POSM>
 __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
@@ -301,6 +337,19 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
         const int kx0 = 32 * mt + 8 * (i >> 2) + (i & 3);
         const bool vis = kx0 <= hi && (kx0 < lo_sink || kx0 > lo_win);
         s[mt][i] = vis ? s[mt][i] : -INFINITY;
+      }
+  } else if (POSM && MASK == MASK_WIN) {
+    // VS window tile from key key0: visible iff 0 <= j < local (the end of the
+    // block's window interval) and j <= row, with j = key0 + 4g + kx0
+    const int base = key0 + 4 * g;
+    const int hi = min(row - base, local - 1 - base);
+    const int lo = -base;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kx0 = 32 * mt + 8 * (i >> 2) + (i & 3);
+        s[mt][i] = (kx0 <= hi && kx0 >= lo) ? s[mt][i] : -INFINITY;
       }
   } else if (POSM && MASK == MASK_POS) {
     // gcols holds the tile's key positions; `row` is this lane's query position
@@ -382,8 +431,9 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
   }
 }
 
-// POSM: the launch has Block-Sparse heads on permuted sequences (a separate
-// instantiation, so the common kernel carries none of that code).
+// POSM: the launch has Block-Sparse heads on permuted sequences or VS window
+// heads (a separate instantiation, so the common kernel carries none of that
+// code).
 // One work item: a head and a pair of query blocks. Item i is the (i % C)-th
 // member of chunk i / C; a chunk is one group of hg heads sharing a KV head
 // times C / hg consecutive query-block pairs (C = 64), and chunks go heaviest
@@ -478,6 +528,25 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     it.bits1 = (need_last && b1 == p.nb - 1) ? sm.bits[1] : sm.bits[0];
     it.base = b0 + 1;
     it.init_bitmap_cursor(it.base);
+  } else if (POSM && hd.kind == KIND_VSW) {
+    // first tile of each block's window list that ends after key 0
+    it.wt = hd.wtiles;
+    it.nwt = (int)uniform_u32((uint32_t)*hd.wcount);
+    it.wb0 = b0 * kBlock;
+    it.wb1 = b1 * kBlock;
+    auto first_tile = [&](int wb) -> int {
+      int lo = 0, hi = it.nwt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (wb + it.wt[mid].y > 0)
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      return (int)uniform_u32((uint32_t)lo);
+    };
+    it.i0 = first_tile(it.wb0);
+    it.i1 = has_b1 ? first_tile(it.wb1) : it.nwt;
   } else {  // KIND_BLOCK (on a permuted sequence: every key block can be selected)
     const int cmax_blk = hd.pos ? p.nb - 1 : bmax;
     const int nwords = (cmax_blk >> 5) + 1;
@@ -537,16 +606,46 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
         }
       }
     };
+    // VS windows: tiles start at any key; e0 / e1 end the tile's interval for b0 / b1
+    const bool vsw = POSM && hd.kind == KIND_VSW;
+    int e0_cur = 0, e1_cur = 0, e0_nxt = 0, e1_nxt = 0;
+    auto next_tile = [&](int& c, int& m, int& e0, int& e1) -> bool {
+      if (POSM && vsw) return it.next_window(c, m, e0, e1);
+      return it.next(c, m);
+    };
+    auto issue_tile = [&](int c, uint16_t* ktn, uint16_t* vtn, uint32_t* psn) {
+      if (POSM && vsw) {
+        // 64 keys from key c; rows outside [0, n) load a valid row and are masked
+        if (c >= 0 && c + kBlock <= n) {
+          const size_t base = (size_t)c * (kHeadDim * 2);
+          issue_contig((const char*)kh + base, (const char*)vh + base, ktn, vtn, lane_off);
+        } else {
+          issue_rows(kh, vh, ktn, vtn, [&](int x) {
+            const int j = c + x;
+            return j < 0 ? 0 : (j < n ? j : n - 1);
+          });
+        }
+      } else {
+        issue_block(c, ktn, vtn, psn);
+      }
+    };
     // one pipelined step: issue the next tile into (ktn, vtn), compute the current one from (ktc, vtc)
     auto step = [&](uint16_t* ktc, uint16_t* vtc, uint32_t* psc, uint16_t* ktn, uint16_t* vtn,
                     uint32_t* psn) -> bool {
-      const bool hn = it.next(c_nxt, m_nxt);
-      if (hn) issue_block(c_nxt, ktn, vtn, psn);
+      const bool hn = next_tile(c_nxt, m_nxt, e0_nxt, e1_nxt);
+      if (hn) issue_tile(c_nxt, ktn, vtn, psn);
       if (wave_on && ((m_cur >> qsel) & 1)) {
         int full, mask;
+        int key0 = c_cur * kBlock, wend = hd.local;
         if (posm) {
           full = hd.blkmax[c_cur] <= wminpos;
           mask = full ? MASK_NONE : MASK_POS;
+        } else if (POSM && vsw) {
+          key0 = c_cur;
+          wend = qsel ? e1_cur : e0_cur;
+          const int rmin = qb * kBlock + (wave & 1) * 32;  // the wave's first row
+          full = key0 >= 0 && key0 + kBlock <= wend && key0 + kBlock - 1 <= rmin;
+          mask = full ? MASK_NONE : MASK_WIN;
         } else {
           if (causal_eff) {
             full = c_cur < qb;
@@ -559,21 +658,22 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
           mask = full ? MASK_NONE : ((causal_eff && !ashape) ? MASK_CAUSAL : MASK_GENERAL);
         }
         // rpos is the query row itself unless the sequence is permuted
-        compute_tile<POSM>(ws, oo, ktc, vtc, mask, c_cur * kBlock, POSM ? psc : nullptr, qsel, rpos, n, causal_eff,
-                           ashape, hd.sink,
-                     hd.local, sl2);
+        compute_tile<POSM>(ws, oo, ktc, vtc, mask, key0, POSM ? psc : nullptr, qsel, rpos, n, causal_eff, ashape,
+                           hd.sink, wend, sl2);
       }
       wait_vmem();
       __syncthreads();
       c_cur = c_nxt;
       m_cur = m_nxt;
+      e0_cur = e0_nxt;
+      e1_cur = e1_nxt;
       return hn;
     };
     // key-position slots of the two tile buffers (phase B, which uses clist, never runs on BLOCK heads)
     uint32_t* ps0 = sm.clist;
     uint32_t* ps1 = sm.clist + kBlock;
-    bool have = it.next(c_cur, m_cur);
-    if (have) issue_block(c_cur, kt0, vt0, ps0);
+    bool have = next_tile(c_cur, m_cur, e0_cur, e1_cur);
+    if (have) issue_tile(c_cur, kt0, vt0, ps0);
     wait_vmem();
     __syncthreads();
     while (have) {
@@ -582,8 +682,8 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     }
   }
 
-  // ---------------- phase B: gathered vertical columns (VS heads)
-  if (hd.kind == KIND_VS && hd.k_v > 0) {
+  // ---------------- phase B: gathered vertical columns (VS and VS window heads)
+  if ((hd.kind == KIND_VS || (POSM && hd.kind == KIND_VSW)) && hd.k_v > 0) {
     const int lim = bmax * kBlock + kBlock - 1;  // last row of the pair
     for (int base = 0; base < hd.k_v; base += kColChunk) {
       // compact this chunk's kept columns (ascending) into clist, with membership bits
@@ -599,8 +699,15 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
           if (j > lim) past = true;
           if (j >= 0 && j < n && j <= lim && j != prev) {
             const int cb = j / kBlock;
-            const int m0 = cb <= b0 && !bit_at(it.bits0, b0 - cb);
-            const int m1 = has_b1 && cb <= b1 && !bit_at(it.bits1, b1 - cb);
+            int m0, m1;
+            if (POSM && hd.kind == KIND_VSW) {
+              // outside the block's windows: no offset dl with 64b - dl <= j <= 64b - dl + 63
+              m0 = cb <= b0 && !any_offset(hd.dbits, b0 * kBlock - j, n);
+              m1 = has_b1 && cb <= b1 && !any_offset(hd.dbits, b1 * kBlock - j, n);
+            } else {
+              m0 = cb <= b0 && !bit_at(it.bits0, b0 - cb);
+              m1 = has_b1 && cb <= b1 && !bit_at(it.bits1, b1 - cb);
+            }
             keep = m0 | m1;
             entry = (uint32_t)j | ((uint32_t)m0 << 30) | ((uint32_t)m1 << 31);
           }
@@ -804,7 +911,7 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   // the grid covers whole rounds of kXcds chunks so that the item map is a bijection
   const long long grid = (chunks + kXcds - 1) / kXcds * kXcds * kChunk;
   bool posm = false;
-  for (int i = 0; i < a.nh; ++i) posm |= a.heads[i].pos != nullptr;
+  for (int i = 0; i < a.nh; ++i) posm |= a.heads[i].pos != nullptr || a.heads[i].kind == KIND_VSW;
   AttnLaunch c = a;
   c.xcd_sync = nullptr;
   c.rounds_flag = nullptr;

@@ -19,6 +19,9 @@ struct AttnHead {
   const int32_t* blk_cnt;  // BLOCK
   const int32_t* pos;      // BLOCK on a permuted sequence: original position of every row (else null)
   const int32_t* blkmax;   // with pos: latest original position in every key block
+  const int2* wtiles;      // VS windows: tile cover of the windows relative to a block's first row
+  const int32_t* wcount;   // VS windows: number of tiles (device)
+  const uint32_t* dbits;   // VS windows: bitmap of the slash offsets over [0, n)
 };
 
 struct AttnLaunch {
@@ -43,6 +46,18 @@ hipError_t launch_vs_offset_bits(const int32_t* const* s_idx, const int32_t* k_s
 // flag = 1 when the VS heads' offset bitmaps (up to 32) average at least min_tiles tiles per item
 hipError_t launch_rounds_flag(uint32_t* const* bits, int count, int n, int min_tiles, int32_t* flag,
                               hipStream_t stream);
+
+// Slash-aligned window preparation for up to kMaxLaunchHeads heads.
+struct VswLaunch {
+  const int32_t* s_idx[kMaxLaunchHeads];
+  int32_t k_s[kMaxLaunchHeads];
+  uint32_t* dbits[kMaxLaunchHeads];  // [(n + 31) / 32]
+  int2* tiles[kMaxLaunchHeads];      // [cap]
+  int32_t* count[kMaxLaunchHeads];   // [1]
+  int32_t n, cap;
+};
+int vsw_tile_capacity(int n);
+hipError_t launch_vsw_prepare(const VswLaunch& a, int count, int max_k_s, hipStream_t stream);
 
 struct VsGroup {
   int32_t kv;        // KV head of the group

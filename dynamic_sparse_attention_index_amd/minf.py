@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libminf.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "minf.h")
 
 MINF_OK = 0
-KIND = {"dense": 0, "ashape": 1, "vs": 2, "block": 3}
+KIND = {"dense": 0, "ashape": 1, "vs": 2, "block": 3, "vs_window": 4}
 
 
 class MinfError(RuntimeError):
@@ -263,7 +263,7 @@ def make_plans(plans):
         e.kind = KIND[kind]
         if kind == "ashape":
             e.sink, e.local = int(p["sink"]), int(p["local"])
-        elif kind == "vs":
+        elif kind in ("vs", "vs_window"):
             vi, si = p["v_idx"], p["s_idx"]
             for t, nm in ((vi, "v_idx"), (si, "s_idx")):
                 _need(t, torch.int32, nm)

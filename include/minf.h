@@ -58,7 +58,7 @@ const char* minf_status_string(minf_status s);
 /* Detail text of the last failure on the calling thread ("" if none). */
 const char* minf_last_error_detail(void);
 
-/* Library ABI version (incremented when a signature or struct changes). */
+/* Library ABI version (incremented when a signature, a struct or the set of plan kinds changes). */
 int minf_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -164,6 +164,14 @@ minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const 
  *                      dl in s_idx, i' - dl >= 0 } (slash lines covered by
  *                      whole 64x64 blocks).
  *   MINF_KIND_BLOCK  : j <= i and block(j) in blk_idx[b][0 .. blk_cnt[b]).
+ *   MINF_KIND_VS_WINDOW : j <= i and (j in W(b) or j in v_idx), where W(b) is
+ *                      the union over dl in s_idx with 64b + 63 - dl >= 0 of the
+ *                      keys [64b - dl, 64b - dl + 64): each slash line as the
+ *                      64-key window it meets from the block's rows, shifted
+ *                      to start at the block's first row, rather than the grid
+ *                      blocks it crosses (the index-shifting reading of the
+ *                      "Method" section and the talk transcript). Same v_idx /
+ *                      s_idx / k_v / k_s fields as MINF_KIND_VS.
  * O_i = softmax over that set of scale * q_i . k_j, applied to V (fp32
  * online softmax and accumulation, bf16 MFMA products, bf16 output). An
  * empty set gives O_i = 0 and LSE_i = -inf.
@@ -180,6 +188,7 @@ minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const 
 #define MINF_KIND_ASHAPE 1
 #define MINF_KIND_VS 2
 #define MINF_KIND_BLOCK 3
+#define MINF_KIND_VS_WINDOW 4
 
 typedef struct minf_head_plan {
   int32_t kind;           /* MINF_KIND_* */

@@ -31,7 +31,7 @@ def test_status_strings():
     assert LIB.minf_status_string(WORKSPACE) == b"MINF_E_WORKSPACE"
     assert LIB.minf_status_string(HIP) == b"MINF_E_HIP"
     assert LIB.minf_status_string(99) == b"MINF_E_UNKNOWN"
-    assert LIB.minf_abi_version() == 2
+    assert LIB.minf_abi_version() == 3
 
 
 def test_workspace_sizes():

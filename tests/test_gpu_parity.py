@@ -267,3 +267,93 @@ def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch, n):
     print(f"  rounds launch: max-abs err {err:.3e}", flush=True)
     assert err <= OUT_TOL
     check_lse(l1[h][t].cpu().numpy(), wl[0])
+
+
+# ---------------------------------------------------------------- VS with slash-aligned windows
+def _window_plans(n, hq, seed, k_s, k_v, local=False, aligned=False):
+    g = torch.Generator().manual_seed(seed)
+    plans = []
+    for h in range(hq):
+        if local:
+            si = torch.arange(min(k_s + h, n), dtype=torch.int32)
+        else:
+            si = torch.randperm(n, generator=g)[:min(k_s + 7 * h, n)].sort().values.to(torch.int32)
+            if aligned:
+                si = torch.unique(si // 64 * 64).to(torch.int32)
+        vi = torch.randperm(n, generator=g)[:min(k_v, n)].sort().values.to(torch.int32)
+        plans.append(dict(kind="vs_window", v_idx=vi.cuda(), s_idx=si.cuda()))
+    return plans
+
+
+@pytest.mark.parametrize("n", [64, 200, 1000, 4160, 4096 + 77])
+def test_vs_window_attention(gpu_lib, n):
+    # scattered offsets (windows at every alignment, overlapping and isolated) and verticals
+    q, k, v, _ = _qkv(n, 4, 2, 26)
+    _attn_parity(gpu_lib, q, k, v, _window_plans(n, 4, 27, k_s=40, k_v=30))
+
+
+@pytest.mark.parametrize("n", [300, 2048 + 64])
+def test_vs_window_local_and_edge_offsets(gpu_lib, n):
+    # local offsets [0, k_s): one long interval per block; offsets past n and duplicates are ignored
+    q, k, v, _ = _qkv(n, 4, 2, 28)
+    plans = _window_plans(n, 4, 29, k_s=150, k_v=50, local=True)
+    extra = torch.tensor([n, n + 5, -3, 0, 0, 1], dtype=torch.int32, device="cuda")
+    gpu_plans = list(plans)
+    gpu_plans[3] = dict(kind="vs_window", v_idx=plans[3]["v_idx"], s_idx=torch.cat([plans[3]["s_idx"], extra]))
+    o, lse = gpu_lib.minf_sparse_attn(q, k, v, gpu_plans, scale=SCALE)
+    torch.cuda.synchronize()
+    # the library ignores offsets outside [0, n): the oracle sees the plan without them
+    want_o, want_l = O.sparse_attn(to_np(q), to_np(k), to_np(v), 4, 2, SCALE, _np_plans(plans))
+    err = max_abs(to_np(o), want_o)
+    print(f"  max-abs err {err:.3e}", flush=True)
+    assert err <= OUT_TOL
+    check_lse(to_np(lse), want_l)
+
+
+def test_vs_window_block_aligned_equals_block_reading(gpu_lib):
+    # offsets that are multiples of 64 give windows equal to the grid blocks they cross
+    n = 4096 + 64
+    q, k, v, _ = _qkv(n, 4, 2, 30)
+    pw = _window_plans(n, 4, 31, k_s=30, k_v=40, aligned=True)
+    pb = [dict(kind="vs", v_idx=p["v_idx"], s_idx=p["s_idx"]) for p in pw]
+    ow, lw = gpu_lib.minf_sparse_attn(q, k, v, pw, scale=SCALE)
+    ob, lb = gpu_lib.minf_sparse_attn(q, k, v, pb, scale=SCALE)
+    torch.cuda.synchronize()
+    assert max_abs(to_np(ow), to_np(ob)) <= 1e-2
+    empty = torch.isneginf(lb)  # rows with no key in either reading
+    assert torch.equal(empty, torch.isneginf(lw))
+    assert float((lw[~empty] - lb[~empty]).abs().max()) <= 1e-3
+
+
+def test_vs_window_full_budget_and_empty(gpu_lib):
+    n = 1000
+    q, k, v, _ = _qkv(n, 2, 1, 32)
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    full = torch.arange(n, dtype=torch.int32, device="cuda")
+    plans = [dict(kind="vs_window", v_idx=e, s_idx=full), dict(kind="vs_window", v_idx=e, s_idx=e)]
+    o, lse = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    od, ld = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE)
+    torch.cuda.synchronize()
+    assert max_abs(to_np(o[0]), to_np(od[0])) <= OUT_TOL
+    assert float((lse[0] - ld[0]).abs().max()) <= 2e-3
+    assert (o[1] == 0).all() and torch.isneginf(lse[1]).all()
+
+
+def test_vs_window_large_sampled_rows(gpu_lib):
+    # 2^19 tokens, scattered offsets: sampled rows against the oracle; mixed with block-reading heads
+    n, hq = 1 << 19, 4
+    q, k, v, _ = _qkv(n, hq, 1, 33)
+    plans = _window_plans(n, hq, 34, k_s=2000, k_v=300)
+    plans[1] = dict(kind="vs", v_idx=plans[1]["v_idx"], s_idx=plans[1]["s_idx"])
+    o, lse = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 64), np.arange(n // 2 + 64, n // 2 + 128), np.arange(n - 64, n)])
+    t = torch.as_tensor(rows, device="cuda")
+    for h in (0, 1):
+        qh = np.zeros((1, n, 128), np.float32)
+        qh[0, rows] = to_np(q[h][t])
+        wo, wl = O.sparse_attn(qh, to_np(k), to_np(v), 1, 1, SCALE, _np_plans([plans[h]]), rows=rows)
+        err = max_abs(to_np(o[h][t]), wo[0])
+        print(f"  head {h} ({plans[h]['kind']}): max-abs err {err:.3e}", flush=True)
+        assert err <= OUT_TOL
+        check_lse(lse[h][t].cpu().numpy(), wl[0])
