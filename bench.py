@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-structured", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-grid", action="store_true")
+    ap.add_argument("--no-window", action="store_true", help="skip the VS slash-aligned window leg")
     ap.add_argument("--grid-blocks", type=int, default=64, help="block budget of the grid track")
     ap.add_argument("--search", action="store_true", help="also time the offline pattern search on the input")
     ap.add_argument("--decode-blocks", type=int, default=64,
@@ -81,6 +82,52 @@ def vs_work(v_idx, s_idx, n):
         hit = off[rel.clamp(min=0)]
         cols += int((ok & ~hit).sum())
     return blocks, cols
+
+
+def vsw_work(v_idx, s_idx, n):
+    """(computed 64-key window tiles, gathered columns) of one VS window head, summed over query blocks.
+
+    The tiles restate the library's cover of U = union over offsets dl of [-dl, -dl + 64): each
+    maximal interval of U cut into 64-key tiles from its start; query block b computes the tiles
+    with 64 b + end > 0. Column j lies in block b's windows iff b = floor((dl + j) / 64) for an
+    offset dl, so it is gathered for every other block b >= floor(j / 64).
+    """
+    import torch
+    nb = (n + 63) // 64
+    dev = s_idx.device
+    d = s_idx.long()
+    d = torch.unique(d[(d >= 0) & (d < n)])                   # ascending
+    if d.numel() == 0:
+        tiles = 0
+        dset_blocks = None
+    else:
+        starts = torch.flip(-d, [0])                           # window starts, ascending
+        brk = torch.ones_like(starts, dtype=torch.bool)
+        brk[1:] = (starts[1:] - starts[:-1]) > 64
+        iv_start = starts[brk]
+        last_idx = torch.cat([torch.nonzero(brk).flatten()[1:] - 1,
+                              torch.tensor([starts.numel() - 1], device=dev)])
+        iv_end = starts[last_idx] + 64
+        ntile = (iv_end - iv_start + 63) // 64
+        first = torch.repeat_interleave(iv_start, ntile)
+        off = torch.arange(int(ntile.sum()), device=dev) - torch.repeat_interleave(torch.cumsum(ntile, 0) - ntile, ntile)
+        t_start = first + 64 * off
+        t_end = torch.minimum(t_start + 64, torch.repeat_interleave(iv_end, ntile))
+        bs = torch.arange(nb, device=dev)
+        tiles = int((t_end.numel() - torch.searchsorted(t_end, -64 * bs, right=True)).sum())
+    cols = 0
+    j = v_idx.long()
+    j = j[(j >= 0) & (j < n)]
+    for part in torch.split(j, 256):
+        base = part // 64
+        own = nb - base
+        if d.numel():
+            m = (d[None, :] + part[:, None]) // 64                # covering blocks, non-decreasing per row
+            valid = m < nb
+            distinct = valid[:, 0].long() + ((m[:, 1:] != m[:, :-1]) & valid[:, 1:]).sum(dim=1)
+            own = own - distinct
+        cols += int(own.sum())
+    return tiles, cols
 
 
 def useful_entries(plan, n):
@@ -411,6 +458,45 @@ def main():
         }
         print(f"[bench] injected track: attention {inj_attn_ms:.2f} ms, "
               f"{extra['injected_track']['attn_tflops']} TFLOP/s", file=sys.stderr, flush=True)
+
+    # VS with slash-aligned windows (index shifting) on the same indexes: literal data (T1) and,
+    # when run, the index-injected track (T3); compared with the block reading of those indexes
+    if not args.no_window and vs_heads:
+        def window_leg(plans_x, ref_ms):
+            pw = [dict(kind="vs_window", v_idx=p["v_idx"], s_idx=p["s_idx"]) if p["kind"] == "vs" else p
+                  for p in plans_x]
+            cpw = minf.make_plans(pw)
+            minf.minf_sparse_attn(q, k, v, cpw, scale=scale, out=o, lse=lse, workspace=ws_at)
+            torch.cuda.synchronize()
+            reps_w = []
+            for _ in range(max(2, args.steps)):
+                a, b = ev(), ev()
+                a.record(stream)
+                minf.minf_sparse_attn(q, k, v, cpw, scale=scale, out=o, lse=lse, workspace=ws_at)
+                b.record(stream)
+                reps_w.append((a, b))
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in reps_w) / len(reps_w)
+            wt = wc = 0
+            for h in range(hq):
+                if pw[h]["kind"] == "vs_window":
+                    t_, c_ = vsw_work(pw[h]["v_idx"], pw[h]["s_idx"], n)
+                else:
+                    t_, c_ = head_work[h]
+                wt += t_
+                wc += c_
+            wf = wt * BLOCK_FLOP + wc * COL_FLOP
+            return {"attn_ms": round(ms, 3), "computed_tiles": wt, "gathered_columns": wc,
+                    "attn_tflops": round(wf / (ms * 1e-3) / 1e12, 1), "vs_block_reading_attn_ms": round(ref_ms, 3),
+                    "time_vs_block_reading": round(ms / ref_ms, 3)}
+        wl = {"literal": window_leg(plans_t, attn_ms)}
+        if "injected_track" in extra:
+            wl["injected"] = window_leg(inj_plans, extra["injected_track"]["attn_ms"])
+        extra["vs_window"] = wl
+        print(f"[bench] VS windows: " + ", ".join(
+            f"{kk} {vv['attn_ms']:.2f} ms ({vv['computed_tiles']} tiles + {vv['gathered_columns']} columns, "
+            f"{vv['attn_tflops']} TFLOP/s; x{vv['time_vs_block_reading']} the block reading)" for kk, vv in wl.items()),
+            file=sys.stderr, flush=True)
 
     # structured track: the same layer on locality-latent data, index built from the data
     if not args.no_structured:

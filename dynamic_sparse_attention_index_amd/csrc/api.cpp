@@ -595,17 +595,20 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
       }
     }
     std::vector<uint32_t*> launch_bits;
-    for (int i = 0; i < nh; ++i)
+    std::vector<const int32_t*> launch_wcount;
+    for (int i = 0; i < nh; ++i) {
       if (plans[h0 + i].kind == MINF_KIND_VS) launch_bits.push_back((uint32_t*)workspace + (size_t)(h0 + i) * words);
+      if (plans[h0 + i].kind == MINF_KIND_VS_WINDOW) launch_wcount.push_back(a.heads[i].wcount);
+    }
     a.head0 = h0;
     a.nh = nh;
     a.hgroup = hg;
     a.xcd_sync = nullptr;
     a.rounds_flag = nullptr;
-    if (!launch_bits.empty() && n >= kRoundsMinTokens && rounds_enabled()) {
+    if ((!launch_bits.empty() || !launch_wcount.empty()) && n >= kRoundsMinTokens && rounds_enabled()) {
       int32_t* flag = sync_ws + 8;
-      hipError_t e = launch_rounds_flag(launch_bits.data(), (int)launch_bits.size(), (int)n, kRoundsMinTiles, flag,
-                                        stream);
+      hipError_t e = launch_rounds_flag(launch_bits.data(), (int)launch_bits.size(), launch_wcount.data(),
+                                        (int)launch_wcount.size(), (int)n, kRoundsMinTiles, flag, stream);
       if (e != hipSuccess) return hip_fail(e, "rounds flag kernel");
       a.xcd_sync = sync_ws;
       a.rounds_flag = flag;

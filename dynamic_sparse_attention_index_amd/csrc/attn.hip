@@ -852,7 +852,8 @@ struct OffBitsLaunch {
   const int32_t* s_idx[kMaxLaunchHeads];
   int32_t k_s[kMaxLaunchHeads];
   uint32_t* bits[kMaxLaunchHeads];
-  int32_t n, nb;
+  const int32_t* wcount[kMaxLaunchHeads];  // rounds flag: tile counts of VS window heads
+  int32_t n, nb, nw;
 };
 
 __global__ __launch_bounds__(256) void vs_offset_bits_kernel(const OffBitsLaunch a) {
@@ -938,9 +939,10 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
 }
 
 // Rounds pay off when the work items are long: flag = 1 when the listed VS
-// heads' offset sets O u (O + 1) hold on average at least `min_tiles` block
-// offsets (the tile count of the longest query-block pairs). One workgroup of
-// 1024 threads walks every head's bitmap words as one flat index space.
+// heads' offset sets O u (O + 1), and the listed VS window heads' tile covers,
+// hold on average at least `min_tiles` tiles (the tile count of the longest
+// query-block pairs). One workgroup of 1024 threads walks every head's bitmap
+// words as one flat index space.
 __global__ __launch_bounds__(1024) void rounds_flag_kernel(const OffBitsLaunch a, int count, int min_tiles,
                                                            int32_t* flag) {
   __shared__ unsigned long long tot;
@@ -957,16 +959,20 @@ __global__ __launch_bounds__(1024) void rounds_flag_kernel(const OffBitsLaunch a
     const uint32_t prev = i > 0 ? w[i - 1] : 0u;
     mine += (unsigned long long)__popc(w[i] | (w[i] << 1) | (prev >> 31));
   }
+  if ((int)threadIdx.x < a.nw) mine += (unsigned long long)*a.wcount[threadIdx.x];
   atomicAdd(&tot, mine);
   __syncthreads();
-  if (threadIdx.x == 0) *flag = (count > 0 && tot >= (unsigned long long)min_tiles * count) ? 1 : 0;
+  const int heads = count + a.nw;
+  if (threadIdx.x == 0) *flag = (heads > 0 && tot >= (unsigned long long)min_tiles * heads) ? 1 : 0;
 }
 
-hipError_t launch_rounds_flag(uint32_t* const* bits, int count, int n, int min_tiles, int32_t* flag,
-                              hipStream_t stream) {
+hipError_t launch_rounds_flag(uint32_t* const* bits, int count, const int32_t* const* wcount, int nw, int n,
+                              int min_tiles, int32_t* flag, hipStream_t stream) {
   OffBitsLaunch a{};
   const int c = count < kMaxLaunchHeads ? count : kMaxLaunchHeads;
   for (int i = 0; i < c; ++i) a.bits[i] = bits[i];
+  a.nw = nw < kMaxLaunchHeads ? nw : kMaxLaunchHeads;
+  for (int i = 0; i < a.nw; ++i) a.wcount[i] = wcount[i];
   a.n = n;
   a.nb = (n + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(rounds_flag_kernel, dim3(1), dim3(1024), 0, stream, a, c, min_tiles, flag);

@@ -43,9 +43,10 @@ struct AttnLaunch {
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_vs_offset_bits(const int32_t* const* s_idx, const int32_t* k_s, uint32_t* const* bits,
                                  int count, int n, hipStream_t stream);
-// flag = 1 when the VS heads' offset bitmaps (up to 32) average at least min_tiles tiles per item
-hipError_t launch_rounds_flag(uint32_t* const* bits, int count, int n, int min_tiles, int32_t* flag,
-                              hipStream_t stream);
+// flag = 1 when the VS heads' offset bitmaps and the VS window heads' tile counts (up to 32 each)
+// average at least min_tiles tiles per item
+hipError_t launch_rounds_flag(uint32_t* const* bits, int count, const int32_t* const* wcount, int nw, int n,
+                              int min_tiles, int32_t* flag, hipStream_t stream);
 
 // Slash-aligned window preparation for up to kMaxLaunchHeads heads.
 struct VswLaunch {
