@@ -295,8 +295,9 @@ constexpr float kRescaleSlack = 0.0f;
 // 3 = gathered columns (per-column membership flag and j <= i).
 // 4 = original positions (permuted sequences): key visible iff its position <= the row's.
 enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_GENERAL = 2, MASK_GATHER = 3, MASK_POS = 4, MASK_WIN = 5 };
+constexpr int kXkPos = 1, kXkWin = 2;  // extended plan kinds of an attention instantiation
 
-template <bool POSM>
+template <int XK>
 __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
                                              const uint16_t* vt, int MASK, int key0, const uint32_t* gcols,
                                              int qsel, int row, int n, int causal, int ashape, int sink,
@@ -338,7 +339,7 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
         const bool vis = kx0 <= hi && (kx0 < lo_sink || kx0 > lo_win);
         s[mt][i] = vis ? s[mt][i] : -INFINITY;
       }
-  } else if (POSM && MASK == MASK_WIN) {
+  } else if ((XK & kXkWin) && MASK == MASK_WIN) {
     // VS window tile from key key0: visible iff 0 <= j < local (the end of the
     // block's window interval) and j <= row, with j = key0 + 4g + kx0
     const int base = key0 + 4 * g;
@@ -351,7 +352,7 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
         const int kx0 = 32 * mt + 8 * (i >> 2) + (i & 3);
         s[mt][i] = (kx0 <= hi && kx0 >= lo) ? s[mt][i] : -INFINITY;
       }
-  } else if (POSM && MASK == MASK_POS) {
+  } else if ((XK & kXkPos) && MASK == MASK_POS) {
     // gcols holds the tile's key positions; `row` is this lane's query position
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -431,14 +432,14 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
   }
 }
 
-// POSM: the launch has Block-Sparse heads on permuted sequences or VS window
-// heads (a separate instantiation, so the common kernel carries none of that
-// code).
+// XK: the extended plan kinds the launch holds (kXkPos: Block-Sparse heads on
+// permuted sequences; kXkWin: VS window heads). Each combination is its own
+// instantiation, so every kernel carries only the code its launch needs.
 // One work item: a head and a pair of query blocks. Item i is the (i % C)-th
 // member of chunk i / C; a chunk is one group of hg heads sharing a KV head
 // times C / hg consecutive query-block pairs (C = 64), and chunks go heaviest
 // pair block first.
-template <bool POSM>
+template <int XK>
 __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, Smem& sm, uint16_t* kt0,
                                           uint16_t* kt1, uint16_t* vt0, uint16_t* vt1) {
   const int tid = threadIdx.x;
@@ -528,7 +529,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     it.bits1 = (need_last && b1 == p.nb - 1) ? sm.bits[1] : sm.bits[0];
     it.base = b0 + 1;
     it.init_bitmap_cursor(it.base);
-  } else if (POSM && hd.kind == KIND_VSW) {
+  } else if ((XK & kXkWin) && hd.kind == KIND_VSW) {
     // first tile of each block's window list that ends after key 0
     it.wt = hd.wtiles;
     it.nwt = (int)uniform_u32((uint32_t)*hd.wcount);
@@ -572,7 +573,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     it.init_bitmap_cursor(cmax_blk);
   }
   // permuted sequences: each lane's query position and the wave's earliest one
-  const bool posm = POSM && hd.kind == KIND_BLOCK && hd.pos != nullptr;
+  const bool posm = (XK & kXkPos) && hd.kind == KIND_BLOCK && hd.pos != nullptr;
   int rpos = row, wminpos = 0;
   if (posm) {
     rpos = row < n ? hd.pos[row] : -1;
@@ -607,14 +608,14 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       }
     };
     // VS windows: tiles start at any key; e0 / e1 end the tile's interval for b0 / b1
-    const bool vsw = POSM && hd.kind == KIND_VSW;
+    const bool vsw = (XK & kXkWin) && hd.kind == KIND_VSW;
     int e0_cur = 0, e1_cur = 0, e0_nxt = 0, e1_nxt = 0;
     auto next_tile = [&](int& c, int& m, int& e0, int& e1) -> bool {
-      if (POSM && vsw) return it.next_window(c, m, e0, e1);
+      if ((XK & kXkWin) && vsw) return it.next_window(c, m, e0, e1);
       return it.next(c, m);
     };
     auto issue_tile = [&](int c, uint16_t* ktn, uint16_t* vtn, uint32_t* psn) {
-      if (POSM && vsw) {
+      if ((XK & kXkWin) && vsw) {
         // 64 keys from key c; rows outside [0, n) load a valid row and are masked
         if (c >= 0 && c + kBlock <= n) {
           const size_t base = (size_t)c * (kHeadDim * 2);
@@ -640,7 +641,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
         if (posm) {
           full = hd.blkmax[c_cur] <= wminpos;
           mask = full ? MASK_NONE : MASK_POS;
-        } else if (POSM && vsw) {
+        } else if ((XK & kXkWin) && vsw) {
           key0 = c_cur;
           wend = qsel ? e1_cur : e0_cur;
           const int rmin = qb * kBlock + (wave & 1) * 32;  // the wave's first row
@@ -658,7 +659,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
           mask = full ? MASK_NONE : ((causal_eff && !ashape) ? MASK_CAUSAL : MASK_GENERAL);
         }
         // rpos is the query row itself unless the sequence is permuted
-        compute_tile<POSM>(ws, oo, ktc, vtc, mask, key0, POSM ? psc : nullptr, qsel, rpos, n, causal_eff, ashape,
+        compute_tile<XK>(ws, oo, ktc, vtc, mask, key0, (XK & kXkPos) ? psc : nullptr, qsel, rpos, n, causal_eff, ashape,
                            hd.sink, wend, sl2);
       }
       wait_vmem();
@@ -683,7 +684,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
   }
 
   // ---------------- phase B: gathered vertical columns (VS and VS window heads)
-  if ((hd.kind == KIND_VS || (POSM && hd.kind == KIND_VSW)) && hd.k_v > 0) {
+  if ((hd.kind == KIND_VS || ((XK & kXkWin) && hd.kind == KIND_VSW)) && hd.k_v > 0) {
     const int lim = bmax * kBlock + kBlock - 1;  // last row of the pair
     for (int base = 0; base < hd.k_v; base += kColChunk) {
       // compact this chunk's kept columns (ascending) into clist, with membership bits
@@ -700,7 +701,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
           if (j >= 0 && j < n && j <= lim && j != prev) {
             const int cb = j / kBlock;
             int m0, m1;
-            if (POSM && hd.kind == KIND_VSW) {
+            if ((XK & kXkWin) && hd.kind == KIND_VSW) {
               // outside the block's windows: no offset dl with 64b - dl <= j <= 64b - dl + 63
               m0 = cb <= b0 && !any_offset(hd.dbits, b0 * kBlock - j, n);
               m1 = has_b1 && cb <= b1 && !any_offset(hd.dbits, b1 * kBlock - j, n);
@@ -737,7 +738,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
             // (padding slots were cleared, so they never count)
             const uint32_t* gc = sm.clist + t * kBlock;
             if (__any((gc[lane] >> (30 + qsel)) & 1u))
-              compute_tile<POSM>(ws, oo, ktc, vtc, MASK_GATHER, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
+              compute_tile<XK>(ws, oo, ktc, vtc, MASK_GATHER, 0, gc, qsel, row, n, 1, 0, 0, 0, sl2);
           }
           wait_vmem();
           __syncthreads();
@@ -799,7 +800,7 @@ __device__ __forceinline__ void xcd_barrier(int32_t* ctr, int target) {
 // through whole chunks of C consecutive items, C = 64 being what one XCD holds
 // at once (32 CUs x 2 workgroups): the workgroups resident on an XCD stream
 // the same K/V tiles through its L2.
-template <bool POSM>
+template <int XK>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   __shared__ Smem sm;
   __shared__ __attribute__((aligned(16))) uint16_t kt0[kTileHalves];
@@ -810,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   if (p.rounds_flag != nullptr && *p.rounds_flag != 0) return;
   const int slot = blockIdx.x >> 3;
   const int xcd = (int)(blockIdx.x & (kXcds - 1));
-  attn_item<POSM>(p, ((slot / kChunk) * kXcds + xcd) * kChunk + slot % kChunk, sm, kt0, kt1, vt0, vt1);
+  attn_item<XK>(p, ((slot / kChunk) * kXcds + xcd) * kChunk + slot % kChunk, sm, kt0, kt1, vt0, vt1);
 }
 
 // Rounds variant: exactly 8 x 64 workgroups, launched cooperatively so that
@@ -820,7 +821,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
 // key position and keep sharing K/V tiles in that XCD's L2. It works only
 // when *p.rounds_flag is set (the flag is computed on the device from the
 // offset bitmaps); otherwise the ordinary launch queued after it does.
-template <bool POSM>
+template <int XK>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel_rounds(const AttnLaunch p) {
   __shared__ Smem sm;
   __shared__ __attribute__((aligned(16))) uint16_t kt0[kTileHalves];
@@ -831,7 +832,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel_rounds(const AttnLaun
   const int slot = blockIdx.x >> 3;
   const int xcd = (int)(blockIdx.x & (kXcds - 1));
   for (int r = 0; r < p.rounds; ++r) {
-    attn_item<POSM>(p, (r * kXcds + xcd) * kChunk + slot, sm, kt0, kt1, vt0, vt1);
+    attn_item<XK>(p, (r * kXcds + xcd) * kChunk + slot, sm, kt0, kt1, vt0, vt1);
     xcd_barrier(p.xcd_sync + xcd, kChunk * (r + 1));
   }
 }
@@ -882,22 +883,30 @@ __global__ __launch_bounds__(256) void vs_offset_bits_kernel(const OffBitsLaunch
 
 }  // namespace
 
+template <int XK>
+static const void* rounds_kernel() { return (const void*)attn_kernel_rounds<XK>; }
+static const void* rounds_kernel_of(int xk) {
+  switch (xk) {
+    case 1: return rounds_kernel<1>();
+    case 2: return rounds_kernel<2>();
+    case 3: return rounds_kernel<3>();
+    default: return rounds_kernel<0>();
+  }
+}
+
 // Whether this device keeps all 8 x 64 workgroups of a rounds launch resident
 // together (cooperative launches are supported and two workgroups fit per CU
 // on at least 256 CUs). Asked once per device and instantiation.
-static bool rounds_supported(bool posm) {
-  static int cache[2][64] = {};  // 0 unknown, 1 yes, 2 no
+static bool rounds_supported(int xk) {
+  static int cache[4][64] = {};  // 0 unknown, 1 yes, 2 no
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-  int& c = cache[posm][dev];
+  int& c = cache[xk & 3][dev];
   if (c == 0) {
     int coop = 0, cus = 0, per_cu = 0;
     hipError_t e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, posm ? (const void*)attn_kernel_rounds<true> : (const void*)attn_kernel_rounds<false>,
-          kThreads, 0);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rounds_kernel_of(xk), kThreads, 0);
     c = (e == hipSuccess && coop && (long long)cus * per_cu >= kXcds * kChunk) ? 1 : 2;
   }
   return c == 1;
@@ -911,12 +920,15 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   const long long chunks = (long long)((npairs + ppc - 1) / ppc) * (a.nh / a.hgroup);
   // the grid covers whole rounds of kXcds chunks so that the item map is a bijection
   const long long grid = (chunks + kXcds - 1) / kXcds * kXcds * kChunk;
-  bool posm = false;
-  for (int i = 0; i < a.nh; ++i) posm |= a.heads[i].pos != nullptr || a.heads[i].kind == KIND_VSW;
+  int xk = 0;
+  for (int i = 0; i < a.nh; ++i) {
+    if (a.heads[i].pos != nullptr) xk |= kXkPos;
+    if (a.heads[i].kind == KIND_VSW) xk |= kXkWin;
+  }
   AttnLaunch c = a;
   c.xcd_sync = nullptr;
   c.rounds_flag = nullptr;
-  if (a.xcd_sync != nullptr && a.rounds_flag != nullptr && rounds_supported(posm)) {
+  if (a.xcd_sync != nullptr && a.rounds_flag != nullptr && rounds_supported(xk)) {
     // the rounds launch, then the ordinary one; the device-side flag lets exactly one of them work
     AttnLaunch b = a;
     b.rounds = (int)((chunks + kXcds - 1) / kXcds);
@@ -924,17 +936,19 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     void* args[] = {&b};
-    const void* fn = posm ? (const void*)attn_kernel_rounds<true> : (const void*)attn_kernel_rounds<false>;
-    e = hipLaunchCooperativeKernel(fn, dim3(kXcds * kChunk), dim3(kThreads), args, 0, stream);
+    e = hipLaunchCooperativeKernel(rounds_kernel_of(xk), dim3(kXcds * kChunk), dim3(kThreads), args, 0, stream);
     if (e == hipSuccess)
       c.rounds_flag = a.rounds_flag;
     else
       (void)hipGetLastError();  // not launchable cooperatively here: the ordinary launch does all the work
   }
-  if (posm)
-    hipLaunchKernelGGL(attn_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, c);
-  else
-    hipLaunchKernelGGL(attn_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, c);
+  const dim3 g((unsigned)grid), t(kThreads);
+  switch (xk) {
+    case 1: hipLaunchKernelGGL(attn_kernel<1>, g, t, 0, stream, c); break;
+    case 2: hipLaunchKernelGGL(attn_kernel<2>, g, t, 0, stream, c); break;
+    case 3: hipLaunchKernelGGL(attn_kernel<3>, g, t, 0, stream, c); break;
+    default: hipLaunchKernelGGL(attn_kernel<0>, g, t, 0, stream, c); break;
+  }
   return hipGetLastError();
 }
 
