@@ -1,13 +1,15 @@
 // Slash-aligned windows of the Vertical-Slash pattern for gfx950.
 //
-// What is computed (MInference 1.0 article, "Method": slash lines are computed
-// as dense key ranges rather than individual diagonals; the talk transcript
-// describes this as index shifting, which turns slashes into dense blocks):
-// for query block b (rows 64b .. 64b + 63) each selected diagonal offset dl
-// contributes the 64 keys [64b - dl, 64b - dl + 64), the keys the slash meets
-// from the block's rows, as one window, instead of the two 64x64 grid blocks
-// the slash crosses. The mask of row i is j <= i and (j in a window of its
-// block or j a vertical column).
+// What is computed (talk transcript, MMInference part on the permutation
+// details: shifting indices, i.e. reading with skipped rows or columns,
+// rearranges vertical and slash lines into dense regions; the plainest
+// reading for a slash is used here): for query block b (rows 64b .. 64b + 63)
+// each selected diagonal offset dl contributes the 64 keys
+// [64b - dl, 64b - dl + 64) -- the keys the slash meets from the block's 64
+// rows, which are one contiguous range -- as one window computed as a dense
+// 64x64 tile, instead of the one or two grid blocks the slash crosses. The
+// mask of row i is j <= i and (j in a window of its block or j a vertical
+// column).
 //
 // Preparation per head, three stream-ordered launches:
 //  * the bitmap of the offsets over [0, n) (cleared, then set);
