@@ -167,11 +167,11 @@ minf_status minf_block_pool(const void* x, int64_t n, int h_total, int d, const 
  *   MINF_KIND_VS_WINDOW : j <= i and (j in W(b) or j in v_idx), where W(b) is
  *                      the union over dl in s_idx with 64b + 63 - dl >= 0 of the
  *                      keys [64b - dl, 64b - dl + 64): each slash line as the
- *                      64-key window it meets from the block's rows, shifted
- *                      to start at the block's first row, rather than the grid
- *                      blocks it crosses (a reading of the index shifting in
- *                      the talk transcript's MMInference part). Same v_idx /
- *                      s_idx / k_v / k_s fields as MINF_KIND_VS.
+ *                      contiguous 64 keys it meets from the block's rows,
+ *                      rather than the grid blocks it crosses (a reading of
+ *                      the index shifting in the talk transcript's MMInference
+ *                      part). Same v_idx / s_idx / k_v / k_s fields as
+ *                      MINF_KIND_VS.
  * O_i = softmax over that set of scale * q_i . k_j, applied to V (fp32
  * online softmax and accumulation, bf16 MFMA products, bf16 output). An
  * empty set gives O_i = 0 and LSE_i = -inf.
