@@ -392,14 +392,23 @@ size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
 // sharing K/V tiles through L2 (at 1M tokens on literal data this cuts the
 // attention's HBM reads from ~34 TB to ~3 TB); the ordinary launch when they
 // are short, because its hardware dispatch balances the load better.
-// MINF_ATTN_ROUNDS=0 in the environment (read on every call) keeps the
-// ordinary launch only; both give bitwise-identical results.
+// MINF_ATTN_ROUNDS=0 in the environment (read on every call), or a stream in
+// graph capture, keeps the ordinary launch only; both give bitwise-identical
+// results.
 constexpr int64_t kRoundsMinTokens = 1 << 19;
 constexpr int kRoundsMinTiles = 1024;
 
-static bool rounds_enabled() {
+static bool rounds_enabled(hipStream_t stream) {
   const char* e = getenv("MINF_ATTN_ROUNDS");
-  return e == nullptr || e[0] != '0';
+  if (e != nullptr && e[0] == '0') return false;
+  // a stream being captured into a graph gets the ordinary launch only (a
+  // cooperative launch is not something every runtime can record)
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs == hipStreamCaptureStatusNone;
 }
 
 static minf_status check_attn_common(const void* q, const void* k, const void* v, void* o, int64_t n, int hq,
@@ -605,7 +614,7 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
     a.hgroup = hg;
     a.xcd_sync = nullptr;
     a.rounds_flag = nullptr;
-    if ((!launch_bits.empty() || !launch_wcount.empty()) && n >= kRoundsMinTokens && rounds_enabled()) {
+    if ((!launch_bits.empty() || !launch_wcount.empty()) && n >= kRoundsMinTokens && rounds_enabled(stream)) {
       int32_t* flag = sync_ws + 8;
       hipError_t e = launch_rounds_flag(launch_bits.data(), (int)launch_bits.size(), launch_wcount.data(),
                                         (int)launch_wcount.size(), (int)n, kRoundsMinTiles, flag, stream);

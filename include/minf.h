@@ -216,7 +216,7 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
  * work items in rounds that start together (long items share K/V tiles in
  * L2) or as one ordinary launch; results are bitwise identical either way.
  * The environment variable MINF_ATTN_ROUNDS=0 (read on every call) keeps the
- * ordinary launch only. The rounds launch is cooperative; where the device
+ * ordinary launch only, as does a stream that is being captured into a graph. The rounds launch is cooperative; where the device
  * refuses it, the ordinary launch does the work. */
 
 /* A BLOCK plan with pos != NULL describes a permuted sequence (q, k, v, o

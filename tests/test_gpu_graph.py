@@ -100,3 +100,33 @@ def test_prefill_step_graph_replay(gpu_lib):
     q2 = (q.float() * 0.5).to(torch.bfloat16)
     _replays(g, (vi, si, bi, bc, o, lse), want,
              lambda: gpu_lib.minf_sparse_attn(q2, k, v, [dict(kind="dense")] * hq, scale=SCALE))
+
+
+def test_long_vs_launch_graph_replay(gpu_lib):
+    # 2^19 tokens with VS heads: eagerly the XCD-round cooperative launch may run; under
+    # capture the library keeps the ordinary launch; the results are bitwise identical
+    n, hq = 1 << 19, 2
+    print(f"[case] long VS graph n={n} hq={hq}", flush=True)
+    q, k, v, _ = planted_qkv(n, hq, 1, seed=73, device="cuda")
+    g_ = torch.Generator().manual_seed(74)
+    plans = []
+    for _ in range(hq):
+        si = torch.randperm(n, generator=g_)[:3000].sort().values.to(torch.int32).cuda()
+        vi = torch.randperm(n, generator=g_)[:200].sort().values.to(torch.int32).cuda()
+        plans.append(dict(kind="vs", v_idx=vi, s_idx=si))
+    lib = gpu_lib.library()
+    ws = torch.empty(lib.minf_sparse_attn_workspace_size(n, hq), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+
+    def step():
+        gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE, out=o, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    want = (o.clone(), lse.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    _replays(g, (o, lse), want, lambda: None)
