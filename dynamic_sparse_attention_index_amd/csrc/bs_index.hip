@@ -147,21 +147,37 @@ __global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) 
         for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(qa[i], kb[j], acc[i][j]);
     }
   }
+  // permuted sequences: a key block whose earliest original position is after
+  // the query block's latest is stored as the all-ones pattern, whose sortable
+  // key is 0 (not a candidate), so the top-k needs no position loads
+  int cmin[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + 64 * h + 4 * tx + j;
+      cmin[h][j] = (!causal && c < a.nb) ? a.blkmin[c] : 0;
+    }
+  const float not_eligible = __builtin_bit_cast(float, 0xffffffffu);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int b = b0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + i - 4);
     if (b >= a.nb || b >= a.r0 + a.rows) continue;
     float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
     const int clim = causal ? b : a.nb - 1;  // last column stored
+    const int bmax = causal ? 0 : a.blkmax[b];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      float v4[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v4[j] = (!causal && cmin[h][j] > bmax) ? not_eligible : acc[i][4 * h + j];
       const int c = c0 + 64 * h + 4 * tx;
       if (c + 3 <= clim && (a.nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
-        *(float4*)(row + c) = float4{acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]};
+        *(float4*)(row + c) = float4{v4[0], v4[1], v4[2], v4[3]};
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (c + j <= clim) row[c + j] = acc[i][4 * h + j];
+          if (c + j <= clim) row[c + j] = v4[j];
       }
     }
   }
@@ -171,7 +187,8 @@ constexpr int kTopkCap = 1024;  // compacted candidates of the pre-filtered top-
 
 // Top-k_b key blocks of every query block of the round, from the stored scores.
 // Causal: the candidates are c <= b. Permuted: every c whose earliest original
-// position is not after the query block's latest one. One workgroup per row;
+// position is not after the query block's latest one (the score kernel stored
+// the others as the all-ones pattern, sortable key 0). One workgroup per row;
 // candidate c = 256 i + tid is held as sortable key k[i] in registers (0 for
 // an ineligible block) for the exact register top-k (ties to the lower id).
 // Long rows (PER >= 16, k_b <= 256) are first narrowed: each wave takes the
@@ -199,27 +216,23 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   const bool causal = a.blkmin == nullptr;
   const int ncand = causal ? b + 1 : a.nb;
   const float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
-  const int hi = causal ? 0 : a.blkmax[b];
   // all loads first (addresses clamped into the row), then the keys
   float sv[PER];
-  int mv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = 256 * i + tid < a.nb ? 256 * i + tid : a.nb - 1;
     sv[i] = 0.f;
-    mv[i] = 0;
-    if (256 * i < ncand) {
-      sv[i] = row[c];
-      if (!causal) mv[i] = a.blkmin[c];
-    }
+    if (256 * i < ncand) sv[i] = row[c];
   }
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = 256 * i + tid;
-    const bool e = c < ncand && (causal || mv[i] <= hi);
     const uint32_t u = sortable_key(sv[i]);
-    key[i] = e ? (u > 0u ? u : 1u) : 0u;  // an eligible key is never 0, even for a NaN score
+    // an eligible key is never 0, even for a NaN score; the stored all-ones pattern marks an
+    // ineligible block of a permuted sequence (tested on the bits, before any arithmetic)
+    const bool marked = !causal && __builtin_bit_cast(uint32_t, sv[i]) == 0xffffffffu;
+    key[i] = (c < ncand && !marked) ? (u > 0u ? u : 1u) : 0u;
   }
   int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
   int keep = -1;
