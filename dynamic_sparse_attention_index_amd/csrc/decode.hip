@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kCombRows * kHeadDim) void decode_combine_kernel(co
   red_m[threadIdx.x] = mm;
   __syncthreads();
   for (int off = kCombRows * kHeadDim / 2; off > 0; off >>= 1) {
-    if (threadIdx.x < off) red_m[threadIdx.x] = fmaxf(red_m[threadIdx.x], red_m[threadIdx.x + off]);
+    if ((int)threadIdx.x < off) red_m[threadIdx.x] = fmaxf(red_m[threadIdx.x], red_m[threadIdx.x + off]);
     __syncthreads();
   }
   mm = red_m[0];
