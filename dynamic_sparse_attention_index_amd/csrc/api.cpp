@@ -181,7 +181,7 @@ minf_status check_vs_args(const void* q, const void* k, int64_t n, int hq, int h
 
 // ---------------- BS workspace
 struct BsWs {
-  float *qbar, *kbar_t, *scores;
+  float *qbar_t, *kbar_t, *scores;
   int32_t *blkmin, *blkmax;
   int rows;
   size_t bytes;
@@ -191,7 +191,7 @@ BsWs carve_bs(void* base, int64_t n, int hkv, int n_heads) {
   Carver c{(char*)base};
   const size_t nb = (size_t)nblocks(n);
   BsWs w;
-  w.qbar = c.take<float>((size_t)std::max(n_heads, 1) * nb * kHeadDim);
+  w.qbar_t = c.take<float>((size_t)std::max(n_heads, 1) * nb * kHeadDim);
   w.kbar_t = c.take<float>((size_t)std::max(std::min(hkv, std::max(n_heads, 1)), 1) * nb * kHeadDim);
   w.rows = block_score_rows((int)nb, std::max(std::min(n_heads, 64), 1));
   w.scores = c.take<float>((size_t)std::max(std::min(n_heads, 64), 1) * w.rows * nb);
@@ -307,13 +307,13 @@ static minf_status build_block_index(const void* q, const void* k, int64_t n, in
   std::vector<int32_t> kv_slots(kv_heads.size());
   for (size_t i = 0; i < kv_heads.size(); ++i) kv_slots[i] = (int32_t)i;
   const int nb = (int)nblocks(n);
-  hipError_t e = launch_block_pool((const uint16_t*)q, (int)n, heads, q_slots.data(), n_heads, w.qbar, nullptr, stream);
+  hipError_t e = launch_block_pool((const uint16_t*)q, (int)n, heads, q_slots.data(), n_heads, nullptr, w.qbar_t, stream);
   if (e == hipSuccess)
     e = launch_block_pool((const uint16_t*)k, (int)n, kv_heads.data(), kv_slots.data(), (int)kv_heads.size(),
                           nullptr, w.kbar_t, stream);
   if (e == hipSuccess && pos) e = launch_block_minmax(pos, (int)n, w.blkmin, w.blkmax, stream);
   if (e == hipSuccess)
-    e = launch_block_topk(w.qbar, w.kbar_t, kv_slot.data(), n_heads, nb, k_b, blk_idx, blk_cnt, w.scores, w.rows,
+    e = launch_block_topk(w.qbar_t, w.kbar_t, kv_slot.data(), n_heads, nb, k_b, blk_idx, blk_cnt, w.scores, w.rows,
                           pos ? w.blkmin : nullptr, pos ? w.blkmax : nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "block index kernels");
   return MINF_OK;

@@ -9,11 +9,12 @@
 // Layout of the work:
 //  * pooling: one workgroup per (head, 64-row block); 16 threads span a row
 //    with 16-byte loads, fp32 sums in a fixed order. K is pooled once per KV
-//    head, into a [d][n_b] layout so that the score pass reads it coalesced.
-//  * scores: 64 x 64 tiles of the lower triangle (query blocks x key blocks)
-//    staged through LDS, so every pooled vector is read once per tile rather
-//    than once per query block; each score is a fixed-order fp32 dot product,
-//    written to a score buffer that holds a bounded band of rows at a time;
+//    head; both go to [d][n_b] layouts, which the score pass reads coalesced.
+//  * scores: 128 x 128 tiles of the lower triangle (query blocks x key blocks)
+//    on the fp32 matrix cores (the pooled product is a dense contraction), Q
+//    and K pooled into [d][n_b] layouts so that the operands are coalesced;
+//    each score is a fixed-order fp32 dot product, written to a score buffer
+//    that holds a bounded band of rows at a time;
 //  * top-k: one workgroup per (head, query block); the row's scores are held
 //    in registers (up to 64 per thread) for an exact bitwise search.
 #include <algorithm>
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const PoolLaunch a) {
 }
 
 struct BsTopkLaunch {
-  const float* qbar;    // [nh][nb][128]
+  const float* qbar_t;  // [nh][128][nb]
   const float* kbar_t;  // [nkv][128][nb]
   float* scores;        // [nh][rows][nb]: rows r0 .. r0 + rows - 1 of this round
   int32_t* blk_idx;     // [nh][nb][k_b]
@@ -90,96 +91,144 @@ struct BsTopkLaunch {
 
 static_assert(kMaxTokens / kBlock <= 256 * 64, "the top-k holds at most 64 candidates per thread");
 constexpr int kTile = 128;  // query blocks x key blocks per score workgroup
-constexpr int kDChunk = 32;  // pooled dimensions staged in LDS at a time
+constexpr int kSteps = 8;   // contraction steps per register batch (2 x 32 loads in flight)
+constexpr int kBufDword3 = 0x00020000;
+constexpr int kStagePitch = 68;  // floats per staged score row (64 + 4 against bank conflicts)  // buffer resource word 3 on gfx9 (32-bit data format)
 
-// Pooled scores of one 128 x 128 tile (query blocks x key blocks): each output
-// is a fixed-order fp32 dot product over d = 0..127 (d ascending across the
-// staged chunks). Thread (ty, tx) owns query blocks {4ty + i, 64 + 4ty + i}
-// and key blocks {4tx + j, 64 + 4tx + j}, i, j < 4: 64 accumulators, and the
-// four float4 LDS reads per d hit consecutive addresses across the wave.
-__global__ __launch_bounds__(256) void block_score_kernel(const BsTopkLaunch a) {
-  __shared__ __attribute__((aligned(16))) float qs[kDChunk][kTile];
-  __shared__ __attribute__((aligned(16))) float ks[kDChunk][kTile];
+// Pooled scores of one 128 x 128 tile (query blocks x key blocks) on the fp32
+// matrix cores. Wave w computes the 64 x 64 sub-tile at query blocks
+// 64 (w >> 1) and key blocks 64 (w & 1) of the tile as 2 x 2 products of
+// v_mfma_f32_32x32x2_f32. Step s of the contraction takes dimension
+// 2s + (lane >> 5): lane l supplies Qbar[row l & 31][2s + (l >> 5)] and
+// Kbar[column l & 31][2s + (l >> 5)], read from the [d][n_b] layouts (128
+// consecutive bytes per half-wave). Each score is an fp32 sum of the 128
+// products in a fixed order, so repeated calls agree bitwise.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void block_score_kernel(
+    const BsTopkLaunch a) {
   const int ct = blockIdx.x;
   const int bt = a.r0 / kTile + (int)blockIdx.z;
   const bool causal = a.blkmin == nullptr;
-  if (causal && ct > bt) return;  // above the block diagonal
+  const int nb = a.nb;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int rb = bt * kTile + 64 * (w >> 1);  // first query block of the wave
+  const int cb = ct * kTile + 64 * (w & 1);   // first key block of the wave
+  const int row_end = min(nb, a.r0 + a.rows);
+  if (rb >= row_end || cb >= nb) return;
+  if (causal && cb > rb + 63) return;  // above the block diagonal
   const int hs = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int b0 = bt * kTile, c0 = ct * kTile;
-  const int ty = tid >> 4, tx = tid & 15;
-  float acc[8][8];
+  const int half = lane >> 5, col = lane & 31;
+  __shared__ __attribute__((aligned(16))) float score_stage[4][32 * kStagePitch];
+  // the head's pooled rows as buffer resources (2 n_b * 4 * 64 bytes <= 8 MiB):
+  // per-lane 32-bit byte offsets of row `half`, column = the lane's block (rows
+  // and columns past n_b read the last block; their scores are not stored), and
+  // a uniform offset per contraction step
+  const uint32_t bytes = (uint32_t)kHeadDim * nb * 4u;
+  const __amdgpu_buffer_rsrc_t qr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.qbar_t + (size_t)hs * kHeadDim * nb), 0, bytes, kBufDword3);
+  const __amdgpu_buffer_rsrc_t kr =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.kbar_t + (size_t)a.kvslot[hs] * kHeadDim * nb), 0, bytes,
+                                        kBufDword3);
+  const int qo[2] = {(half * nb + min(rb + col, nb - 1)) * 4, (half * nb + min(rb + 32 + col, nb - 1)) * 4};
+  const int ko[2] = {(half * nb + min(cb + col, nb - 1)) * 4, (half * nb + min(cb + 32 + col, nb - 1)) * 4};
+  // permuted sequences: the earliest original position of each key block this
+  // lane stores, loaded now so that the stores do not wait for it
+  const int c4 = cb + 4 * (lane & 15);  // first of the 4 key blocks this lane stores
+  int cmin[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int e = 0; e < 4; ++e) cmin[e] = causal ? 0 : a.blkmin[min(c4 + e, nb - 1)];
+  f32x16 acc[2][2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
-  // staging roles: query row r = tid / 2 (16 dims each), key dim kd = tid / 8 (16 blocks each)
-  const int qr = tid >> 1, qpart = (tid & 1) * 16;
-  const bool qok = b0 + qr < a.nb;
-  const float* qsrc = a.qbar + ((size_t)hs * a.nb + (qok ? b0 + qr : 0)) * kHeadDim + qpart;
-  const int kd = tid >> 3, kc = (tid & 7) * 16;
-  const float* ksrc = a.kbar_t + (size_t)a.kvslot[hs] * kHeadDim * a.nb + c0 + kc;
-  for (int dc = 0; dc < kHeadDim; dc += kDChunk) {
-    if (dc) __syncthreads();  // the previous chunk has been read
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      const float4 x = qok ? *(const float4*)(qsrc + dc + e) : float4{0.f, 0.f, 0.f, 0.f};
-      qs[qpart + e][qr] = x.x;
-      qs[qpart + e + 1][qr] = x.y;
-      qs[qpart + e + 2][qr] = x.z;
-      qs[qpart + e + 3][qr] = x.w;
-    }
-    const float* kp = ksrc + (size_t)(dc + kd) * a.nb;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ks[kd][kc + e] = c0 + kc + e < a.nb ? kp[e] : 0.f;
-    __syncthreads();
-#pragma unroll 4
-    for (int d = 0; d < kDChunk; ++d) {
-      const float4 q0 = *(const float4*)&qs[d][4 * ty];
-      const float4 q1 = *(const float4*)&qs[d][64 + 4 * ty];
-      const float4 k0 = *(const float4*)&ks[d][4 * tx];
-      const float4 k1 = *(const float4*)&ks[d][64 + 4 * tx];
-      const float qa[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      const float kb[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  // two register batches in ping-pong: batch B loads while A is multiplied, then
+  // A reloads while B is multiplied (no register copies, so no early waits)
+  float aq[2][kSteps], ak[2][kSteps], bq[2][kSteps], bk[2][kSteps];
+  auto load = [&](int s0, float (&lq)[2][kSteps], float (&lk)[2][kSteps]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int e = 0; e < kSteps; ++e) {
+      const int so = 2 * (s0 + e) * nb * 4;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(qa[i], kb[j], acc[i][j]);
-    }
-  }
-  // permuted sequences: a key block whose earliest original position is after
-  // the query block's latest is stored as the all-ones pattern, whose sortable
-  // key is 0 (not a candidate), so the top-k needs no position loads
-  int cmin[2][4];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + 64 * h + 4 * tx + j;
-      cmin[h][j] = (!causal && c < a.nb) ? a.blkmin[c] : 0;
-    }
-  const float not_eligible = __builtin_bit_cast(float, 0xffffffffu);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int b = b0 + (i < 4 ? 4 * ty + i : 64 + 4 * ty + i - 4);
-    if (b >= a.nb || b >= a.r0 + a.rows) continue;
-    float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
-    const int clim = causal ? b : a.nb - 1;  // last column stored
-    const int bmax = causal ? 0 : a.blkmax[b];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float v4[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v4[j] = (!causal && cmin[h][j] > bmax) ? not_eligible : acc[i][4 * h + j];
-      const int c = c0 + 64 * h + 4 * tx;
-      if (c + 3 <= clim && (a.nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
-        *(float4*)(row + c) = float4{v4[0], v4[1], v4[2], v4[3]};
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (c + j <= clim) row[c + j] = v4[j];
+      for (int i = 0; i < 2; ++i) {
+        lq[i][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(qr, qo[i], so, 0));
+        lk[i][e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kr, ko[i], so, 0));
       }
     }
+  };
+  auto mul = [&](const float (&lq)[2][kSteps], const float (&lk)[2][kSteps]) {
+#pragma unroll
+    for (int e = 0; e < kSteps; ++e)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(lq[i][e], lk[j][e], acc[i][j], 0, 0, 0);
+  };
+  // the last round is peeled so that the loop has no branch (the wait counts
+  // then only cover the batch about to be multiplied); scheduling barriers keep
+  // each batch's loads issued before the other batch's products
+  constexpr int kLast = kHeadDim / 2 - 2 * kSteps;
+  static_assert(kLast % (2 * kSteps) == 0 && kLast > 0, "whole ping-pong rounds");
+  load(0, aq, ak);
+#pragma unroll 1
+  for (int s0 = 0; s0 < kLast; s0 += 2 * kSteps) {
+    load(s0 + kSteps, bq, bk);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(aq, ak);
+    __builtin_amdgcn_sched_barrier(0);
+    load(s0 + 2 * kSteps, aq, ak);
+    __builtin_amdgcn_sched_barrier(0);
+    mul(bq, bk);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load(kLast + kSteps, bq, bk);
+  __builtin_amdgcn_sched_barrier(0);
+  mul(aq, ak);
+  mul(bq, bk);
+  // accumulator v of lane l holds query block 32 i + (v & 3) + 8 (v >> 2) + 4 (l >> 5)
+  // and key block 32 j + (l & 31) of the sub-tile. The stores go through LDS,
+  // 32 rows at a time, so that each lane writes 4 consecutive scores of a row
+  // (a store instruction covers 256 contiguous bytes of 4 rows).
+  // Permuted sequences: a key block whose earliest original position is after
+  // the query block's latest is stored as the all-ones pattern, whose sortable
+  // key is 0 (not a candidate), so the top-k needs no position loads.
+  const float not_eligible = __builtin_bit_cast(float, 0xffffffffu);
+  float* t = score_stage[w];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) t[((v & 3) + 8 * (v >> 2) + 4 * half) * kStagePitch + 32 * j + col] = acc[i][j][v];
+    __builtin_amdgcn_wave_barrier();  // LDS accesses of a wave complete in order
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = (lane >> 4) + 4 * k;  // row within this half of the sub-tile
+      const int r = 32 * i + rr;
+      const int bmax = causal ? 0 : a.blkmax[min(rb + r, nb - 1)];  // uniform branch
+      const int b = rb + r;
+      if (b >= row_end) continue;
+      float4 x = *(const float4*)&t[rr * kStagePitch + 4 * (lane & 15)];
+      if (!causal) {
+        x.x = cmin[0] > bmax ? not_eligible : x.x;
+        x.y = cmin[1] > bmax ? not_eligible : x.y;
+        x.z = cmin[2] > bmax ? not_eligible : x.z;
+        x.w = cmin[3] > bmax ? not_eligible : x.w;
+      }
+      const int clim = causal ? b : nb - 1;  // last column stored
+      float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * nb;
+      if (c4 + 3 <= clim && (nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
+        *(float4*)(row + c4) = x;
+      } else {
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c4 + e <= clim) row[c4 + e] = xs[e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();  // the next half overwrites the staging rows
   }
 }
 
@@ -384,14 +433,14 @@ hipError_t launch_permute_rows(const void* x, void* out, int heads, int64_t n, i
   return hipGetLastError();
 }
 
-hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
+hipError_t launch_block_topk(const float* qbar_t, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
                              int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
                              const int32_t* blkmin, const int32_t* blkmax, hipStream_t stream) {
   const int nbt = (nb + kTile - 1) / kTile;
   for (int base = 0; base < n_heads; base += kMaxPoolHeads) {
     const int c = n_heads - base < kMaxPoolHeads ? n_heads - base : kMaxPoolHeads;
     BsTopkLaunch a{};
-    a.qbar = qbar + (size_t)base * nb * kHeadDim;
+    a.qbar_t = qbar_t + (size_t)base * nb * kHeadDim;
     a.kbar_t = kbar_t;
     a.scores = scores;
     a.blk_idx = blk_idx;

@@ -137,10 +137,11 @@ inline int decode_topk_segments(int nb, int kb) {
 int decode_blocks_per_split(int kb, int rows);
 hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream);
-// Scores and top-k for n_heads pooled query heads (qbar slots 0..n_heads-1), head i
-// reading pooled keys kbar_t slot kvslot[i]; writes blk_idx/blk_cnt slot i.
+// Scores and top-k for n_heads pooled query heads (qbar_t slots 0..n_heads-1, each
+// [128][nb]), head i reading pooled keys kbar_t slot kvslot[i] ([128][nb]); writes
+// blk_idx/blk_cnt slot i.
 int block_score_rows(int nb, int n_heads);
-hipError_t launch_block_topk(const float* qbar, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
+hipError_t launch_block_topk(const float* qbar_t, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
                              int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
                              const int32_t* blkmin, const int32_t* blkmax, hipStream_t stream);
 // Per-block min / max of the original positions of a permuted sequence.

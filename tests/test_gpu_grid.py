@@ -88,7 +88,7 @@ def test_permute_rows_roundtrip(gpu_lib):
     assert torch.equal(gpu_lib.minf_permute_rows(y.unsqueeze(-1).contiguous(), src).squeeze(-1), y[:, src.long()])
 
 
-@pytest.mark.parametrize("frames,patches,k_b", [(64, 64, 2), (40, 50, 3)])
+@pytest.mark.parametrize("frames,patches,k_b", [(64, 64, 2), (40, 50, 3), (120, 130, 6)])
 def test_grid_layer_matches_oracle(gpu_lib, frames, patches, k_b):
     print(f"[case] grid F={frames} P={patches} k_b={k_b}", flush=True)
     q, k, v = grid_qkv(frames, patches, 4, 2, device="cuda")

@@ -119,6 +119,35 @@ def test_block_index_and_attention(gpu_lib, n, k_b):
     _attn_parity(gpu_lib, q, k, v, plans)
 
 
+@pytest.mark.parametrize("n,k_b", [(64 * 300 + 17, 20), (64 * 129, 128)])
+def test_block_index_multi_tile(gpu_lib, n, k_b):
+    # several 128 x 128 score tiles with a ragged last block; every row checked
+    print(f"[case] block index n={n} k_b={k_b}", flush=True)
+    hq, hkv = 4, 2
+    q, k, v, _ = _qkv(n, hq, hkv, 18)
+    heads = [0, 3]
+    bi, bc = gpu_lib.minf_build_block_index(q, k, heads, k_b=k_b)
+    torch.cuda.synchronize()
+    wi, wc, scores = O.build_block_index(to_np(q), to_np(k), hq, hkv, heads, k_b)
+    assert np.array_equal(bc.cpu().numpy(), wc)
+    qn, kn = to_np(q), to_np(k)
+    exact = amb = 0
+    for t, h in enumerate(heads):
+        qbar = O.pool_blocks(qn[h])
+        kabs = np.abs(O.pool_blocks(kn[h // 2]))
+        bi_h = bi[t].cpu().numpy()
+        for b in range(wi.shape[1]):
+            c = int(wc[t, b])
+            abs_tol = 1e-5 * float(np.abs(qbar[b]) @ kabs[: b + 1].max(axis=0))
+            if check_topk(scores[t][b, : b + 1], bi_h[b, :c], k_b, abs_tol=abs_tol, want=wi[t, b, :c]):
+                exact += 1
+            else:
+                amb += 1
+            assert (bi_h[b, c:] == -1).all()
+    print(f"  block rows exact {exact}, ambiguous {amb}")
+    assert exact > amb
+
+
 def test_block_pool(gpu_lib):
     n = 64 * 7 + 9
     q, k, v, _ = _qkv(n, 3, 3, 16)
