@@ -30,7 +30,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int KSTR = 136;
-constexpr int PSTR = 65;   // floats per probability-tile row in LDS
+constexpr int PSTR = 64;   // floats per probability-tile row in LDS (rows stored skewed)
 constexpr int PROWS = 32;  // query rows of the probability tile staged at a time
 
 struct VsSmem1 {
@@ -154,9 +154,11 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
       }
     }
     if constexpr (PASS == 2) {
-      // normalised probabilities, staged 32 query rows at a time; the column sum
-      // (lane = key) and the diagonal partials (lane = e, e + 64 with e = t - c + 63)
-      // run over t in ascending order across the two halves
+      // normalised probabilities, staged 32 query rows at a time with row t
+      // rotated by t, so that every diagonal e = t - c + 63 of the tile lies in
+      // one LDS column; the column sum (lane = key) and the diagonal partials
+      // (lane = column s: diagonals 63 - s and 127 - s) run over t in ascending
+      // order across the two halves, each a 32-step loop with no divergence
       float* pt = sm.pt[wave];
       float cs = 0.f;
       float ds[2] = {0.f, 0.f};
@@ -183,35 +185,38 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
               const int64_t j = (int64_t)T * kBlock + kx;
               const bool ok = row_ok && (!edge || j <= iq);
               const float pv = ok ? fast_exp2(fmaf(s[mt][i], sl2, -rm[nt])) * ril[nt] : 0.f;
-              pt[r32 * PSTR + kx] = pv;
+              pt[r32 * PSTR + ((kx - t) & 63)] = pv;
             }
         }
-        __syncthreads();
+        // pt is private to the wave and a wave's LDS accesses complete in order:
+        // no workgroup barrier around its staging
+        __builtin_amdgcn_wave_barrier();
         if (active) {
-#pragma unroll 8
-          for (int tl = 0; tl < PROWS; ++tl) cs += pt[tl * PSTR + lane];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const int e = lane + 64 * h2;
-            if (e < 127) {
-              int tlo = e - 63 > 32 * nt ? e - 63 : 32 * nt;
-              int thi = e < 32 * nt + 31 ? e : 32 * nt + 31;
-              for (int t = tlo; t <= thi; ++t) ds[h2] += pt[(t - 32 * nt) * PSTR + (t - e + 63)];
-            }
+          // row t holds key c at column (c - t) mod 64: key `lane` of row t is at
+          // (lane - t) mod 64, and column s holds diagonal 63 - s for t < 64 - s
+          // and diagonal 127 - s after (c = s + t, resp. s + t - 64)
+#pragma unroll 4
+          for (int tl = 0; tl < PROWS; ++tl) {
+            const int t = 32 * nt + tl;
+            cs += pt[tl * PSTR + ((lane - t) & 63)];
+            const float x = pt[tl * PSTR + lane];
+            if (t < 64 - lane)
+              ds[0] += x;
+            else
+              ds[1] += x;
           }
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();  // the next half overwrites pt
       }
       if (active) {
         const int64_t j = (int64_t)T * kBlock + lane;
         if (j < n) a.vcol[(size_t)slot * n + j] = cs;
         float* dp = a.dpart + ((size_t)slot * a.ntiles + T) * 128;
-        dp[lane] = ds[0];
-        dp[lane + 64] = ds[1];
+        dp[63 - lane] = ds[0];
+        dp[127 - lane] = ds[1];
       }
-    } else {
-      __syncthreads();  // every wave is done with this K tile
     }
+    __syncthreads();  // every wave is done with this K tile
     if (T + 1 < t1) {
       store_tile();
       __syncthreads();
