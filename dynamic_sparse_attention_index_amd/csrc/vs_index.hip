@@ -32,6 +32,8 @@ constexpr int kThreads = 256;
 constexpr int KSTR = 136;
 constexpr int PSTR = 64;   // floats per probability-tile row in LDS (rows stored skewed)
 constexpr int PROWS = 32;  // query rows of the probability tile staged at a time
+// s_waitcnt immediate on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVmem0 = 0x0F70;
 
 struct VsSmem1 {
   uint16_t kt[kBlock * KSTR];
@@ -105,6 +107,9 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
     load_tile(t0);
     store_tile();
   }
+  // the query operands (and the row statistics) have arrived on every path
+  // into the loop, so that the loop's wait counts only cover the next K tile
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
   for (int T = t0; T < t1; ++T) {
     if (T + 1 < t1) load_tile(T + 1);
