@@ -610,6 +610,9 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     // VS windows: tiles start at any key; e0 / e1 end the tile's interval for b0 / b1
     const bool vsw = (XK & kXkWin) && hd.kind == KIND_VSW;
     int e0_cur = 0, e1_cur = 0, e0_nxt = 0, e1_nxt = 0;
+    // permuted sequences: the latest original position of the tile's key block,
+    // loaded with the tile so that the visibility test does not wait for it
+    int bm_cur = 0, bm_nxt = 0;
     auto next_tile = [&](int& c, int& m, int& e0, int& e1) -> bool {
       if ((XK & kXkWin) && vsw) return it.next_window(c, m, e0, e1);
       return it.next(c, m);
@@ -635,11 +638,12 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
                     uint32_t* psn) -> bool {
       const bool hn = next_tile(c_nxt, m_nxt, e0_nxt, e1_nxt);
       if (hn) issue_tile(c_nxt, ktn, vtn, psn);
+      if ((XK & kXkPos) && posm && hn) bm_nxt = hd.blkmax[c_nxt];
       if (wave_on && ((m_cur >> qsel) & 1)) {
         int full, mask;
         int key0 = c_cur * kBlock, wend = hd.local;
-        if (posm) {
-          full = hd.blkmax[c_cur] <= wminpos;
+        if ((XK & kXkPos) && posm) {
+          full = bm_cur <= wminpos;
           mask = full ? MASK_NONE : MASK_POS;
         } else if ((XK & kXkWin) && vsw) {
           key0 = c_cur;
@@ -668,6 +672,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       m_cur = m_nxt;
       e0_cur = e0_nxt;
       e1_cur = e1_nxt;
+      bm_cur = bm_nxt;
       return hn;
     };
     // key-position slots of the two tile buffers (phase B, which uses clist, never runs on BLOCK heads)
@@ -675,6 +680,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     uint32_t* ps1 = sm.clist + kBlock;
     bool have = next_tile(c_cur, m_cur, e0_cur, e1_cur);
     if (have) issue_tile(c_cur, kt0, vt0, ps0);
+    if ((XK & kXkPos) && posm && have) bm_cur = hd.blkmax[c_cur];
     wait_vmem();
     __syncthreads();
     while (have) {
