@@ -240,13 +240,14 @@ constexpr int kTopkCap = 1024;  // compacted candidates of the pre-filtered top-
 // the others as the all-ones pattern, sortable key 0). One workgroup per row;
 // candidate c = 256 i + tid is held as sortable key k[i] in registers (0 for
 // an ineligible block) for the exact register top-k (ties to the lower id).
-// Long rows (PER >= 16, k_b <= 256) are first narrowed: each wave takes the
-// ceil(k_b / 4)-th largest of its 64 threads' maxima (a wave-only bitwise
-// search), and the smallest of the four, t0, has at least k_b keys >= it
-// (each wave has ceil(k_b / 4) threads whose maximum is >= t0). The keys >= t0
-// (typically ~2 k_b) are compacted into LDS in block order and the register
-// top-k runs over them; when they exceed kTopkCap the whole row is searched.
-template <int PER>
+// Long rows (PER >= 16, k_b <= 256) are first narrowed: each thread keeps its
+// 4 largest keys, each wave takes the ceil(k_b / 4)-th largest of those 256
+// (a wave-only bitwise search), and the smallest of the four, t0, has at least
+// k_b keys >= it (each wave holds ceil(k_b / 4) distinct keys >= t0). The keys
+// >= t0 (typically ~2 k_b) are compacted into LDS in block order and the
+// register top-k runs over them; when they exceed kTopkCap the whole row is
+// searched.
+template <int PER, bool PERM>
 __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   __shared__ uint64_t gmask[4 * PER];
   __shared__ uint64_t emask[4 * PER];
@@ -262,16 +263,21 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   const int hs = blockIdx.y;
   const int slot = a.outslot[hs];
   const int kb = a.k_b;
-  const bool causal = a.blkmin == nullptr;
+  const bool causal = !PERM;
   const int ncand = causal ? b + 1 : a.nb;
   const float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
-  // all loads first (addresses clamped into the row), then the keys
+  // all loads first, then the keys: the loads are unconditional (no branch for
+  // the compiler to sink the key arithmetic into, which would wait for every
+  // load in turn); a slot past the row's candidates reads a valid address near
+  // the row's start, whose value the key step discards
+  // (the row is uniform: 32-bit byte offsets from it, n_b * 4 < 2^32)
   float sv[PER];
+  const char* rowb = (const char*)row;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int c = 256 * i + tid < a.nb ? 256 * i + tid : a.nb - 1;
-    sv[i] = 0.f;
-    if (256 * i < ncand) sv[i] = row[c];
+    const uint32_t off = (uint32_t)(256 * i < ncand ? c : (tid < a.nb ? tid : a.nb - 1)) * 4u;
+    sv[i] = *(const float*)(rowb + off);
   }
   uint32_t key[PER];
 #pragma unroll
@@ -287,15 +293,33 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   int keep = -1;
   if constexpr (PER >= 16) {
     if (kb <= 256 && ncand > kTopkCap) {
-      // t0: the smallest of the waves' ceil(kb / 4)-th largest thread maxima
-      uint32_t tm = 0u;
+      // t0: the smallest of the waves' ceil(kb / 4)-th largest keys among their
+      // threads' largest key (causal rows) or 4 largest keys (permuted rows,
+      // whose eligible keys can sit in a few threads: a query block of an early
+      // frame chunk sees only the key blocks of chunks up to its own, which
+      // are the same few lanes of every wave)
+      uint32_t t1 = 0u, t2 = 0u, t3 = 0u, t4 = 0u;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) tm = key[i] > tm ? key[i] : tm;
+      for (int i = 0; i < PER; ++i) {
+        if constexpr (PERM) {
+          uint32_t x = key[i], y;
+          y = max(t1, x); x = min(t1, x); t1 = y;
+          y = max(t2, x); x = min(t2, x); t2 = y;
+          y = max(t3, x); x = min(t3, x); t3 = y;
+          t4 = max(t4, x);
+        } else {
+          t1 = max(t1, key[i]);
+        }
+      }
       const int kq = (kb + 3) >> 2;
       uint32_t tw = 0u;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tw | (1u << bit);
-        if ((int)__popcll(__ballot(tm >= cand)) >= kq) tw = cand;
+        int c = (int)__popcll(__ballot(t1 >= cand));
+        if constexpr (PERM)
+          c += (int)(__popcll(__ballot(t2 >= cand)) + __popcll(__ballot(t3 >= cand)) +
+                     __popcll(__ballot(t4 >= cand)));
+        if (c >= kq) tw = cand;
       }
       if (lane == 0) red[wave] = (int)tw;
       __syncthreads();
@@ -461,14 +485,16 @@ hipError_t launch_block_topk(const float* qbar_t, const float* kbar_t, const int
       const int col_tiles = blkmin ? nbt : std::min(nbt, (r0 + rows) / kTile);
       hipLaunchKernelGGL(block_score_kernel, dim3(col_tiles, c, row_tiles), dim3(256), 0, stream, a);
       const dim3 tg(std::min(rows, nb - r0), c);
+      auto topk = [&](auto kern) { hipLaunchKernelGGL(kern, tg, dim3(256), 0, stream, a); };
+      const bool perm = blkmin != nullptr;
       if (nb <= 256)
-        hipLaunchKernelGGL(block_topk_kernel<1>, tg, dim3(256), 0, stream, a);
+        perm ? topk(block_topk_kernel<1, true>) : topk(block_topk_kernel<1, false>);
       else if (nb <= 1024)
-        hipLaunchKernelGGL(block_topk_kernel<4>, tg, dim3(256), 0, stream, a);
+        perm ? topk(block_topk_kernel<4, true>) : topk(block_topk_kernel<4, false>);
       else if (nb <= 4096)
-        hipLaunchKernelGGL(block_topk_kernel<16>, tg, dim3(256), 0, stream, a);
+        perm ? topk(block_topk_kernel<16, true>) : topk(block_topk_kernel<16, false>);
       else
-        hipLaunchKernelGGL(block_topk_kernel<64>, tg, dim3(256), 0, stream, a);
+        perm ? topk(block_topk_kernel<64, true>) : topk(block_topk_kernel<64, false>);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
