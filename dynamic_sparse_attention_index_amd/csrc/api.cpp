@@ -183,6 +183,10 @@ minf_status check_vs_args(const void* q, const void* k, int64_t n, int hq, int h
 struct BsWs {
   float *qbar_t, *kbar_t, *scores;
   int32_t *blkmin, *blkmax;
+  // permuted sequences: the block orders (PermRankLaunch)
+  uint32_t *bits_min, *bits_max;
+  int32_t *pre_min, *pre_max, *rank_q, *rank_k, *tau, *sigma, *lrow;
+  int words;
   int rows;
   size_t bytes;
 };
@@ -197,6 +201,16 @@ BsWs carve_bs(void* base, int64_t n, int hkv, int n_heads) {
   w.scores = c.take<float>((size_t)std::max(std::min(n_heads, 64), 1) * w.rows * nb);
   w.blkmin = c.take<int32_t>(nb);
   w.blkmax = c.take<int32_t>(nb);
+  w.words = (int)((n + 31) / 32);
+  w.bits_min = c.take<uint32_t>((size_t)w.words);
+  w.bits_max = c.take<uint32_t>((size_t)w.words);
+  w.pre_min = c.take<int32_t>((size_t)w.words);
+  w.pre_max = c.take<int32_t>((size_t)w.words);
+  w.rank_q = c.take<int32_t>(nb);
+  w.rank_k = c.take<int32_t>(nb);
+  w.tau = c.take<int32_t>(nb);
+  w.sigma = c.take<int32_t>(nb);
+  w.lrow = c.take<int32_t>(nb);
   w.bytes = c.off;
   return w;
 }
@@ -307,14 +321,25 @@ static minf_status build_block_index(const void* q, const void* k, int64_t n, in
   std::vector<int32_t> kv_slots(kv_heads.size());
   for (size_t i = 0; i < kv_heads.size(); ++i) kv_slots[i] = (int32_t)i;
   const int nb = (int)nblocks(n);
-  hipError_t e = launch_block_pool((const uint16_t*)q, (int)n, heads, q_slots.data(), n_heads, nullptr, w.qbar_t, stream);
+  hipError_t e = hipSuccess;
+  // permuted sequences: rows (pooled query blocks) in latest-position order and
+  // columns (pooled key blocks) in earliest-position order, so that every row's
+  // eligible key blocks are its first columns
+  if (pos) {
+    e = launch_block_minmax(pos, (int)n, w.blkmin, w.blkmax, stream);
+    PermRankLaunch pr{w.blkmin, w.blkmax, w.bits_min, w.bits_max, w.pre_min, w.pre_max, w.rank_q,
+                      w.rank_k, w.tau, w.sigma, w.lrow, (int32_t)n, nb, w.words};
+    if (e == hipSuccess) e = launch_perm_ranks(pr, stream);
+  }
+  if (e == hipSuccess)
+    e = launch_block_pool((const uint16_t*)q, (int)n, heads, q_slots.data(), n_heads, nullptr, w.qbar_t, stream, 0,
+                          pos ? w.rank_q : nullptr);
   if (e == hipSuccess)
     e = launch_block_pool((const uint16_t*)k, (int)n, kv_heads.data(), kv_slots.data(), (int)kv_heads.size(),
-                          nullptr, w.kbar_t, stream);
-  if (e == hipSuccess && pos) e = launch_block_minmax(pos, (int)n, w.blkmin, w.blkmax, stream);
+                          nullptr, w.kbar_t, stream, 0, pos ? w.rank_k : nullptr);
   if (e == hipSuccess)
     e = launch_block_topk(w.qbar_t, w.kbar_t, kv_slot.data(), n_heads, nb, k_b, blk_idx, blk_cnt, w.scores, w.rows,
-                          pos ? w.blkmin : nullptr, pos ? w.blkmax : nullptr, stream);
+                          pos ? w.lrow : nullptr, pos ? w.sigma : nullptr, pos ? w.tau : nullptr, stream);
   if (e != hipSuccess) return hip_fail(e, "block index kernels");
   return MINF_OK;
 }

@@ -31,6 +31,7 @@ struct PoolLaunch {
   const uint16_t* x;
   float* out_rm;  // [nh][nb][128] or null
   float* out_t;   // [nh][128][nb] or null
+  const int32_t* col_map;  // block b goes to column col_map[b] (null: column b)
   int32_t n, nb, nh, b0;
   int32_t heads[kMaxPoolHeads];
   int32_t slots[kMaxPoolHeads];
@@ -70,8 +71,9 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const PoolLaunch a) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) s += part[q][tid];
     const float mean = s / (float)cnt;
-    if (a.out_rm) a.out_rm[((size_t)slot * a.nb + b) * kHeadDim + tid] = mean;
-    if (a.out_t) a.out_t[((size_t)slot * kHeadDim + tid) * a.nb + b] = mean;
+    const int col = a.col_map ? a.col_map[b] : b;
+    if (a.out_rm) a.out_rm[((size_t)slot * a.nb + col) * kHeadDim + tid] = mean;
+    if (a.out_t) a.out_t[((size_t)slot * kHeadDim + tid) * a.nb + col] = mean;
   }
 }
 
@@ -81,9 +83,11 @@ struct BsTopkLaunch {
   float* scores;        // [nh][rows][nb]: rows r0 .. r0 + rows - 1 of this round
   int32_t* blk_idx;     // [nh][nb][k_b]
   int32_t* blk_cnt;     // [nh][nb]
-  // permuted sequences: per-block min / max of the original positions (null: causal c <= b)
-  const int32_t* blkmin;
-  const int32_t* blkmax;
+  // permuted sequences (null: causal, row b's candidates are the key blocks c <= b): rows
+  // are query blocks by latest original position and columns key blocks by earliest one
+  const int32_t* lrow;   // [nb] candidates of row r: columns 0 .. lrow[r] - 1 (the eligible key blocks)
+  const int32_t* sigma;  // [nb] key block of column s
+  const int32_t* tau;    // [nb] query block of row r
   int32_t nb, k_b, nh, r0, rows;
   int32_t kvslot[kMaxPoolHeads];
   int32_t outslot[kMaxPoolHeads];
@@ -92,8 +96,8 @@ struct BsTopkLaunch {
 static_assert(kMaxTokens / kBlock <= 256 * 64, "the top-k holds at most 64 candidates per thread");
 constexpr int kTile = 128;  // query blocks x key blocks per score workgroup
 constexpr int kSteps = 8;   // contraction steps per register batch (2 x 32 loads in flight)
-constexpr int kBufDword3 = 0x00020000;
-constexpr int kStagePitch = 68;  // floats per staged score row (64 + 4 against bank conflicts)  // buffer resource word 3 on gfx9 (32-bit data format)
+constexpr int kBufDword3 = 0x00020000;  // buffer resource word 3 on gfx9 (32-bit data format)
+constexpr int kStagePitch = 68;  // floats per staged score row (64 + 4 against bank conflicts)
 
 // Pooled scores of one 128 x 128 tile (query blocks x key blocks) on the fp32
 // matrix cores. Wave w computes the 64 x 64 sub-tile at query blocks
@@ -107,14 +111,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     const BsTopkLaunch a) {
   const int ct = blockIdx.x;
   const int bt = a.r0 / kTile + (int)blockIdx.z;
-  const bool causal = a.blkmin == nullptr;
+  const bool causal = a.lrow == nullptr;
   const int nb = a.nb;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int rb = bt * kTile + 64 * (w >> 1);  // first query block of the wave
-  const int cb = ct * kTile + 64 * (w & 1);   // first key block of the wave
+  const int rb = bt * kTile + 64 * (w >> 1);  // first row (query block or rank) of the wave
+  const int cb = ct * kTile + 64 * (w & 1);   // first column (key block or rank) of the wave
   const int row_end = min(nb, a.r0 + a.rows);
   if (rb >= row_end || cb >= nb) return;
-  if (causal && cb > rb + 63) return;  // above the block diagonal
+  // past the last candidate of the wave's last row: above the block diagonal, or
+  // past the eligible key blocks (permuted; lrow is non-decreasing over the rows)
+  if (causal ? cb > rb + 63 : cb >= a.lrow[min(rb + 63, row_end - 1)]) return;
   const int hs = blockIdx.y;
   const int half = lane >> 5, col = lane & 31;
   __shared__ __attribute__((aligned(16))) float score_stage[4][32 * kStagePitch];
@@ -130,12 +136,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
                                         kBufDword3);
   const int qo[2] = {(half * nb + min(rb + col, nb - 1)) * 4, (half * nb + min(rb + 32 + col, nb - 1)) * 4};
   const int ko[2] = {(half * nb + min(cb + col, nb - 1)) * 4, (half * nb + min(cb + 32 + col, nb - 1)) * 4};
-  // permuted sequences: the earliest original position of each key block this
-  // lane stores, loaded now so that the stores do not wait for it
-  const int c4 = cb + 4 * (lane & 15);  // first of the 4 key blocks this lane stores
-  int cmin[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) cmin[e] = causal ? 0 : a.blkmin[min(c4 + e, nb - 1)];
+  const int c4 = cb + 4 * (lane & 15);  // first of the 4 columns this lane stores
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -187,14 +188,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
   __builtin_amdgcn_sched_barrier(0);
   mul(aq, ak);
   mul(bq, bk);
-  // accumulator v of lane l holds query block 32 i + (v & 3) + 8 (v >> 2) + 4 (l >> 5)
-  // and key block 32 j + (l & 31) of the sub-tile. The stores go through LDS,
+  // accumulator v of lane l holds row 32 i + (v & 3) + 8 (v >> 2) + 4 (l >> 5)
+  // and column 32 j + (l & 31) of the sub-tile. The stores go through LDS,
   // 32 rows at a time, so that each lane writes 4 consecutive scores of a row
-  // (a store instruction covers 256 contiguous bytes of 4 rows).
-  // Permuted sequences: a key block whose earliest original position is after
-  // the query block's latest is stored as the all-ones pattern, whose sortable
-  // key is 0 (not a candidate), so the top-k needs no position loads.
-  const float not_eligible = __builtin_bit_cast(float, 0xffffffffu);
+  // (a store instruction covers 256 contiguous bytes of 4 rows); only a row's
+  // candidates are stored.
   float* t = score_stage[w];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -206,18 +204,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int rr = (lane >> 4) + 4 * k;  // row within this half of the sub-tile
-      const int r = 32 * i + rr;
-      const int bmax = causal ? 0 : a.blkmax[min(rb + r, nb - 1)];  // uniform branch
-      const int b = rb + r;
+      const int b = rb + 32 * i + rr;
       if (b >= row_end) continue;
-      float4 x = *(const float4*)&t[rr * kStagePitch + 4 * (lane & 15)];
-      if (!causal) {
-        x.x = cmin[0] > bmax ? not_eligible : x.x;
-        x.y = cmin[1] > bmax ? not_eligible : x.y;
-        x.z = cmin[2] > bmax ? not_eligible : x.z;
-        x.w = cmin[3] > bmax ? not_eligible : x.w;
-      }
-      const int clim = causal ? b : nb - 1;  // last column stored
+      const float4 x = *(const float4*)&t[rr * kStagePitch + 4 * (lane & 15)];
+      const int clim = causal ? b : a.lrow[b] - 1;  // last column stored
       float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * nb;
       if (c4 + 3 <= clim && (nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
         *(float4*)(row + c4) = x;
@@ -234,17 +224,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
 
 constexpr int kTopkCap = 1024;  // compacted candidates of the pre-filtered top-k
 
+// Permuted rows: the top kb keys by the rule of reg_topk_threshold (keys > thr,
+// then `need` of the keys == thr), where key i of this thread is column rank(i)
+// and column s is key block sigma[s]. The keys at the threshold are taken in
+// ascending block id, and the selected blocks are written in ascending id:
+// both through a bitmap over block ids in LDS (one 64-bit word per thread).
+template <int PERQ, class RankFn>
+__device__ int topk_by_block_id(const uint32_t (&key)[PERQ], int n, int kb, RankFn rank, const int32_t* sigma,
+                                int nb, uint64_t* gid, uint64_t* eid, int* red, int* wsum, int32_t* out) {
+  const int tid = threadIdx.x;
+  const int nwords = (nb + 63) >> 6;  // <= 256
+  uint32_t thr;
+  int need;
+  const int keep = reg_topk_threshold<256, PERQ>(key, n, kb, red, thr, need);
+  if (tid < nwords) {
+    gid[tid] = 0ull;
+    eid[tid] = 0ull;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PERQ; ++i) {
+    const uint32_t x = key[i];
+    if (256 * i < n && x > 0u && (x > thr || (need > 0 && x == thr))) {
+      const int id = sigma[rank(i)];
+      atomicOr((unsigned long long*)((x > thr ? gid : eid) + (id >> 6)), 1ull << (id & 63));
+    }
+  }
+  __syncthreads();
+  uint64_t sel = tid < nwords ? gid[tid] : 0ull;
+  uint64_t eq = tid < nwords ? eid[tid] : 0ull;
+  int tot;
+  if (need > 0) {
+    int m = need - block_excl_scan_int<256>((int)__popcll(eq), wsum, tot);  // equal keys this word may take
+    while (m > 0 && eq != 0ull) {
+      const uint64_t low = eq & (~eq + 1ull);
+      sel |= low;
+      eq ^= low;
+      --m;
+    }
+  }
+  int pos = block_excl_scan_int<256>((int)__popcll(sel), wsum, tot);
+  while (sel != 0ull) {
+    out[pos++] = 64 * tid + __builtin_ctzll(sel);
+    sel &= sel - 1ull;
+  }
+  return keep;
+}
+
 // Top-k_b key blocks of every query block of the round, from the stored scores.
-// Causal: the candidates are c <= b. Permuted: every c whose earliest original
-// position is not after the query block's latest one (the score kernel stored
-// the others as the all-ones pattern, sortable key 0). One workgroup per row;
-// candidate c = 256 i + tid is held as sortable key k[i] in registers (0 for
-// an ineligible block) for the exact register top-k (ties to the lower id).
-// Long rows (PER >= 16, k_b <= 256) are first narrowed: each thread keeps its
-// 4 largest keys, each wave takes the ceil(k_b / 4)-th largest of those 256
-// (a wave-only bitwise search), and the smallest of the four, t0, has at least
-// k_b keys >= it (each wave holds ceil(k_b / 4) distinct keys >= t0). The keys
-// >= t0 (typically ~2 k_b) are compacted into LDS in block order and the
+// Row r of the round is query block r (causal: candidates are the key blocks
+// c <= r) or the query block tau[r] (permuted: candidates are the columns
+// 0 .. lrow[r] - 1, the eligible key blocks in earliest-position order). One
+// workgroup per row; the candidates are held as sortable keys k[i] in
+// registers for the exact register top-k (ties to the lower block id).
+// Long rows (PER >= 16, k_b <= 256) are first narrowed: each wave takes the
+// ceil(k_b / 4)-th largest of its 64 threads' maxima (a wave-only bitwise
+// search), and the smallest of the four, t0, has at least k_b keys >= it
+// (each wave has ceil(k_b / 4) threads whose maximum is >= t0). The keys
+// >= t0 (typically ~2 k_b) are compacted into LDS in column order and the
 // register top-k runs over them; when they exceed kTopkCap the whole row is
 // searched.
 template <int PER, bool PERM>
@@ -256,78 +293,63 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   __shared__ uint32_t ckey[PER >= 16 ? kTopkCap : 1];
   __shared__ int32_t cid[PER >= 16 ? kTopkCap : 1];
   __shared__ int coff[PER >= 16 ? 4 * PER : 1];
+  // (gmask / emask double as the id bitmaps of a permuted row: 4 PER words hold
+  // 256 PER >= n_b ids)
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r_end = a.r0 + a.rows < a.nb ? a.r0 + a.rows : a.nb;
-  const int b = r_end - 1 - (int)blockIdx.x;  // longest rows first
+  const int r = r_end - 1 - (int)blockIdx.x;  // longest rows first
+  const int b = PERM ? a.tau[r] : r;          // the query block of the row
   const int hs = blockIdx.y;
   const int slot = a.outslot[hs];
   const int kb = a.k_b;
-  const bool causal = !PERM;
-  const int ncand = causal ? b + 1 : a.nb;
-  const float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * a.nb;
+  const int ncand = PERM ? a.lrow[r] : r + 1;
+  const float* row = a.scores + ((size_t)hs * a.rows + (r - a.r0)) * a.nb;
   // all loads first, then the keys: the loads are unconditional (no branch for
   // the compiler to sink the key arithmetic into, which would wait for every
   // load in turn); a slot past the row's candidates reads a valid address near
   // the row's start, whose value the key step discards
   // (the row is uniform: 32-bit byte offsets from it, n_b * 4 < 2^32)
+  // Register i of thread tid is column 256 i + tid (causal) or 256 i + (tid + i)
+  // mod 256 (permuted: the key blocks of one patch of a video, which the
+  // earliest-position order spaces 256 apart, then rotate over the threads
+  // instead of piling up in one, and the narrowing below stays tight)
+  auto col_of = [&](int i) { return PERM ? 256 * i + ((tid + i) & 255) : 256 * i + tid; };
   float sv[PER];
   const char* rowb = (const char*)row;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int c = 256 * i + tid < a.nb ? 256 * i + tid : a.nb - 1;
+    const int c = col_of(i) < a.nb ? col_of(i) : a.nb - 1;
     const uint32_t off = (uint32_t)(256 * i < ncand ? c : (tid < a.nb ? tid : a.nb - 1)) * 4u;
     sv[i] = *(const float*)(rowb + off);
   }
   uint32_t key[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int c = 256 * i + tid;
     const uint32_t u = sortable_key(sv[i]);
-    // an eligible key is never 0, even for a NaN score; the stored all-ones pattern marks an
-    // ineligible block of a permuted sequence (tested on the bits, before any arithmetic)
-    const bool marked = !causal && __builtin_bit_cast(uint32_t, sv[i]) == 0xffffffffu;
-    key[i] = (c < ncand && !marked) ? (u > 0u ? u : 1u) : 0u;
+    key[i] = col_of(i) < ncand ? (u > 0u ? u : 1u) : 0u;  // a candidate's key is never 0
   }
   int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
   int keep = -1;
   if constexpr (PER >= 16) {
     if (kb <= 256 && ncand > kTopkCap) {
-      // t0: the smallest of the waves' ceil(kb / 4)-th largest keys among their
-      // threads' largest key (causal rows) or 4 largest keys (permuted rows,
-      // whose eligible keys can sit in a few threads: a query block of an early
-      // frame chunk sees only the key blocks of chunks up to its own, which
-      // are the same few lanes of every wave)
-      uint32_t t1 = 0u, t2 = 0u, t3 = 0u, t4 = 0u;
+      // t0: the smallest of the waves' ceil(kb / 4)-th largest thread maxima
+      uint32_t tm = 0u;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        if constexpr (PERM) {
-          uint32_t x = key[i], y;
-          y = max(t1, x); x = min(t1, x); t1 = y;
-          y = max(t2, x); x = min(t2, x); t2 = y;
-          y = max(t3, x); x = min(t3, x); t3 = y;
-          t4 = max(t4, x);
-        } else {
-          t1 = max(t1, key[i]);
-        }
-      }
+      for (int i = 0; i < PER; ++i) tm = key[i] > tm ? key[i] : tm;
       const int kq = (kb + 3) >> 2;
       uint32_t tw = 0u;
       for (int bit = 31; bit >= 0; --bit) {
         const uint32_t cand = tw | (1u << bit);
-        int c = (int)__popcll(__ballot(t1 >= cand));
-        if constexpr (PERM)
-          c += (int)(__popcll(__ballot(t2 >= cand)) + __popcll(__ballot(t3 >= cand)) +
-                     __popcll(__ballot(t4 >= cand)));
-        if (c >= kq) tw = cand;
+        if ((int)__popcll(__ballot(tm >= cand)) >= kq) tw = cand;
       }
       if (lane == 0) red[wave] = (int)tw;
       __syncthreads();
       uint32_t t0 = (uint32_t)red[0];
 #pragma unroll
       for (int w = 1; w < 4; ++w) t0 = (uint32_t)red[w] < t0 ? (uint32_t)red[w] : t0;
-      if (t0 == 0u) t0 = 1u;  // never ineligible blocks
-      // per (i, wave) counts of keys >= t0, then their offsets in block order
+      if (t0 == 0u) t0 = 1u;  // never a non-candidate
+      // per (i, wave) counts of keys >= t0, then their offsets in column order
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int cnt = (int)__popcll(__ballot(key[i] >= t0));
@@ -346,27 +368,34 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
           if (key[i] >= t0) {
             const int pos = coff[4 * i + wave] + (int)__popcll(bal & lt);
             ckey[pos] = key[i];
-            cid[pos] = 256 * i + tid;
+            cid[pos] = col_of(i);
           }
         }
         __syncthreads();
         uint32_t k2[kTopkCap / 256];
 #pragma unroll
         for (int j = 0; j < kTopkCap / 256; ++j) k2[j] = 256 * j + tid < tot ? ckey[256 * j + tid] : 0u;
-        keep = reg_topk_ordered<256, kTopkCap / 256>(k2, tot, kb, gmask, emask, red, wsum,
-                                                     [&](int pos, int x) { out[pos] = cid[x]; });
+        if constexpr (PERM)
+          keep = topk_by_block_id<kTopkCap / 256>(k2, tot, kb, [&](int j) { return cid[256 * j + tid]; },
+                                                   a.sigma, a.nb, gmask, emask, red, wsum, out);
+        else
+          keep = reg_topk_ordered<256, kTopkCap / 256>(k2, tot, kb, gmask, emask, red, wsum,
+                                                       [&](int pos, int x) { out[pos] = cid[x]; });
       }
       __syncthreads();  // red / wsum / coff are reused below
     }
   }
-  if (keep < 0)
-    keep = reg_topk_ordered<256, PER>(key, ncand, kb, gmask, emask, red, wsum,
-                                      [&](int pos, int c) { out[pos] = c; });
+  if (keep < 0) {
+    if constexpr (PERM)
+      keep = topk_by_block_id<PER>(key, ncand, kb, col_of, a.sigma, a.nb, gmask, emask, red, wsum, out);
+    else
+      keep = reg_topk_ordered<256, PER>(key, ncand, kb, gmask, emask, red, wsum,
+                                        [&](int pos, int c) { out[pos] = c; });
+  }
   for (int e = keep + tid; e < kb; e += 256) out[e] = -1;
   if (tid == 0) a.blk_cnt[(size_t)slot * a.nb + b] = keep;
 }
 
-// Per-block min and max of the original positions of a permuted sequence.
 __global__ __launch_bounds__(64) void block_minmax_kernel(const int32_t* pos, int n, int32_t* bmin, int32_t* bmax) {
   const int c = blockIdx.x;
   const int j = c * kBlock + threadIdx.x;
@@ -380,6 +409,68 @@ __global__ __launch_bounds__(64) void block_minmax_kernel(const int32_t* pos, in
     bmin[c] = lo;
     bmax[c] = hi;
   }
+}
+
+// Orders of the blocks of a permuted sequence. The positions are distinct, so
+// the blocks' earliest positions are distinct, and so are their latest ones:
+// a bitmap over [0, n) of the earliest (latest) positions with a prefix count
+// per 32-bit word gives each block's rank among the blocks by earliest
+// (latest) position, and for a query block b the number of key blocks whose
+// earliest position is <= b's latest -- its eligible key blocks, which are the
+// first of them in the earliest-position order.
+__global__ __launch_bounds__(256) void perm_clear_kernel(const PermRankLaunch a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < a.words) {
+    a.bits_min[i] = 0u;
+    a.bits_max[i] = 0u;
+  }
+}
+
+__global__ __launch_bounds__(256) void perm_bits_kernel(const PermRankLaunch a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.nb) return;
+  const int x = a.bmin[c], y = a.bmax[c];
+  atomicOr(a.bits_min + (x >> 5), 1u << (x & 31));
+  atomicOr(a.bits_max + (y >> 5), 1u << (y & 31));
+}
+
+// exclusive prefix counts of both bitmaps' set bits per word (one workgroup)
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const PermRankLaunch a) {
+  __shared__ int wsum[16];
+  const int t = threadIdx.x;
+  const int per = (a.words + 1023) / 1024;
+  const int w0 = t * per;
+  const int w1 = min(w0 + per, a.words);
+  int cmin = 0, cmax = 0;
+  for (int w = w0; w < w1; ++w) {
+    cmin += __popc(a.bits_min[w]);
+    cmax += __popc(a.bits_max[w]);
+  }
+  int tot;
+  int pmin = block_excl_scan_int<1024>(cmin, wsum, tot);
+  int pmax = block_excl_scan_int<1024>(cmax, wsum, tot);
+  for (int w = w0; w < w1; ++w) {
+    a.pre_min[w] = pmin;
+    a.pre_max[w] = pmax;
+    pmin += __popc(a.bits_min[w]);
+    pmax += __popc(a.bits_max[w]);
+  }
+}
+
+__global__ __launch_bounds__(256) void perm_rank_kernel(const PermRankLaunch a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= a.nb) return;
+  const int x = a.bmin[c], y = a.bmax[c];
+  const uint32_t below_x = (1u << (x & 31)) - 1u;
+  const uint32_t below_y = (1u << (y & 31)) - 1u;
+  const uint32_t upto_y = (y & 31) == 31 ? 0xffffffffu : (2u << (y & 31)) - 1u;
+  const int rk = a.pre_min[x >> 5] + __popc(a.bits_min[x >> 5] & below_x);
+  const int rq = a.pre_max[y >> 5] + __popc(a.bits_max[y >> 5] & below_y);
+  a.rank_k[c] = rk;
+  a.sigma[rk] = c;
+  a.rank_q[c] = rq;
+  a.tau[rq] = c;
+  a.lrow[rq] = a.pre_min[y >> 5] + __popc(a.bits_min[y >> 5] & upto_y);
 }
 
 // Row permutation of [heads][n] rows of row_bytes bytes (a multiple of 4):
@@ -404,7 +495,8 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const W* x, W* out, i
 }  // namespace
 
 hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, const int32_t* slots, int n_heads,
-                             float* out_rm, float* out_t, hipStream_t stream, int first_block) {
+                             float* out_rm, float* out_t, hipStream_t stream, int first_block,
+                             const int32_t* col_map) {
   const int nb = (n + kBlock - 1) / kBlock;
   if (first_block < 0 || first_block >= nb) return hipSuccess;
   for (int base = 0; base < n_heads; base += kMaxPoolHeads) {
@@ -413,6 +505,7 @@ hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, con
     a.x = x;
     a.out_rm = out_rm;
     a.out_t = out_t;
+    a.col_map = col_map;
     a.n = n;
     a.nb = nb;
     a.nh = c;
@@ -457,10 +550,19 @@ hipError_t launch_permute_rows(const void* x, void* out, int heads, int64_t n, i
   return hipGetLastError();
 }
 
+hipError_t launch_perm_ranks(const PermRankLaunch& a, hipStream_t stream) {
+  hipLaunchKernelGGL(perm_clear_kernel, dim3((a.words + 255) / 256), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(perm_bits_kernel, dim3((a.nb + 255) / 256), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipLaunchKernelGGL(perm_rank_kernel, dim3((a.nb + 255) / 256), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_topk(const float* qbar_t, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
                              int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
-                             const int32_t* blkmin, const int32_t* blkmax, hipStream_t stream) {
+                             const int32_t* lrow, const int32_t* sigma, const int32_t* tau, hipStream_t stream) {
   const int nbt = (nb + kTile - 1) / kTile;
+  const bool perm = lrow != nullptr;
   for (int base = 0; base < n_heads; base += kMaxPoolHeads) {
     const int c = n_heads - base < kMaxPoolHeads ? n_heads - base : kMaxPoolHeads;
     BsTopkLaunch a{};
@@ -473,8 +575,9 @@ hipError_t launch_block_topk(const float* qbar_t, const float* kbar_t, const int
     a.k_b = k_b;
     a.nh = c;
     a.rows = rows;
-    a.blkmin = blkmin;
-    a.blkmax = blkmax;
+    a.lrow = lrow;
+    a.sigma = sigma;
+    a.tau = tau;
     for (int i = 0; i < c; ++i) {
       a.kvslot[i] = kvslot[base + i];
       a.outslot[i] = base + i;
@@ -482,11 +585,12 @@ hipError_t launch_block_topk(const float* qbar_t, const float* kbar_t, const int
     for (int r0 = 0; r0 < nb; r0 += rows) {
       a.r0 = r0;
       const int row_tiles = (std::min(nb, r0 + rows) - r0 + kTile - 1) / kTile;
-      const int col_tiles = blkmin ? nbt : std::min(nbt, (r0 + rows) / kTile);
+      // permuted: the band's last candidate column is known only on the device,
+      // so every column tile is launched and those past it return at once
+      const int col_tiles = perm ? nbt : std::min(nbt, (r0 + rows) / kTile);
       hipLaunchKernelGGL(block_score_kernel, dim3(col_tiles, c, row_tiles), dim3(256), 0, stream, a);
       const dim3 tg(std::min(rows, nb - r0), c);
       auto topk = [&](auto kern) { hipLaunchKernelGGL(kern, tg, dim3(256), 0, stream, a); };
-      const bool perm = blkmin != nullptr;
       if (nb <= 256)
         perm ? topk(block_topk_kernel<1, true>) : topk(block_topk_kernel<1, false>);
       else if (nb <= 1024)

@@ -148,12 +148,13 @@ __device__ __forceinline__ int block_excl_scan_int(int v, int* wsum, int& total)
   return before + incl - v;
 }
 
-template <int NT, int PER, class OutFn>
-__device__ int reg_topk_ordered(const uint32_t (&key)[PER], int n, int k, uint64_t* gmask, uint64_t* emask,
-                                int* red, int* wsum, OutFn out) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+// First stage of the exact register top-k: the number of keys kept,
+// min(k, number of keys > 0), and the selection rule: every key > thr, then
+// `need` more among the keys == thr (need = 0 when exactly the kept keys are
+// > thr). Key i of thread t is candidate NT * i + t; keys of 0 are not
+// candidates; only slots NT * i < n are read.
+template <int NT, int PER>
+__device__ int reg_topk_threshold(const uint32_t (&key)[PER], int n, int k, int* red, uint32_t& thr, int& need) {
   int half = 0;
   int c = 0;
 #pragma unroll
@@ -161,8 +162,8 @@ __device__ int reg_topk_ordered(const uint32_t (&key)[PER], int n, int k, uint64
     if (NT * i < n) c += (int)__popcll(__ballot(key[i] > 0u));
   const int ncand = block_sum_waves<NT>(c, red, half);
   const int keep = ncand < k ? ncand : k;
-  uint32_t thr = 0u;  // selected: key > thr, then `need` lowest-id keys == thr
-  int need = 0;
+  thr = 0u;
+  need = 0;
   if (keep < ncand) {
     uint32_t t = 0u;
     bool exact = false;
@@ -192,6 +193,18 @@ __device__ int reg_topk_ordered(const uint32_t (&key)[PER], int n, int k, uint64
       need = k - block_sum_waves<NT>(c, red, half);
     }
   }
+  return keep;
+}
+
+template <int NT, int PER, class OutFn>
+__device__ int reg_topk_ordered(const uint32_t (&key)[PER], int n, int k, uint64_t* gmask, uint64_t* emask,
+                                int* red, int* wsum, OutFn out) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t thr;
+  int need;
+  const int keep = reg_topk_threshold<NT, PER>(key, n, k, red, thr, need);
   // word NW * i + wave holds ids NT * i + 64 * wave .. + 63, bit = lane
 #pragma unroll
   for (int i = 0; i < PER; ++i) {

@@ -106,7 +106,8 @@ hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);
 // and/or out_t ([slot][128][nb]); either output may be null. Blocks below
 // first_block are left untouched.
 hipError_t launch_block_pool(const uint16_t* x, int n, const int32_t* heads, const int32_t* slots, int n_heads,
-                             float* out_rm, float* out_t, hipStream_t stream, int first_block = 0);
+                             float* out_rm, float* out_t, hipStream_t stream, int first_block = 0,
+                             const int32_t* col_map = nullptr);
 
 // Decoding: one query row per head against a cache of n keys.
 constexpr int kDecMaxBlocks = 16384;  // n_b limit of the single-workgroup block top-k
@@ -137,13 +138,31 @@ inline int decode_topk_segments(int nb, int kb) {
 int decode_blocks_per_split(int kb, int rows);
 hipError_t launch_iota_rows(int32_t* dst, int rows, int cols, hipStream_t stream);
 hipError_t launch_decode(const DecodeLaunch& a, bool select, hipStream_t stream);
+// Orders of the blocks of a permuted sequence (positions distinct): ranks by
+// earliest / latest original position and each query rank's eligible count.
+struct PermRankLaunch {
+  const int32_t* bmin;  // [nb] earliest original position of every block
+  const int32_t* bmax;  // [nb] latest
+  uint32_t* bits_min;   // [words] bitmap of the earliest positions over [0, n)
+  uint32_t* bits_max;   // [words] bitmap of the latest positions
+  int32_t* pre_min;     // [words] set bits of bits_min before each word
+  int32_t* pre_max;     // [words]
+  int32_t* rank_q;      // [nb] rank of block b by latest position
+  int32_t* rank_k;      // [nb] rank of block c by earliest position
+  int32_t* tau;         // [nb] block of query rank r
+  int32_t* sigma;       // [nb] block of key rank s
+  int32_t* lrow;        // [nb] key blocks whose earliest position <= the latest of query rank r
+  int32_t n, nb, words;
+};
+hipError_t launch_perm_ranks(const PermRankLaunch& a, hipStream_t stream);
 // Scores and top-k for n_heads pooled query heads (qbar_t slots 0..n_heads-1, each
 // [128][nb]), head i reading pooled keys kbar_t slot kvslot[i] ([128][nb]); writes
-// blk_idx/blk_cnt slot i.
+// blk_idx/blk_cnt slot i. Permuted sequences pass lrow / sigma / tau (with the pooled
+// columns in rank order: query blocks by rank_q, key blocks by rank_k), else null.
 int block_score_rows(int nb, int n_heads);
 hipError_t launch_block_topk(const float* qbar_t, const float* kbar_t, const int32_t* kvslot, int n_heads, int nb,
                              int k_b, int32_t* blk_idx, int32_t* blk_cnt, float* scores, int rows,
-                             const int32_t* blkmin, const int32_t* blkmax, hipStream_t stream);
+                             const int32_t* lrow, const int32_t* sigma, const int32_t* tau, hipStream_t stream);
 // Per-block min / max of the original positions of a permuted sequence.
 hipError_t launch_block_minmax(const int32_t* pos, int n, int32_t* bmin, int32_t* bmax, hipStream_t stream);
 // Gather (scatter = 0) or scatter (1) rows of row_bytes bytes of [heads][n] data by src.
