@@ -372,6 +372,9 @@ minf_status minf_permute_rows(const void* x, void* out, int heads, int64_t n, in
   if (n > kMaxTokens) return fail(MINF_E_UNSUPPORTED, "n = %lld exceeds the supported %lld", (long long)n,
                                   (long long)kMaxTokens);
   if (scatter != 0 && scatter != 1) return fail(MINF_E_INVALID_ARG, "scatter must be 0 or 1");
+  if (n * (int64_t)(row_bytes / 4) >= ((int64_t)1 << 31))
+    return fail(MINF_E_UNSUPPORTED, "n * row_bytes / 4 = %lld words per head exceeds 2^31 - 1",
+                (long long)(n * (int64_t)(row_bytes / 4)));
   hipError_t e = launch_permute_rows(x, out, heads, n, row_bytes, src, scatter, stream);
   if (e != hipSuccess) return hip_fail(e, "row permutation kernel");
   return MINF_OK;

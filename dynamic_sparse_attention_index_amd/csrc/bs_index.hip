@@ -475,21 +475,37 @@ __global__ __launch_bounds__(256) void perm_rank_kernel(const PermRankLaunch a) 
 
 // Row permutation of [heads][n] rows of row_bytes bytes (a multiple of 4):
 // gather out[h][t] = x[h][src[t]], or scatter out[h][src[t]] = x[h][t].
-// W is the access unit (16 bytes when the row size allows, else 4).
+// W is the access unit (16 bytes when the row size allows, else 4). Each
+// thread moves kPermUnits units on a grid stride: the row indices are loaded
+// first, then every unit, then the stores, so that several independent
+// chains are in flight per thread (n * words < 2^31: 32-bit index arithmetic).
+constexpr int kPermUnits = 4;
 template <typename W>
-__global__ __launch_bounds__(256) void permute_rows_kernel(const W* x, W* out, int64_t n, int words,
+__global__ __launch_bounds__(256) void permute_rows_kernel(const W* x, W* out, int n, int words,
                                                            const int32_t* src, int scatter) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int h = blockIdx.y;
-  if (idx >= n * words) return;
-  const int64_t t = idx / words;
-  const int w = (int)(idx % words);
-  const int64_t s = src[t];
-  const size_t base = (size_t)h * n * words;
-  if (scatter)
-    out[base + (size_t)s * words + w] = x[base + (size_t)t * words + w];
-  else
-    out[base + (size_t)t * words + w] = x[base + (size_t)s * words + w];
+  const int total = n * words;
+  const int stride = gridDim.x * 256;
+  const int i0 = blockIdx.x * 256 + threadIdx.x;
+  const size_t base = (size_t)blockIdx.y * total;
+  int t[kPermUnits], w[kPermUnits], sr[kPermUnits];
+#pragma unroll
+  for (int u = 0; u < kPermUnits; ++u) {
+    const int idx = i0 + u * stride;
+    t[u] = idx < total ? idx / words : 0;
+    w[u] = idx - t[u] * words;
+    sr[u] = idx < total ? src[t[u]] : 0;
+  }
+  W v[kPermUnits];
+#pragma unroll
+  for (int u = 0; u < kPermUnits; ++u) {
+    const int row = scatter ? t[u] : sr[u];
+    if (i0 + u * stride < total) v[u] = x[base + (size_t)row * words + w[u]];
+  }
+#pragma unroll
+  for (int u = 0; u < kPermUnits; ++u) {
+    const int row = scatter ? sr[u] : t[u];
+    if (i0 + u * stride < total) out[base + (size_t)row * words + w[u]] = v[u];
+  }
 }
 
 }  // namespace
@@ -540,13 +556,14 @@ hipError_t launch_permute_rows(const void* x, void* out, int heads, int64_t n, i
   const bool wide = row_bytes % 16 == 0 && ((uintptr_t)x | (uintptr_t)out) % 16 == 0;
   const int words = wide ? row_bytes / 16 : row_bytes / 4;
   const int64_t total = n * words;
-  const dim3 grid((unsigned)((total + 255) / 256), heads);
+  if (total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((total + 256 * kPermUnits - 1) / (256 * kPermUnits)), heads);
   if (wide)
-    hipLaunchKernelGGL(permute_rows_kernel<u32x4>, grid, dim3(256), 0, stream, (const u32x4*)x, (u32x4*)out, n,
+    hipLaunchKernelGGL(permute_rows_kernel<u32x4>, grid, dim3(256), 0, stream, (const u32x4*)x, (u32x4*)out, (int)n,
                        words, src, scatter);
   else
     hipLaunchKernelGGL(permute_rows_kernel<uint32_t>, grid, dim3(256), 0, stream, (const uint32_t*)x,
-                       (uint32_t*)out, n, words, src, scatter);
+                       (uint32_t*)out, (int)n, words, src, scatter);
   return hipGetLastError();
 }
 

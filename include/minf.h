@@ -141,7 +141,8 @@ minf_status minf_build_permuted_block_index(const void* q, const void* k, int64_
 /* Row permutation of [heads][n] rows of row_bytes bytes (a multiple of 4):
  * scatter == 0 gathers out[h][t] = x[h][src[t]]; scatter == 1 scatters
  * out[h][src[t]] = x[h][t]. src: device int32 [n], a permutation of 0..n-1
- * (not checked). out must not alias x. */
+ * (not checked). out must not alias x. MINF_E_UNSUPPORTED when one head holds
+ * 2^31 or more 4-byte words (n * row_bytes / 4). */
 minf_status minf_permute_rows(const void* x, void* out, int heads, int64_t n, int row_bytes, const int32_t* src,
                               int scatter, hipStream_t stream);
 

@@ -170,6 +170,8 @@ def test_permutation_entry_points_reject():
     assert LIB.minf_permute_rows(FAKE, ctypes.c_void_p(0x20000), 1, 64, 6, FAKE, 0, None) == INVALID
     assert LIB.minf_permute_rows(FAKE, ctypes.c_void_p(0x20000), 1, 64, 256, None, 0, None) == INVALID
     assert LIB.minf_permute_rows(FAKE, ctypes.c_void_p(0x20000), 1, 64, 256, FAKE, 2, None) == INVALID
+    # one head of 2^31 or more 4-byte words
+    assert LIB.minf_permute_rows(FAKE, ctypes.c_void_p(0x20000), 1, 1 << 20, 8192, FAKE, 0, None) == UNSUPPORTED
     arr, nh = _heads(0)
     ws = LIB.minf_block_index_workspace_size(4096, 2, 1, 1)
     assert LIB.minf_build_permuted_block_index(FAKE, FAKE, 4096, 2, 1, 128, arr, nh, 4, None, FAKE, FAKE, FAKE, ws,
