@@ -17,6 +17,15 @@
 //    that holds a bounded band of rows at a time;
 //  * top-k: one workgroup per (head, query block); the row's scores are held
 //    in registers (up to 64 per thread) for an exact bitwise search.
+//
+// On a permuted sequence (a video in patch-major order: talk transcript,
+// MMInference part, on permuting rows and columns so that grid attention
+// becomes blocks) key block c is eligible for query block b when c's earliest
+// original position is not after b's latest. The rows and columns are then
+// taken in rank order (query blocks by latest position, key blocks by earliest
+// position), where each row's eligible key blocks are its first columns: the
+// score pass is a staircase like the causal triangle, and the selection is
+// mapped back to block ids.
 #include <algorithm>
 
 #include "common.h"
