@@ -97,6 +97,17 @@ def test_grid_layer_matches_oracle(gpu_lib, frames, patches, k_b):
     _check(q, k, v, src, o, lse, bi, bc, k_b, heads=[0, 3], rows_per_head=48, seed=frames)
 
 
+def test_grid_layer_several_score_bands(gpu_lib):
+    # 1024 frames x 256 patches, 32 heads: 4096 blocks, and the index's score
+    # buffer holds 1024 rows at a time (four bands); every row of two heads checked
+    frames, patches, k_b = 1024, 256, 64
+    print(f"[case] grid F={frames} P={patches} 32 heads k_b={k_b}", flush=True)
+    q, k, v = grid_qkv(frames, patches, 32, 8, device="cuda")
+    src = O.grid_permutation(frames, patches)
+    o, lse, bi, bc = _permuted_layer(gpu_lib, q, k, v, src, k_b)
+    _check(q, k, v, src, o, lse, bi, bc, k_b, heads=[0, 21], rows_per_head=16, seed=frames)
+
+
 def test_random_permutation_and_full_budget(gpu_lib):
     n = 1500
     print(f"[case] random permutation n={n}", flush=True)
