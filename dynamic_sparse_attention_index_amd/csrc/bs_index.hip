@@ -108,6 +108,19 @@ constexpr int kSteps = 8;   // contraction steps per register batch (2 x 32 load
 constexpr int kBufDword3 = 0x00020000;  // buffer resource word 3 on gfx9 (32-bit data format)
 constexpr int kStagePitch = 68;  // floats per staged score row (64 + 4 against bank conflicts)
 
+// Stored position of column c of a permuted score row, and its inverse: each
+// whole group of 256 columns is rotated by 4 x its group index (a last, partial
+// group stays in place, so no position reaches n_b). In earliest-position
+// order the key blocks of one video patch are 256 columns apart; the top-k
+// reads register i of thread t from position 256 i + t, so the rotation puts
+// them in different threads (and keeps 4-aligned runs of 4 columns together).
+__device__ __forceinline__ int score_pos(int c, int nb) {
+  return (c | 255) < nb ? (c & ~255) + ((c + 4 * (c >> 8)) & 255) : c;
+}
+__device__ __forceinline__ int score_col(int p, int nb) {
+  return (p | 255) < nb ? (p & ~255) + ((p - 4 * (p >> 8)) & 255) : p;
+}
+
 // Pooled scores of one 128 x 128 tile (query blocks x key blocks) on the fp32
 // matrix cores. Wave w computes the 64 x 64 sub-tile at query blocks
 // 64 (w >> 1) and key blocks 64 (w & 1) of the tile as 2 x 2 products of
@@ -217,14 +230,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       if (b >= row_end) continue;
       const float4 x = *(const float4*)&t[rr * kStagePitch + 4 * (lane & 15)];
       const int clim = causal ? b : a.lrow[b] - 1;  // last column stored
+      const int p4 = causal ? c4 : score_pos(c4, nb);  // where the 4 columns are stored
       float* row = a.scores + ((size_t)hs * a.rows + (b - a.r0)) * nb;
       if (c4 + 3 <= clim && (nb & 3) == 0) {  // 16-byte aligned when rows are whole float4s
-        *(float4*)(row + c4) = x;
+        *(float4*)(row + p4) = x;
       } else {
         const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (c4 + e <= clim) row[c4 + e] = xs[e];
+          if (c4 + e <= clim) row[p4 + e] = xs[e];
       }
     }
     __builtin_amdgcn_wave_barrier();  // the next half overwrites the staging rows
@@ -319,16 +333,22 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   // load in turn); a slot past the row's candidates reads a valid address near
   // the row's start, whose value the key step discards
   // (the row is uniform: 32-bit byte offsets from it, n_b * 4 < 2^32)
-  // Register i of thread tid is column 256 i + tid (causal) or 256 i + (tid + i)
-  // mod 256 (permuted: the key blocks of one patch of a video, which the
-  // earliest-position order spaces 256 apart, then rotate over the threads
-  // instead of piling up in one, and the narrowing below stays tight)
-  auto col_of = [&](int i) { return PERM ? 256 * i + ((tid + i) & 255) : 256 * i + tid; };
+  // Register i of thread tid holds position 256 i + tid of the row: column
+  // 256 i + tid (causal) or score_col of it (permuted: the stored rotation
+  // spreads the key blocks of one video patch over the threads, so that the
+  // narrowing below stays tight). A position becomes its column where it is
+  // used; the empty asm keeps the compiler from holding all 64 columns live
+  // between the key step and the selection.
+  auto col_at = [&](int p) {
+    if (!PERM) return p;
+    asm volatile("" : "+v"(p));
+    return score_col(p, a.nb);
+  };
   float sv[PER];
   const char* rowb = (const char*)row;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    const int c = col_of(i) < a.nb ? col_of(i) : a.nb - 1;
+    const int c = 256 * i + tid < a.nb ? 256 * i + tid : a.nb - 1;
     const uint32_t off = (uint32_t)(256 * i < ncand ? c : (tid < a.nb ? tid : a.nb - 1)) * 4u;
     sv[i] = *(const float*)(rowb + off);
   }
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const uint32_t u = sortable_key(sv[i]);
-    key[i] = col_of(i) < ncand ? (u > 0u ? u : 1u) : 0u;  // a candidate's key is never 0
+    key[i] = col_at(256 * i + tid) < ncand ? (u > 0u ? u : 1u) : 0u;  // a candidate's key is never 0
   }
   int32_t* out = a.blk_idx + ((size_t)slot * a.nb + b) * kb;
   int keep = -1;
@@ -377,7 +397,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
           if (key[i] >= t0) {
             const int pos = coff[4 * i + wave] + (int)__popcll(bal & lt);
             ckey[pos] = key[i];
-            cid[pos] = col_of(i);
+            cid[pos] = 256 * i + tid;
           }
         }
         __syncthreads();
@@ -385,7 +405,7 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
 #pragma unroll
         for (int j = 0; j < kTopkCap / 256; ++j) k2[j] = 256 * j + tid < tot ? ckey[256 * j + tid] : 0u;
         if constexpr (PERM)
-          keep = topk_by_block_id<kTopkCap / 256>(k2, tot, kb, [&](int j) { return cid[256 * j + tid]; },
+          keep = topk_by_block_id<kTopkCap / 256>(k2, tot, kb, [&](int j) { return col_at(cid[256 * j + tid]); },
                                                    a.sigma, a.nb, gmask, emask, red, wsum, out);
         else
           keep = reg_topk_ordered<256, kTopkCap / 256>(k2, tot, kb, gmask, emask, red, wsum,
@@ -396,7 +416,8 @@ __global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
   }
   if (keep < 0) {
     if constexpr (PERM)
-      keep = topk_by_block_id<PER>(key, ncand, kb, col_of, a.sigma, a.nb, gmask, emask, red, wsum, out);
+      keep = topk_by_block_id<PER>(key, ncand, kb, [&](int i) { return col_at(256 * i + tid); }, a.sigma, a.nb,
+                                   gmask, emask, red, wsum, out);
     else
       keep = reg_topk_ordered<256, PER>(key, ncand, kb, gmask, emask, red, wsum,
                                         [&](int pos, int c) { out[pos] = c; });
