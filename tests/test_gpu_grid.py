@@ -123,6 +123,17 @@ def test_random_permutation_and_full_budget(gpu_lib):
     assert float((lf - ld).abs().max()) <= 2e-3
 
 
+def test_random_permutation_whole_and_partial_column_groups(gpu_lib):
+    # 600 blocks (the last one ragged): columns 256..511 form a whole group, which
+    # the index stores rotated, and 512..599 a partial one, which it stores in place
+    n = 64 * 600 - 5
+    print(f"[case] random permutation n={n}", flush=True)
+    q, k, v, _ = planted_qkv(n, 4, 2, seed=93, device="cuda")
+    src = np.random.default_rng(7).permutation(n)
+    o, lse, bi, bc = _permuted_layer(gpu_lib, q, k, v, src, 24)
+    _check(q, k, v, src, o, lse, bi, bc, 24, heads=[0, 3], rows_per_head=24, seed=3)
+
+
 def test_identity_permutation_is_block_sparse(gpu_lib):
     n = 4096
     q, k, v, _ = planted_qkv(n, 4, 2, seed=92, device="cuda")
