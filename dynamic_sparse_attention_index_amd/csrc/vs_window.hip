@@ -18,8 +18,8 @@
 //    U is cut into 64-key tiles from its start, a tile being (start, end) with
 //    end - start <= 64. Block b's windows are U + 64b, so one cover serves every
 //    query block. One wave per head walks the bitmap from the highest offset
-//    down (window starts ascending) 64 words at a time, reading each word into
-//    scalar registers.
+//    down (window starts ascending) 64 words at a time, reading each non-empty
+//    word into scalar registers.
 #include "common.h"
 #include "launch.h"
 
@@ -52,16 +52,25 @@ __global__ __launch_bounds__(64) void vsw_cover_kernel(const VswLaunch a) {
   int cnt = 0;
   bool open = false;
   int cs = 0, ce = 0;  // the open interval [cs, ce)
-  auto emit = [&](int s, int e) {
-    for (int t = s; t < e; t += kBlock) {
-      if (lane == 0 && cnt < cap) out[cnt] = int2{t, t + kBlock < e ? t + kBlock : e};
-      ++cnt;
+  auto emit = [&](int s, int e) {  // the interval's tiles, 64 at a time across the lanes
+    const int nt = (e - s + kBlock - 1) / kBlock;
+    for (int t0 = 0; t0 < nt; t0 += 64) {
+      const int t = t0 + lane;
+      if (t < nt && cnt + t < cap) {
+        const int ts = s + t * kBlock;
+        out[cnt + t] = int2{ts, ts + kBlock < e ? ts + kBlock : e};
+      }
     }
+    cnt += nt;
   };
   for (int w0 = ((nwords - 1) >> 6) << 6; w0 >= 0; w0 -= 64) {
     const int wi = w0 + lane;
     const uint32_t mine = wi < nwords ? bits[wi] : 0u;
-    for (int j = 63; j >= 0; --j) {
+    // only the non-empty words, highest first (the offsets are sparse)
+    uint64_t nz = __ballot(mine != 0u);
+    while (nz != 0ull) {
+      const int j = 63 - __builtin_clzll(nz);
+      nz &= ~(1ull << j);
       uint32_t wd = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
       while (wd != 0u) {
         const int bit = 31 - __builtin_clz(wd);
