@@ -308,7 +308,7 @@ __device__ int topk_by_block_id(const uint32_t (&key)[PERQ], int n, int kb, Rank
 // register top-k runs over them; when they exceed kTopkCap the whole row is
 // searched.
 template <int PER, bool PERM>
-__global__ __launch_bounds__(256) void block_topk_kernel(const BsTopkLaunch a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void block_topk_kernel(const BsTopkLaunch a) {
   __shared__ uint64_t gmask[4 * PER];
   __shared__ uint64_t emask[4 * PER];
   __shared__ int red[8];
