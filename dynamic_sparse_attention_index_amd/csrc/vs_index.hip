@@ -44,7 +44,7 @@ struct VsSmem2 {
 };
 
 template <int PASS>
-__global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
+__device__ __forceinline__ void vs_pass(const VsLaunch& a) {
   __shared__ typename std::conditional<PASS == 1, VsSmem1, VsSmem2>::type sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -243,6 +243,20 @@ __global__ __launch_bounds__(kThreads) void vs_pass_kernel(const VsLaunch a) {
       }
     }
   }
+}
+
+// Pass 1 fits 3 waves per SIMD (168 VGPRs, a few spilled: 1.15 -> 0.96 ms at 1M
+// tokens); pass 2 runs 2 (at 3 waves it spilled 35 VGPRs and took 3.1 instead
+// of 2.0 ms).
+template <int PASS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_pass_kernel(
+    const VsLaunch a) {
+  vs_pass<PASS>(a);
+}
+template <>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void vs_pass_kernel<1>(
+    const VsLaunch a) {
+  vs_pass<1>(a);
 }
 
 // Merge the chunk partials of every row in chunk order: max and 1 / sum.
