@@ -411,8 +411,8 @@ size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
          align_up((size_t)hq * 2 * nblocks(n) * sizeof(int32_t)) + kAlign + (size_t)hq * vsw_head_bytes(n);
 }
 
-// Launches with Vertical-Slash heads at long lengths queue two launches of
-// the same work: a cooperative one in which the 64 workgroups of an XCD run
+// Launches of Vertical-Slash heads only, at long lengths, queue two launches
+// of the same work: a cooperative one in which the 64 workgroups of an XCD run
 // their items in rounds that start together, and an ordinary one. A flag
 // computed on the device from the offset bitmaps, without a host round trip,
 // lets exactly one of them work: rounds when the items are long (thousands of
@@ -642,7 +642,11 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
     a.hgroup = hg;
     a.xcd_sync = nullptr;
     a.rounds_flag = nullptr;
-    if ((!launch_bits.empty() || !launch_wcount.empty()) && n >= kRoundsMinTokens && rounds_enabled(stream)) {
+    // only launches whose heads are all Vertical-Slash (or VS windows): with other
+    // kinds beside them the items of a round differ in length and the workgroups
+    // of a round wait for its longest (mixed 512K layer: rounds 1696 ms, ordinary 1647)
+    const bool all_vs = (int)(launch_bits.size() + launch_wcount.size()) == nh;
+    if (all_vs && n >= kRoundsMinTokens && rounds_enabled(stream)) {
       int32_t* flag = sync_ws + 8;
       hipError_t e = launch_rounds_flag(launch_bits.data(), (int)launch_bits.size(), launch_wcount.data(),
                                         (int)launch_wcount.size(), (int)n, kRoundsMinTiles, flag, stream);
