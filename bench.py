@@ -269,8 +269,8 @@ def cpu_baseline(q, k, v, kinds, cfg, plans_gpu, n, blocks_per_head):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
-                                   "(heads shard across GPUs without exchange; see DESIGN.md)"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus above 1 is not supported "
+                                   "(the heads of a layer would shard across GPUs with no exchange)"}))
         sys.exit(2)
     import torch
 

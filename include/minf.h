@@ -48,7 +48,7 @@ extern "C" {
 typedef int minf_status;
 #define MINF_OK 0
 #define MINF_E_INVALID_ARG 1 /* null pointer, bad size, bad head list, ... */
-#define MINF_E_UNSUPPORTED 2 /* valid request this build does not implement (d != 128, last_q > 64) */
+#define MINF_E_UNSUPPORTED 2 /* valid request the library does not implement (d != 128, last_q > 64) */
 #define MINF_E_WORKSPACE 3   /* workspace pointer null or smaller than required */
 #define MINF_E_HIP 4         /* a HIP runtime call or launch failed */
 

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The HIP library through its Python binding; fails loudly when absent on a GPU machine."""
+    """The HIP library through its Python binding; fails loudly when absent on a machine with a GPU."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU visible")
