@@ -9,7 +9,6 @@ from .minf_oracle import (  # noqa: F401
     topk_lowidx,
     attend_rows,
     dense_attn,
-    causal_mask_row,
     ashape_mask_row,
     vs_last_query_probs,
     vs_column_diag_sums,

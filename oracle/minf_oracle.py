@@ -122,11 +122,6 @@ def attend_rows(q_rows, k, v, mask, scale: float):
     return out, lse
 
 
-def causal_mask_row(i: int, n: int) -> np.ndarray:
-    """Causal prefill: query i sees keys j <= i."""
-    return np.arange(n) <= i
-
-
 def _kv_head(h: int, hq: int, hkv: int) -> int:
     """GQA reading: consecutive groups of hq // hkv query heads share a KV head."""
     return h // (hq // hkv)

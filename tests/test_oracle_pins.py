@@ -425,10 +425,61 @@ def test_plan_blocks_counts_blocks_with_mask_entries():
         assert O.plan_blocks(dict(kind="ashape", sink=sink, local=local), n) == want
     cnt = rng.integers(1, 4, nb)
     assert O.plan_blocks(dict(kind="block", blk_idx=None, blk_cnt=cnt), n) == cnt.sum()
-    s_idx = np.array([0, 130, 400])
-    v_idx = np.array([5, 300, 699])
-    want = sum(len(O.vs_block_set(n, s_idx, b)) + len(O.vs_column_set(n, s_idx, v_idx, b)) / 64 for b in range(nb))
-    assert O.plan_blocks(dict(kind="vs", s_idx=s_idx, v_idx=v_idx), n) == want
+
+
+def _vs_work_loops(n, s_idx, v_idx):
+    """VS work from scalar loops over rows and offsets: for every query block, the
+    key blocks that some row i of the block meets at i - dl (dl selected, i - dl >= 0),
+    plus 1/64 for every selected column at or before the block's last row whose key
+    block is not among them."""
+    tot = 0.0
+    for b in range((n + 63) // 64):
+        last = min(64 * b + 63, n - 1)
+        met = set()
+        for i in range(64 * b, last + 1):
+            for dl in s_idx:
+                if i - int(dl) >= 0:
+                    met.add((i - int(dl)) // 64)
+        cols = 0
+        for j in sorted(set(int(x) for x in v_idx)):
+            if j <= last and j // 64 not in met:
+                cols += 1
+        tot += len(met) + cols / 64
+    return tot
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 700, 640])
+def test_plan_blocks_vs_brute_force(n):
+    # the oracle's work count of a VS plan, against scalar loops that never form Bs(b) or Cv(b)
+    rng = np.random.default_rng(n)
+    cases = [(np.array([0, 130, 400]), np.array([5, 300, 699])), (np.array([]), np.array([0, 3])),
+             (np.array([1]), np.array([])), (np.array([63, 64, 65]), np.array([62, 63, 64, 127, 128]))]
+    for _ in range(3):
+        cases.append((np.sort(rng.choice(n, size=min(n, 7), replace=False)),
+                      np.sort(rng.choice(n, size=min(n, 9), replace=False))))
+    for s_idx, v_idx in cases:
+        s_in = s_idx[s_idx < n]
+        v_in = v_idx[v_idx < n]
+        got = O.plan_blocks(dict(kind="vs", s_idx=s_in, v_idx=v_in), n)
+        assert got == _vs_work_loops(n, s_in, v_in), (n, s_in, v_in)
+
+
+def test_plan_blocks_vs_closed_forms():
+    # hand-derived counts, n = 700 (11 query blocks, the last one of 60 rows):
+    #  * D = {0}: every block meets only its own diagonal block -> 11 blocks;
+    #  * D = {128}: a multiple of 64 shifts every row by exactly two blocks, so
+    #    blocks b >= 2 meet block b - 2 -> 9 blocks;
+    #  * D = {1}: rows 64b + 1.. meet block b, row 64b meets block b - 1 (b >= 1)
+    #    -> 11 + 10 = 21 blocks;
+    #  * D = {0}, V = {5, 699}: column 5 lies in block 0, met by block 0 itself and
+    #    gathered by blocks 1..10 (10 columns); column 699 is in the last block,
+    #    which computes its own diagonal block -> 11 + 10/64.
+    n = 700
+    vs = lambda s, v: O.plan_blocks(dict(kind="vs", s_idx=np.array(s), v_idx=np.array(v)), n)  # noqa: E731
+    assert vs([0], []) == 11
+    assert vs([128], []) == 9
+    assert vs([1], []) == 21
+    assert vs([0], [5, 699]) == 11 + 10 / 64
 
 
 def test_search_picks_best_recall_within_budget():
