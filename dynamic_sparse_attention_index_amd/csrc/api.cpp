@@ -661,6 +661,90 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
   return MINF_OK;
 }
 
+minf_status minf_plan_work(const minf_head_plan* plans, int64_t n, int hq, double* work, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
+  g_detail.clear();
+  if (n < 1) return fail(MINF_E_INVALID_ARG, "n must be >= 1 (got %lld)", (long long)n);
+  if (n > kMaxTokens)
+    return fail(MINF_E_UNSUPPORTED, "n = %lld exceeds the supported %lld", (long long)n, (long long)kMaxTokens);
+  if (hq < 1) return fail(MINF_E_INVALID_ARG, "hq must be >= 1");
+  if (!plans) return fail(MINF_E_INVALID_ARG, "plans must be a host array of hq entries");
+  if (!work) return fail(MINF_E_INVALID_ARG, "work must be a device array of hq doubles");
+  bool any_vs = false;
+  for (int h = 0; h < hq; ++h) {
+    const minf_head_plan& p = plans[h];
+    switch (p.kind) {
+      case MINF_KIND_DENSE: break;
+      case MINF_KIND_ASHAPE:
+        if (p.sink < 0 || p.local < 0) return fail(MINF_E_INVALID_ARG, "head %d: sink and local must be >= 0", h);
+        break;
+      case MINF_KIND_VS:
+        if (p.k_v < 0 || p.k_s < 0) return fail(MINF_E_INVALID_ARG, "head %d: k_v and k_s must be >= 0", h);
+        if ((p.k_v > 0 && !p.v_idx) || (p.k_s > 0 && !p.s_idx))
+          return fail(MINF_E_INVALID_ARG, "head %d: v_idx / s_idx null with a positive count", h);
+        any_vs = true;
+        break;
+      case MINF_KIND_BLOCK:
+        if (!p.blk_cnt) return fail(MINF_E_INVALID_ARG, "head %d: blk_cnt is null", h);
+        break;
+      case MINF_KIND_VS_WINDOW:
+        return fail(MINF_E_UNSUPPORTED, "head %d: the work count covers dense, A-shape, VS and Block-Sparse plans", h);
+      default: return fail(MINF_E_INVALID_ARG, "head %d: unknown plan kind %d", h, p.kind);
+    }
+  }
+  minf_status s;
+  if (any_vs && (s = check_ws(workspace, ws_bytes, minf_sparse_attn_workspace_size(n, hq))) != MINF_OK) return s;
+  // the attention call's block-offset bitmaps, at the same place in the workspace
+  const size_t words = 2 * bitmap_words(n);
+  std::vector<const int32_t*> vs_s;
+  std::vector<int32_t> vs_k;
+  std::vector<uint32_t*> vs_bits;
+  for (int h = 0; h < hq; ++h) {
+    if (plans[h].kind != MINF_KIND_VS) continue;
+    vs_s.push_back(plans[h].s_idx);
+    vs_k.push_back(plans[h].k_s);
+    vs_bits.push_back((uint32_t*)workspace + (size_t)h * words);
+  }
+  if (!vs_s.empty()) {
+    hipError_t e = launch_vs_offset_bits(vs_s.data(), vs_k.data(), vs_bits.data(), (int)vs_s.size(), (int)n, stream);
+    if (e != hipSuccess) return hip_fail(e, "VS offset bitmap kernel");
+  }
+  for (int h0 = 0; h0 < hq; h0 += kMaxLaunchHeads) {
+    WorkLaunch a{};
+    const int cnt = std::min(kMaxLaunchHeads, hq - h0);
+    for (int i = 0; i < cnt; ++i) {
+      const minf_head_plan& p = plans[h0 + i];
+      WorkHead& w = a.heads[i];
+      w.kind = p.kind;
+      w.sink = p.sink;
+      w.local = p.local;
+      w.k_v = p.kind == MINF_KIND_VS ? p.k_v : 0;
+      w.v_idx = p.v_idx;
+      w.obits = p.kind == MINF_KIND_VS ? (const uint32_t*)workspace + (size_t)(h0 + i) * words : nullptr;
+      w.blk_cnt = p.blk_cnt;
+    }
+    a.n = (int)n;
+    a.nb = (int)nblocks(n);
+    a.out = work + h0;
+    hipError_t e = launch_plan_work(a, cnt, stream);
+    if (e != hipSuccess) return hip_fail(e, "plan work kernel");
+  }
+  return MINF_OK;
+}
+
+minf_status minf_attention_recall(const float* lse_mask, const float* lse_dense, int64_t n, int hq,
+                                  const int32_t* rows, int n_rows, double* recall, hipStream_t stream) {
+  g_detail.clear();
+  if (!lse_mask || !lse_dense || !recall) return fail(MINF_E_INVALID_ARG, "lse_mask, lse_dense and recall must be non-null");
+  if (n < 1 || n > ((int64_t)1 << 30)) return fail(MINF_E_INVALID_ARG, "n must be in [1, 2^30] (got %lld)", (long long)n);
+  if (hq < 1) return fail(MINF_E_INVALID_ARG, "hq must be >= 1");
+  if (rows && n_rows < 1) return fail(MINF_E_INVALID_ARG, "n_rows must be >= 1 when rows is given");
+  const int nr = rows ? n_rows : (int)n;
+  hipError_t e = launch_recall(lse_mask, lse_dense, (int)n, hq, rows, nr, recall, stream);
+  if (e != hipSuccess) return hip_fail(e, "recall kernel");
+  return MINF_OK;
+}
+
 minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o, float* lse, int64_t n, int hq,
                             int hkv, int d, float scale, int causal, hipStream_t stream) {
   g_detail.clear();
@@ -835,3 +919,4 @@ minf_status minf_dense_decode(const void* q, const void* k, const void* v, int64
 }
 
 }  // extern "C"
+

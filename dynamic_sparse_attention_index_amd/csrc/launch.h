@@ -169,4 +169,21 @@ hipError_t launch_block_minmax(const int32_t* pos, int n, int32_t* bmin, int32_t
 hipError_t launch_permute_rows(const void* x, void* out, int heads, int64_t n, int row_bytes, const int32_t* src,
                                int scatter, hipStream_t stream);
 
+// Work of plans in the sparse kernel's unit, and attention recall (pattern search).
+enum : int32_t { KIND_W_DENSE = 0, KIND_W_ASHAPE = 1, KIND_W_VS = 2, KIND_W_BLOCK = 3 };
+struct WorkHead {
+  int32_t kind, sink, local, k_v;
+  const int32_t* v_idx;    // VS: ascending columns
+  const uint32_t* obits;   // VS: block-offset bitmaps (full blocks, then a partial last block)
+  const int32_t* blk_cnt;  // BLOCK
+};
+struct WorkLaunch {
+  WorkHead heads[kMaxLaunchHeads];
+  int32_t n, nb;
+  double* out;  // [count] work of each head, in 64x64 blocks
+};
+hipError_t launch_plan_work(const WorkLaunch& a, int count, hipStream_t stream);
+hipError_t launch_recall(const float* lse_mask, const float* lse_dense, int n, int hq, const int32_t* rows,
+                         int n_rows, double* out, hipStream_t stream);
+
 }  // namespace minf

@@ -235,6 +235,43 @@ minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o
                             hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Offline pattern search support (MInference 1.0 article, "Method": each
+ * head's pattern is chosen offline by a kernel-aware search that compares
+ * candidates at their cost in the sparse kernel; talk transcript, MInference
+ * part: attention recall, the share of attention an index keeps).
+ * ---------------------------------------------------------------------- */
+
+/* Work of each head's plan in the sparse kernel's unit, summed over query
+ * blocks b = 0 .. n_b - 1: the 64-key blocks minf_sparse_attn computes for b
+ * plus every gathered vertical column as 1/64 of a block.
+ *   DENSE : c <= b.
+ *   ASHAPE: sink blocks c < ceil(sink / 64), c <= b, and window blocks from
+ *           the block of key 64 b - local + 1 up to b (none when local == 0).
+ *   VS    : Bs(b) (as in minf_sparse_attn), plus 1/64 for every column j of
+ *           v_idx (ascending, unique, in [0, n)) with j <= b's last row and
+ *           block(j) not in Bs(b).
+ *   BLOCK : blk_cnt[b].
+ * plans  host array [hq] as for minf_sparse_attn (index pointers on the device;
+ *        pos is ignored). MINF_KIND_VS_WINDOW plans: MINF_E_UNSUPPORTED.
+ * work   device double [hq]; exact (integer block and column counts).
+ * workspace / ws_bytes  at least minf_sparse_attn_workspace_size(n, hq) when a
+ *        VS plan is present (else may be NULL). n <= 2^20. */
+minf_status minf_plan_work(const minf_head_plan* plans, int64_t n, int hq, double* work, void* workspace,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Attention recall of each head's mask from the log-sum-exp rows of sparse
+ * and dense attention over the same inputs:
+ *   recall[h] = (1 / R) * sum over the R listed rows i of exp(lse_mask[h][i] -
+ *   lse_dense[h][i]), a row with lse_mask = -inf (empty mask) counting 0.
+ * exp(LSE_mask - LSE_dense) is the share of row i's causal softmax mass that
+ * lies inside the mask. fp64 accumulation in a fixed order.
+ * lse_mask, lse_dense  device float [hq][n]. rows  device int32 [n_rows] of
+ * row ids (entries outside [0, n) count 0), or NULL for every row (R = n).
+ * recall  device double [hq]. */
+minf_status minf_attention_recall(const float* lse_mask, const float* lse_dense, int64_t n, int hq,
+                                  const int32_t* rows, int n_rows, double* recall, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Sparse decoding with top-k block loads ("KV-cache-centric efficient
  * long-context methods" talk transcript: in decoding, loading the KV cache is
  * the bottleneck and can be done sparsely; decode attention splits into a

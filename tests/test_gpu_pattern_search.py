@@ -76,3 +76,50 @@ def test_pattern_search_gqa_ragged(gpu_lib):
     print(f"[case] pattern search GQA n={n}", flush=True)
     q, k, v, _ = planted_qkv(n, 4, 2, seed=77, device="cuda")
     _check(q, k, v, budget=600, rows=np.arange(0, n, 11))
+
+
+def _np(t):
+    return t.cpu().numpy().astype(np.int64)
+
+
+@pytest.mark.parametrize("n", [37, 64, 700, 1300, 4096 + 17])
+def test_plan_work_matches_oracle(gpu_lib, n):
+    """minf_plan_work against the oracle's work count (exact: integer block and column counts)."""
+    rng = np.random.default_rng(n)
+    nb = (n + 63) // 64
+    dev = "cuda"
+    plans = [dict(kind="dense")]
+    for sink, local in ((0, 100), (70, 1), (64, 200), (10, 0), (128, 4096), (65, 63), (65, 64), (65, 65)):
+        plans.append(dict(kind="ashape", sink=sink, local=local))
+    for ks, kv in ((7, 30), (0, 5), (3, 0), (n, n), (64, 64)):
+        si = np.sort(rng.choice(n, min(n, ks), replace=False))
+        vi = np.sort(rng.choice(n, min(n, kv), replace=False))
+        plans.append(dict(kind="vs", s_idx=torch.tensor(si, dtype=torch.int32, device=dev),
+                          v_idx=torch.tensor(vi, dtype=torch.int32, device=dev)))
+    cnt = rng.integers(1, 5, nb)
+    plans.append(dict(kind="block", blk_idx=torch.zeros((nb, 4), dtype=torch.int32, device=dev),
+                      blk_cnt=torch.tensor(cnt, dtype=torch.int32, device=dev)))
+    print(f"[case] plan work n={n}, {len(plans)} plans", flush=True)
+    got = gpu_lib.minf_plan_work(plans, n).cpu().numpy()
+    for h, p in enumerate(plans):
+        want = O.plan_blocks(_np_plan(p), n)
+        assert got[h] == want, (h, p["kind"], got[h], want)
+
+
+def test_attention_recall_reduction(gpu_lib):
+    """minf_attention_recall against the same reduction of the same LSE values in fp64 on the host."""
+    rng = np.random.default_rng(5)
+    hq, n = 3, 5000
+    ld = rng.normal(5.0, 1.0, (hq, n)).astype(np.float32)
+    lm = (ld - rng.exponential(0.5, (hq, n))).astype(np.float32)
+    lm[1, ::7] = -np.inf
+    lm[2, :] = -np.inf
+    rows = rng.integers(0, n, 777).astype(np.int32)
+    tm, td = torch.tensor(lm, device="cuda"), torch.tensor(ld, device="cuda")
+    for r in (None, rows):
+        got = gpu_lib.minf_attention_recall(tm, td, None if r is None else torch.tensor(r, device="cuda")).cpu().numpy()
+        idx = np.arange(n) if r is None else r
+        e = np.where(np.isneginf(lm[:, idx]), 0.0, np.exp(lm[:, idx].astype(np.float64) - ld[:, idx]))
+        want = e.mean(axis=1)
+        assert np.allclose(got, want, rtol=1e-12, atol=0), (got, want)
+    assert got[2] == 0.0
