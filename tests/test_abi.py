@@ -180,3 +180,83 @@ def test_permutation_entry_points_reject():
     plans = _plans(dict(kind=0, pos=0x10000), dict(kind=0))
     assert _sparse(plans) == INVALID
     assert LIB.minf_sparse_attn_workspace_size(4096, 2) >= 2 * 2 * 64 * 4
+
+
+# ---------------------------------------------------------------------------
+# the Python binding checks every tensor before the C call
+# ---------------------------------------------------------------------------
+def test_binding_rejects_host_tensors_and_unknown_kinds():
+    import torch
+    q = torch.zeros((2, 64, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        minf.minf_dense_attn(q, q[:1], q[:1])
+    with pytest.raises(ValueError):
+        minf.minf_build_vs_index(q, q[:1], [0])
+    with pytest.raises(ValueError):
+        minf.make_plans([dict(kind="diagonal")])
+    with pytest.raises(ValueError):
+        minf.make_plans([dict(kind="vs", v_idx=torch.zeros(3, dtype=torch.int32), s_idx=torch.zeros(3, dtype=torch.int32))])
+
+
+@pytest.mark.gpu
+def test_binding_rejects_mismatched_shapes(gpu_lib):
+    import torch
+    n, d = 256, 128
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    i32 = dict(dtype=torch.int32, device="cuda")
+    q = torch.zeros((4, n, d), **bf)
+    k = torch.zeros((2, n, d), **bf)
+    bad = [
+        lambda: gpu_lib.minf_dense_attn(q, torch.zeros((2, n + 64, d), **bf), k),          # k of another length
+        lambda: gpu_lib.minf_dense_attn(q, k, torch.zeros((1, n, d), **bf)),               # v not shaped like k
+        lambda: gpu_lib.minf_dense_attn(q, k, k, out=torch.zeros((4, n - 1, d), **bf)),     # out
+        lambda: gpu_lib.minf_dense_attn(q, k, k, lse=torch.zeros((4, n + 1), dtype=torch.float32, device="cuda")),
+        lambda: gpu_lib.minf_dense_attn(q, k, k, lse=torch.zeros((4, n), **bf)),            # lse dtype
+        lambda: gpu_lib.minf_dense_attn(q, k.float(), k),                                   # k dtype
+        lambda: gpu_lib.minf_sparse_attn(q, k, k, [dict(kind="block", blk_idx=torch.zeros((3, 2), **i32),
+                                                        blk_cnt=torch.zeros((3,), **i32))] * 4),   # rows != n_b
+        lambda: gpu_lib.minf_sparse_attn(q, k, k, [dict(kind="block", blk_idx=torch.zeros((4, 2), **i32),
+                                                        blk_cnt=torch.zeros((5,), **i32))] * 4),   # counts
+        lambda: gpu_lib.minf_sparse_attn(q, k, k, [dict(kind="block", blk_idx=torch.zeros((4, 2), **i32),
+                                                        blk_cnt=torch.zeros((4,), **i32),
+                                                        pos=torch.zeros((n - 1,), **i32))] * 4),   # pos length
+        lambda: gpu_lib.minf_sparse_attn(q, k, k, [dict(kind="vs", v_idx=torch.zeros((2, 2), **i32),
+                                                        s_idx=torch.zeros((2,), **i32))] * 4),     # 2-D v_idx
+        lambda: gpu_lib.minf_sparse_attn(q, k, k, [dict(kind="dense")] * 3),                       # plan count
+        lambda: gpu_lib.minf_build_vs_index(q, k, [0], k_v=8, k_s=8, out=(torch.zeros((1, 7), **i32),
+                                                                           torch.zeros((1, 8), **i32))),
+        lambda: gpu_lib.minf_build_block_index(q, k, [0], k_b=4, out=(torch.zeros((1, 4, 3), **i32),
+                                                                       torch.zeros((1, 4), **i32))),
+        lambda: gpu_lib.minf_build_permuted_block_index(q, k, [0], torch.zeros((n + 1,), **i32), k_b=4),
+        lambda: gpu_lib.minf_permute_rows(q, torch.zeros((n - 1,), **i32)),
+        lambda: gpu_lib.minf_decode_pool_keys(k, out=torch.zeros((2, d, 3), dtype=torch.float32, device="cuda")),
+        lambda: gpu_lib.minf_sparse_decode(q[:, 0].contiguous(), k, k, torch.zeros((2, d, 3), dtype=torch.float32,
+                                                                       device="cuda"), 2),          # kbar_t
+        lambda: gpu_lib.minf_sparse_decode(q[:, 0].contiguous(), k, k, None, 4,
+                                           blk_idx=torch.zeros((4, 3), **i32)),                    # blk_idx
+        lambda: gpu_lib.minf_dense_decode(q[:, 0].contiguous(), k, k, out=torch.zeros((4, 64), **bf)),
+    ]
+    for i, fn in enumerate(bad):
+        with pytest.raises(ValueError):
+            fn()
+            print("accepted case", i)
+
+
+@pytest.mark.gpu
+def test_binding_side_stream_matches_current_stream(gpu_lib):
+    # outputs and workspaces allocated for a side stream: same results as on the current stream
+    import torch
+    from workload import planted_qkv
+    q, k, v, _ = planted_qkv(2048 + 64, 4, 2, seed=31, device="cuda")
+    vi, si = gpu_lib.minf_build_vs_index(q, k, [0, 1, 2, 3], k_v=64, k_s=64)
+    plans = [dict(kind="vs", v_idx=vi[h], s_idx=si[h]) for h in range(4)]
+    o0, l0 = gpu_lib.minf_sparse_attn(q, k, v, plans)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    vi1, si1 = gpu_lib.minf_build_vs_index(q, k, [0, 1, 2, 3], k_v=64, k_s=64, stream=side)
+    plans1 = [dict(kind="vs", v_idx=vi1[h], s_idx=si1[h]) for h in range(4)]
+    o1, l1 = gpu_lib.minf_sparse_attn(q, k, v, plans1, stream=side)
+    side.synchronize()
+    assert torch.equal(vi, vi1) and torch.equal(si, si1)
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)

@@ -152,7 +152,34 @@ def test_c4_gqa_mixed_512k(gpu_lib):
 def test_c5_gqa_all_vs_1m(gpu_lib):
     L = _run_layer(gpu_lib, "c5_gqa_1m_vs")
     _check_vs_index(L, [0])
-    _check_attention(L, [0, 13, 31], 1, seed=7)
+    # every head: its first and last query blocks and one seeded block in between
+    _check_attention(L, list(range(32)), 1, seed=7)
+
+
+@pytest.mark.parametrize("name,heads", [("c3_gqa_128k", list(range(32))),
+                                        ("c5_gqa_1m_vs", [0, 5, 10, 15, 16, 21, 26, 31])])
+def test_vs_index_exact_at_planted_counts(gpu_lib, name, heads):
+    """Budgets equal to the planted counts (k_v = 8 columns per KV group, k_s = 4 offsets),
+    on the workload's own data and row length: the planted items stand far above the rest,
+    so every list is unambiguous under the margin rule and must equal the oracle's exactly
+    (MInference 1.0 article, "Method": the VS index from the last queries' attention)."""
+    cfg = CONFIGS[name]
+    n, hq, hkv = cfg["n"], cfg["hq"], cfg["hkv"]
+    print(f"[case] {name}: exact VS index, k_v=8 k_s=4, heads {heads}", flush=True)
+    q, k, _, info = planted_qkv(n, hq, hkv, seed=1000 + cfg["index"], device="cuda")
+    vi, si = gpu_lib.minf_build_vs_index(q, k, heads, last_q=64, k_v=8, k_s=4, scale=SCALE)
+    torch.cuda.synchronize()
+    vi, si = vi.cpu().numpy(), si.cpu().numpy()
+    planted_cols = planted_offs = 0
+    for t, h in enumerate(heads):
+        g = h // (hq // hkv)
+        wvi, wsi, wv, ws = O.vs_index(to_np(q[h]), to_np(k[g]), 64, 8, 4, SCALE)
+        assert check_topk(wv, vi[t], 8, abs_tol=1e-7, want=wvi), (h, "verticals ambiguous")
+        assert check_topk(ws, si[t], 4, abs_tol=1e-7, want=wsi), (h, "slashes ambiguous")
+        planted_cols += len(set(info.columns[g]) & set(vi[t].tolist()))
+        planted_offs += len(set(info.offsets) & set(si[t].tolist()))
+    print(f"  {len(heads)} heads exact; planted columns in the top 8: {planted_cols}/{8 * len(heads)}, "
+          f"planted offsets in the top 4: {planted_offs}/{4 * len(heads)}", flush=True)
 
 
 def test_c3_structured_latent_128k(gpu_lib):
