@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -920,3 +921,71 @@ minf_status minf_dense_decode(const void* q, const void* k, const void* v, int64
 
 }  // extern "C"
 
+
+// ---------------- decoding without allocation
+// Callers that cannot allocate device memory (code under graph capture, tight
+// serving loops) use minf_sparse_decode_noalloc: its scratch is this
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+namespace {
+
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+minf_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MINF_E_UNSUPPORTED, "device %d is beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch symbol address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MINF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t minf_decode_noalloc_max_bytes(void) { return kDecodeScratchBytes; }
+
+minf_status minf_sparse_decode_noalloc(const void* q, const void* k, const void* v, const float* kbar_t, int64_t n,
+                                       int hq, int hkv, int d, float scale, int k_b, int32_t* blk_idx, void* o,
+                                       float* lse, hipStream_t stream) {
+  g_detail.clear();
+  minf_status s;
+  if ((s = check_decode(q, k, v, o, n, hq, hkv, d, scale)) != MINF_OK) return s;
+  if (k_b < 1) return fail(MINF_E_INVALID_ARG, "k_b must be >= 1");
+  const int64_t nb = nblocks(n);
+  const bool select = k_b < nb;
+  const int kb_eff = (int)std::min<int64_t>(k_b, nb);
+  if (select && !kbar_t) return fail(MINF_E_INVALID_ARG, "kbar_t must be non-null when k_b < n_b");
+  const size_t need = carve_decode(nullptr, n, hq, kb_eff, select).bytes;
+  if (need > kDecodeScratchBytes)
+    return fail(MINF_E_UNSUPPORTED, "this decode step needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kDecodeScratchBytes);
+  void* base = nullptr;
+  if ((s = scratch_for_current_device(&base)) != MINF_OK) return s;
+  // every scratch word a kernel reads was written earlier in the same call: nothing to clear
+  const DecWs w = carve_decode(base, n, hq, kb_eff, select);
+  if ((s = run_decode(q, k, v, kbar_t, n, hq, hkv, scale, kb_eff, select, blk_idx, o, lse, w, stream)) != MINF_OK)
+    return s;
+  if (!select && blk_idx) {
+    hipError_t e = launch_iota_rows(blk_idx, hq, kb_eff, stream);
+    if (e != hipSuccess) return hip_fail(e, "full block list");
+  }
+  return MINF_OK;
+}
+
+}  // extern "C"

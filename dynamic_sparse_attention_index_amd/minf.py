@@ -76,6 +76,8 @@ def _load():
         "minf_dense_decode": (i32, [vp, vp, vp, i64, i32, i32, i32, f32, vp, vp, vp, sz, vp]),
         "minf_plan_work": (i32, [ctypes.POINTER(HeadPlan), i64, i32, vp, vp, sz, vp]),
         "minf_attention_recall": (i32, [vp, vp, i64, i32, vp, i32, vp, vp]),
+        "minf_decode_noalloc_max_bytes": (sz, []),
+        "minf_sparse_decode_noalloc": (i32, [vp, vp, vp, vp, i64, i32, i32, i32, f32, i32, vp, vp, vp, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -482,3 +484,23 @@ def minf_attention_recall(lse_mask, lse_dense, rows=None, stream=None):
     out = _empty((hq,), torch.float64, lse_mask.device, s)
     _check(_lib.minf_attention_recall(_ptr(lse_mask), _ptr(lse_dense), n, hq, _ptr(rows), nr, _ptr(out), _stream(s)))
     return out
+
+
+def minf_sparse_decode_noalloc(q, k, v, kbar_t, k_b, out, lse, blk_idx=None, scale=None, stream=None):
+    """minf_sparse_decode with the library's static scratch: no allocation by the library or here.
+
+    out [hq, d] bf16, lse [hq] float32 and the optional blk_idx [hq, min(k_b, n_b)] int32 are the
+    caller's (preallocated) tensors; returns (out, lse, blk_idx).
+    """
+    hq, d, hkv, n = _decode_args(q, k, v)
+    s = _stream_of(stream)
+    nb = (n + 63) // 64
+    if kbar_t is not None:
+        _need(kbar_t, torch.float32, "kbar_t", shape=(hkv, d, nb), device=q.device)
+    _need(out, torch.bfloat16, "out", shape=tuple(q.shape), device=q.device)
+    _need(lse, torch.float32, "lse", shape=(hq,), device=q.device)
+    if blk_idx is not None:
+        _need_out(blk_idx, (hq, min(int(k_b), nb)), "blk_idx", q.device)
+    _check(_lib.minf_sparse_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(kbar_t), n, hq, hkv, d, _scale(scale, d),
+                                           int(k_b), _ptr(blk_idx), _ptr(out), _ptr(lse), _stream(s)))
+    return out, lse, blk_idx

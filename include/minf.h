@@ -314,6 +314,27 @@ minf_status minf_dense_decode(const void* q, const void* k, const void* v, int64
                               float scale, void* o, float* lse, void* workspace, size_t ws_bytes,
                               hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Sparse decoding without allocation, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and errors as minf_sparse_decode, without the
+ * workspace: the scratch lives in a static device array of the library,
+ * minf_decode_noalloc_max_bytes() bytes on each GPU, held until the process
+ * ends. A step whose scratch (minf_decode_workspace_size(n, hq, k_b)) exceeds
+ * it returns MINF_E_UNSUPPORTED. The call itself allocates nothing (no
+ * hipMalloc, no library allocation). Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (two streams, two threads) race and
+ * must be ordered by the caller. The scratch keeps the last call's contents;
+ * no call relies on them (each kernel writes every scratch word it later
+ * reads).
+ * ---------------------------------------------------------------------- */
+size_t minf_decode_noalloc_max_bytes(void);
+minf_status minf_sparse_decode_noalloc(const void* q, const void* k, const void* v, const float* kbar_t, int64_t n,
+                                       int hq, int hkv, int d, float scale, int k_b, int32_t* blk_idx, void* o,
+                                       float* lse, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
