@@ -53,7 +53,12 @@ def parse():
     ap.add_argument("--search", action="store_true", help="also time the offline pattern search on the input")
     ap.add_argument("--decode-blocks", type=int, default=64,
                     help="decode budget in 64-token blocks (64 blocks = 4096 tokens)")
-    ap.add_argument("--dense-runs", type=int, default=1)
+    ap.add_argument("--dense-runs", type=int, default=3, help="timed dense runs (after one untimed warm-up)")
+    ap.add_argument("--layers", default="c3_gqa_128k,c4_gqa_512k",
+                    help="further mixed-pattern layers measured after the headline ('' for none)")
+    ap.add_argument("--layer-steps", type=int, default=3, help="timed steps of each further layer")
+    ap.add_argument("--only-index", action="store_true",
+                    help="time only the index build of the workload (for counter runs of the index kernels)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -218,8 +223,19 @@ def profiled_traffic(workload):
 
 
 # ---------------------------------------------------------------- CPU oracle sample
-def cpu_baseline(q, k, v, kinds, cfg, plans_gpu, n, blocks_per_head):
-    """Time the fp64 oracle on a bounded sample and scale it to one layer."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(q, k, v, kinds, cfg, plans_gpu, n):
+    """Time the fp64 oracle: the index build of every head in full, and the sparse attention
+    of a sample of query blocks of one head, extrapolated to the layer."""
     import numpy as np
     import oracle as O
     try:
@@ -228,20 +244,35 @@ def cpu_baseline(q, k, v, kinds, cfg, plans_gpu, n, blocks_per_head):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     scale = 1 / math.sqrt(128)
+    grp = cfg["hq"] // cfg["hkv"]
+    # index build, every head at full length (the VS estimate reads the last queries and all keys)
+    t_index = 0.0
+    n_vs = n_bs = 0
+    for g in range(cfg["hkv"]):
+        kg = None
+        for h in range(g * grp, (g + 1) * grp):
+            if kinds[h] not in ("vs", "block"):
+                continue
+            if kg is None:
+                kg = k[g].float().cpu().numpy()
+            qh = q[h].float().cpu().numpy()
+            t1 = time.perf_counter()
+            if kinds[h] == "vs":
+                O.vs_index(qh, kg, cfg["last_q"], cfg["k_v"], cfg["k_s"], scale)
+                n_vs += 1
+            else:
+                O.block_index(qh, kg, cfg["k_b"])
+                n_bs += 1
+            t_index += time.perf_counter() - t1
+        del kg
+    # attention: first, last and 14 seeded query blocks of one head, scaled to every block of every head
     h = kinds.index("vs") if "vs" in kinds else 0
-    g = h // (cfg["hq"] // cfg["hkv"])
+    g = h // grp
     qh = q[h].float().cpu().numpy()
     kg = k[g].float().cpu().numpy()
     vg = v[g].float().cpu().numpy()
-    t0 = time.perf_counter()
-    reps = 0
-    while kinds[h] == "vs" and (reps == 0 or time.perf_counter() - t0 < 3.0):
-        O.vs_index(qh, kg, cfg["last_q"], cfg["k_v"], cfg["k_s"], scale)
-        reps += 1
-    t_index = (time.perf_counter() - t0) / max(reps, 1)
     nb = (n + 63) // 64
     rng = np.random.default_rng(0)
-    # first, last and 14 seeded query blocks (about 10-20 s of CPU work at 1M tokens)
     mid = rng.choice(np.arange(1, nb - 1), size=min(14, max(nb - 2, 0)), replace=False).tolist()
     sample_blocks = sorted({0, nb - 1, *mid})
     p = plans_gpu[h]
@@ -251,19 +282,140 @@ def cpu_baseline(q, k, v, kinds, cfg, plans_gpu, n, blocks_per_head):
         rows = np.arange(64 * b, min(64 * b + 64, n))
         O.sparse_attn(qh[None], kg[None], vg[None], 1, 1, scale, [plan], rows=rows)
     t_attn = time.perf_counter() - t0
-    # scale: index cost per VS head; attention cost per query block of the layer
-    n_vs = sum(1 for x in kinds if x == "vs")
-    layer_s = t_index * n_vs + (t_attn / len(sample_blocks)) * nb * len(kinds)
+    attn_layer_s = (t_attn / len(sample_blocks)) * nb * len(kinds)
     return {
-        "value": layer_s * 1e3,
-        "unit": "ms/layer (extrapolated)",
+        "value": (t_index + attn_layer_s) * 1e3,
+        "unit": "ms/layer (index timed in full, attention extrapolated)",
         "cores": int(cores),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: VS index of 1 head at N={n} ({t_index:.1f} s per head) and sparse attention "
-                   f"of {len(sample_blocks)} query blocks of that head ({t_attn:.1f} s); scaled to {n_vs} "
-                   f"VS-index heads and {nb} query blocks x {len(kinds)} heads"),
-        "sample_seconds": round(t_index * max(reps, 1) + t_attn, 2),
+        "index_s": round(t_index, 2),
+        "attention_extrapolated_s": round(attn_layer_s, 1),
+        "sample": (f"fp64 NumPy oracle on {cores} threads: the index of all {n_vs} VS and {n_bs} BS heads at "
+                   f"N={n} timed in full ({t_index:.1f} s), and sparse attention of {len(sample_blocks)} query "
+                   f"blocks of head {h} ({t_attn:.1f} s) scaled to {nb} query blocks x {len(kinds)} heads"),
+        "sample_seconds": round(t_index + t_attn, 2),
     }
+
+
+def plans_for(kinds, cfg, vs_heads, bs_heads, vi, si, bi, bc):
+    plans = []
+    for h, kd in enumerate(kinds):
+        if kd == "vs":
+            t = vs_heads.index(h)
+            plans.append(dict(kind="vs", v_idx=vi[t], s_idx=si[t]))
+        elif kd == "block":
+            t = bs_heads.index(h)
+            plans.append(dict(kind="block", blk_idx=bi[t], blk_cnt=bc[t]))
+        else:
+            plans.append(dict(kind="ashape", sink=cfg["sink"], local=cfg["local"]))
+    return plans
+
+
+def layer_work(plans, n, cfg):
+    """(blocks, columns, density per kind) of a layer's plans."""
+    nb = (n + 63) // 64
+    a_blocks = None
+    blocks = cols = 0
+    per_kind = {}
+    for p in plans:
+        if p["kind"] == "vs":
+            b_, c_ = vs_work(p["v_idx"], p["s_idx"], n)
+        elif p["kind"] == "block":
+            b_, c_ = int(p["blk_cnt"].long().sum()), 0
+        else:
+            if a_blocks is None:
+                a_blocks = ashape_blocks(n, cfg["sink"], cfg["local"])
+            b_, c_ = a_blocks, 0
+        blocks += b_
+        cols += c_
+        pk = per_kind.setdefault(p["kind"], [0, 0, 0])
+        pk[0] += b_
+        pk[1] += c_
+        pk[2] += 1
+    dens = {kd: round((bk + cl / 64) / (cnt * nb * (nb + 1) / 2), 4) for kd, (bk, cl, cnt) in per_kind.items()}
+    return blocks, cols, dens
+
+
+def layer_leg(name, steps, dense_runs, no_dense):
+    """One further layer of the pages' length range: the whole step (index of every VS and BS head
+    from the data, one sparse attention launch) timed over `steps` after a warm-up, its work, and
+    the dense kernel on the same inputs (one warm-up, then `dense_runs` timed runs)."""
+    import torch
+
+    from dynamic_sparse_attention_index_amd import minf
+    from workload import CONFIGS, config_kinds, planted_qkv
+    cfg = CONFIGS[name]
+    n, hq, hkv = cfg["n"], cfg["hq"], cfg["hkv"]
+    kinds = config_kinds(name)
+    scale = 1 / math.sqrt(128)
+    q, k, v, _ = planted_qkv(n, hq, hkv, seed=1000 + cfg["index"], device="cuda")
+    dev = q.device
+    vs_heads = [h for h in range(hq) if kinds[h] == "vs"]
+    bs_heads = [h for h in range(hq) if kinds[h] == "block"]
+    lib = minf.library()
+    ws_vs = torch.empty(max(1, lib.minf_vs_index_workspace_size(n, len(vs_heads))), dtype=torch.uint8, device=dev)
+    ws_bs = torch.empty(max(1, lib.minf_block_index_workspace_size(n, hq, hkv, len(bs_heads))), dtype=torch.uint8,
+                        device=dev)
+    ws_at = torch.empty(max(1, lib.minf_sparse_attn_workspace_size(n, hq)), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((hq, n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    st = {}
+
+    def step(record=None):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        st["vi"] = st["si"] = st["bi"] = st["bc"] = None
+        if vs_heads:
+            st["vi"], st["si"] = minf.minf_build_vs_index(q, k, vs_heads, last_q=cfg["last_q"], k_v=cfg["k_v"],
+                                                          k_s=cfg["k_s"], scale=scale, workspace=ws_vs)
+        if bs_heads:
+            st["bi"], st["bc"] = minf.minf_build_block_index(q, k, bs_heads, k_b=cfg["k_b"], workspace=ws_bs)
+        e[1].record(stream)
+        plans = plans_for(kinds, cfg, vs_heads, bs_heads, st["vi"], st["si"], st["bi"], st["bc"])
+        minf.minf_sparse_attn(q, k, v, minf.make_plans(plans, n=n, device=dev), scale=scale, out=o, lse=lse,
+                              workspace=ws_at)
+        e[2].record(stream)
+        if record is not None:
+            record.append(e)
+        return plans
+
+    step()
+    torch.cuda.synchronize()
+    recs = []
+    for _ in range(max(1, steps)):
+        plans = step(recs)
+    torch.cuda.synchronize()
+    idx_ms = sum(a.elapsed_time(b) for a, b, _ in recs) / len(recs)
+    attn_ms = sum(b.elapsed_time(c) for _, b, c in recs) / len(recs)
+    step_ms = sum(a.elapsed_time(c) for a, _, c in recs) / len(recs)
+    blocks, cols, dens = layer_work(plans, n, cfg)
+    flop = blocks * BLOCK_FLOP + cols * COL_FLOP
+    nb = (n + 63) // 64
+    out = {"tokens": n, "patterns": {kd: kinds.count(kd) for kd in sorted(set(kinds))}, "steps": len(recs),
+           "warmup": 1, "step_ms": round(step_ms, 3), "index_ms": round(idx_ms, 3), "attn_ms": round(attn_ms, 3),
+           "attn_tflops": round(flop / (attn_ms * 1e-3) / 1e12, 1),
+           "mfma_frac": round(flop / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "computed_blocks": blocks, "gathered_columns": cols, "density": dens}
+    if not no_dense:
+        minf.minf_dense_attn(q, k, v, scale=scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(max(1, dense_runs)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            minf.minf_dense_attn(q, k, v, scale=scale, out=o, lse=lse)
+            b.record(stream)
+            runs.append((a, b))
+        torch.cuda.synchronize()
+        dense_ms = sum(a.elapsed_time(b) for a, b in runs) / len(runs)
+        out["dense"] = {"ms": round(dense_ms, 2), "runs": len(runs), "warmup": 1,
+                        "tflops": round(hq * nb * (nb + 1) // 2 * BLOCK_FLOP / (dense_ms * 1e-3) / 1e12, 1),
+                        "speedup_step": round(dense_ms / step_ms, 3)}
+    del q, k, v, o, lse, ws_vs, ws_bs, ws_at, st
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -339,12 +491,30 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    if args.only_index:
+        # the index build alone (VS and BS heads from the data), e.g. under a counter profiler
+        for _ in range(args.warmup):
+            build_index()
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            build_index()
+            b.record(stream)
+            reps.append((a, b))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in reps) / len(reps)
+        print(json.dumps({"workload": args.config, "index_only": True, "steps": args.steps, "warmup": args.warmup,
+                          "index_ms": round(ms, 3), "vs_heads": len(vs_heads), "bs_heads": len(bs_heads)}))
+        return
+
     def step(record=None):
         e0, e1, e2 = ev(), ev(), ev()
         e0.record(stream)
         build_index()
         e1.record(stream)
-        plans = minf.make_plans(plans_from_state())
+        plans = minf.make_plans(plans_from_state(), n=n, device=dev)
         minf.minf_sparse_attn(q, k, v, plans, scale=scale, out=o, lse=lse, workspace=ws_at)
         e2.record(stream)
         if record is not None:
@@ -425,7 +595,7 @@ def main():
                 inj_plans.append(dict(kind="vs", v_idx=vi_l[t], s_idx=si_l[t]))
             else:
                 inj_plans.append(plans_t[h])
-        cp = minf.make_plans(inj_plans)
+        cp = minf.make_plans(inj_plans, n=n, device=dev)
         minf.minf_sparse_attn(q, k, v, cp, scale=scale, out=o, lse=lse, workspace=ws_at)
         torch.cuda.synchronize()
         reps = []
@@ -465,7 +635,7 @@ def main():
         def window_leg(plans_x, ref_ms):
             pw = [dict(kind="vs_window", v_idx=p["v_idx"], s_idx=p["s_idx"]) if p["kind"] == "vs" else p
                   for p in plans_x]
-            cpw = minf.make_plans(pw)
+            cpw = minf.make_plans(pw, n=n, device=dev)
             minf.minf_sparse_attn(q, k, v, cpw, scale=scale, out=o, lse=lse, workspace=ws_at)
             torch.cuda.synchronize()
             reps_w = []
@@ -512,7 +682,7 @@ def main():
             e0.record(stream)
             build_index(q2, k2, st2)
             e1.record(stream)
-            cp2 = minf.make_plans(plans_from_state(st2))
+            cp2 = minf.make_plans(plans_from_state(st2), n=n, device=dev)
             minf.minf_sparse_attn(q2, k2, v2, cp2, scale=scale, out=o, lse=lse, workspace=ws_at)
             e2.record(stream)
             if record is not None:
@@ -557,8 +727,10 @@ def main():
 
     dense = None
     if not args.no_dense:
+        minf.minf_dense_attn(q, k, v, scale=scale, out=o, lse=lse)  # untimed warm-up
+        torch.cuda.synchronize()
         runs = []
-        for _ in range(args.dense_runs):
+        for _ in range(max(1, args.dense_runs)):
             a, b = ev(), ev()
             a.record(stream)
             minf.minf_dense_attn(q, k, v, scale=scale, out=o, lse=lse)
@@ -567,7 +739,7 @@ def main():
         torch.cuda.synchronize()
         dense_ms = sum(a.elapsed_time(b) for a, b in runs) / len(runs)
         dense = {
-            "ms": round(dense_ms, 2),
+            "ms": round(dense_ms, 2), "runs": max(1, args.dense_runs), "warmup": 1,
             "tflops": round(dense_blocks * BLOCK_FLOP / (dense_ms * 1e-3) / 1e12, 1),
             "speedup_step": round(dense_ms / step_ms, 3),
             "speedup_attention": round(dense_ms / attn_ms, 3),
@@ -607,7 +779,8 @@ def main():
             vp = minf.minf_permute_rows(vg, src)
             bi, bc = minf.minf_build_permuted_block_index(qp, kp, heads_all, src, k_b=k_b)
             e1.record(stream)
-            plans_g = minf.make_plans([dict(kind="block", blk_idx=bi[h], blk_cnt=bc[h], pos=src) for h in heads_all])
+            plans_g = minf.make_plans([dict(kind="block", blk_idx=bi[h], blk_cnt=bc[h], pos=src) for h in heads_all],
+                                       n=n, device=dev)
             op, lp = minf.minf_sparse_attn(qp, kp, vp, plans_g, scale=scale, workspace=ws_at)
             e2.record(stream)
             minf.minf_permute_rows(op, src, scatter=True, out=og)
@@ -630,7 +803,7 @@ def main():
         lse_perm = lg.clone()
         # the same budget in the original order
         bj, bd = minf.minf_build_block_index(qg, kg, heads_all, k_b=k_b)
-        plans_b = minf.make_plans([dict(kind="block", blk_idx=bj[h], blk_cnt=bd[h]) for h in heads_all])
+        plans_b = minf.make_plans([dict(kind="block", blk_idx=bj[h], blk_cnt=bd[h]) for h in heads_all], n=n, device=dev)
         a_, b_ = ev(), ev()
         a_.record(stream)
         _, lse_plain = minf.minf_sparse_attn(qg, kg, vg, plans_b, scale=scale, workspace=ws_at)
@@ -765,9 +938,21 @@ def main():
         }
         print(f"[bench] pattern search: {search_s:.2f} s, choices {picks}", file=sys.stderr, flush=True)
 
+    # further layers of the pages' length range (mixed pattern maps), after the headline
+    layers = [x for x in args.layers.split(",") if x and x != args.config] if args.layers else []
+    if layers:
+        extra["layers"] = {}
+        for name in layers:
+            t_l = time.perf_counter()
+            r = layer_leg(name, args.layer_steps, args.dense_runs, args.no_dense)
+            extra["layers"][name] = r
+            print(f"[bench] layer {name}: step {r['step_ms']:.2f} ms (index {r['index_ms']:.3f}, attention "
+                  f"{r['attn_ms']:.2f}), {r['attn_tflops']} TFLOP/s, density {r['density']}, dense "
+                  f"{r.get('dense', {}).get('ms')} ms ({time.perf_counter() - t_l:.1f} s)", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(q, k, v, kinds, cfg, plans_t, n, None)
+        cpu = cpu_baseline(q, k, v, kinds, cfg, plans_t, n)
         print(f"[bench] cpu oracle sample {cpu['sample_seconds']} s", file=sys.stderr, flush=True)
 
     out = {
@@ -782,7 +967,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic seeded N(0,1) Q/K/V with planted verticals and slashes; index built on device from the data",
+        "data": (f"synthetic seeded N(0,1) Q/K/V with planted verticals (8 columns per KV head, gain "
+                 f"Q += {info.vert_gain[0]:g} u, K[c] += {info.vert_gain[1]:g} u, calibrated; the literal recipe's "
+                 f"(1, 3) is not recoverable) and slashes (offsets {list(info.offsets)}, K_j += "
+                 f"{info.slash_gain:g} Q0_(j+d)); index built on device from the data"),
         "config": {"workload": args.config, "tokens": n, "q_heads": hq, "kv_heads": hkv, "head_dim": 128,
                    "patterns": {kd: kinds.count(kd) for kd in sorted(set(kinds))},
                    "budgets": {key: cfg[key] for key in ("last_q", "k_v", "k_s", "k_b", "sink", "local") if key in cfg},
