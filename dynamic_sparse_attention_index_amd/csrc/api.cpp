@@ -413,8 +413,9 @@ size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
 }
 
 // Launches of Vertical-Slash heads only, at long lengths, queue two launches
-// of the same work: a cooperative one in which the 64 workgroups of an XCD run
-// their items in rounds that start together, and an ordinary one. A flag
+// of the same work: a rounds one (exactly as many workgroups as the device
+// holds at once) in which the 64 workgroups of an XCD run their items in
+// rounds that start together, and an ordinary one. A flag
 // computed on the device from the offset bitmaps, without a host round trip,
 // lets exactly one of them work: rounds when the items are long (thousands of
 // key tiles), because workgroups that stay at the same key position keep
@@ -430,8 +431,9 @@ constexpr int kRoundsMinTiles = 1024;
 static bool rounds_enabled(hipStream_t stream) {
   const char* e = getenv("MINF_ATTN_ROUNDS");
   if (e != nullptr && e[0] == '0') return false;
-  // a stream being captured into a graph gets the ordinary launch only (a
-  // cooperative launch is not something every runtime can record)
+  // a stream being captured into a graph gets the ordinary launch only (the
+  // rounds launch's waits assume it has the device to itself, which a replay
+  // beside other graph work need not give)
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
     (void)hipGetLastError();

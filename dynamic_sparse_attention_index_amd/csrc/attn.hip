@@ -820,8 +820,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(const AttnLaunch p) {
   attn_item<XK>(p, ((slot / kChunk) * kXcds + xcd) * kChunk + slot % kChunk, sm, kt0, kt1, vt0, vt1);
 }
 
-// Rounds variant: exactly 8 x 64 workgroups, launched cooperatively so that
-// they are resident together. In round r workgroup L takes item
+// Rounds variant: exactly 8 x 64 workgroups, as many as the device holds at
+// once (two per CU), so that they are resident together. In round r workgroup L takes item
 // (r * 8 + L % 8) * C + L / 8, and the 64 workgroups of an XCD start every
 // round together: long items (thousands of key tiles) then stay near the same
 // key position and keep sharing K/V tiles in that XCD's L2. It works only
@@ -900,20 +900,21 @@ static const void* rounds_kernel_of(int xk) {
   }
 }
 
-// Whether this device keeps all 8 x 64 workgroups of a rounds launch resident
-// together (cooperative launches are supported and two workgroups fit per CU
-// on at least 256 CUs). Asked once per device and instantiation.
+// Whether this device holds all 8 x 64 workgroups of a rounds launch at once
+// (at least two per CU on at least 256 CUs). The launch is an ordinary one: its
+// per-XCD waits are bounded, so it ends even if some workgroups were not
+// resident together (only the L2 sharing would suffer). Asked once per device
+// and instantiation.
 static bool rounds_supported(int xk) {
   static int cache[4][64] = {};  // 0 unknown, 1 yes, 2 no
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   int& c = cache[xk & 3][dev];
   if (c == 0) {
-    int coop = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = 0, per_cu = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rounds_kernel_of(xk), kThreads, 0);
-    c = (e == hipSuccess && coop && (long long)cus * per_cu >= kXcds * kChunk) ? 1 : 2;
+    c = (e == hipSuccess && (long long)cus * per_cu >= kXcds * kChunk) ? 1 : 2;
   }
   return c == 1;
 }
@@ -941,12 +942,15 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
     hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, b.xcd_sync, kXcds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    void* args[] = {&b};
-    e = hipLaunchCooperativeKernel(rounds_kernel_of(xk), dim3(kXcds * kChunk), dim3(kThreads), args, 0, stream);
-    if (e == hipSuccess)
-      c.rounds_flag = a.rounds_flag;
-    else
-      (void)hipGetLastError();  // not launchable cooperatively here: the ordinary launch does all the work
+    const dim3 gr(kXcds * kChunk), tr(kThreads);
+    switch (xk) {
+      case 1: hipLaunchKernelGGL(attn_kernel_rounds<1>, gr, tr, 0, stream, b); break;
+      case 2: hipLaunchKernelGGL(attn_kernel_rounds<2>, gr, tr, 0, stream, b); break;
+      case 3: hipLaunchKernelGGL(attn_kernel_rounds<3>, gr, tr, 0, stream, b); break;
+      default: hipLaunchKernelGGL(attn_kernel_rounds<0>, gr, tr, 0, stream, b); break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    c.rounds_flag = a.rounds_flag;
   }
   const dim3 g((unsigned)grid), t(kThreads);
   switch (xk) {

@@ -217,8 +217,9 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
  * work items in rounds that start together (long items share K/V tiles in
  * L2) or as one ordinary launch; results are bitwise identical either way.
  * The environment variable MINF_ATTN_ROUNDS=0 (read on every call) keeps the
- * ordinary launch only, as does a stream that is being captured into a graph. The rounds launch is cooperative; where the device
- * refuses it, the ordinary launch does the work. */
+ * ordinary launch only, as does a stream that is being captured into a graph. The rounds launch
+ * has exactly as many workgroups as the device holds at once (two per CU); its
+ * waits are bounded, so it ends even if some were not resident together. */
 
 /* A BLOCK plan with pos != NULL describes a permuted sequence (q, k, v, o
  * and lse are all in the permuted row order): key block c may appear in any
