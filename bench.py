@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--layer-steps", type=int, default=3, help="timed steps of each further layer")
     ap.add_argument("--only-index", action="store_true",
                     help="time only the index build of the workload (for counter runs of the index kernels)")
+    ap.add_argument("--only-dense", action="store_true",
+                    help="time only the dense attention of the workload (for counter runs of the attention kernel)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device copy of this many MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -490,6 +492,27 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    if args.only_dense:
+        # the dense causal attention alone on the workload's inputs
+        for _ in range(args.warmup):
+            minf.minf_dense_attn(q, k, v, scale=scale, out=o, lse=lse)
+        torch.cuda.synchronize()
+        reps = []
+        for _ in range(args.steps):
+            a, b = ev(), ev()
+            a.record(stream)
+            minf.minf_dense_attn(q, k, v, scale=scale, out=o, lse=lse)
+            b.record(stream)
+            reps.append((a, b))
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in reps) / len(reps)
+        nb_ = (n + 63) // 64
+        tf = hq * nb_ * (nb_ + 1) // 2 * BLOCK_FLOP / (ms * 1e-3) / 1e12
+        print(json.dumps({"workload": args.config, "dense_only": True, "steps": args.steps, "warmup": args.warmup,
+                          "dense_ms": round(ms, 3), "tflops": round(tf, 1),
+                          "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}))
+        return
 
     if args.only_index:
         # the index build alone (VS and BS heads from the data), e.g. under a counter profiler

@@ -69,9 +69,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(const TopkLaunc
   __syncthreads();
   const int lo = blockIdx.x * a.chunk;
   const int hi = min(a.n, lo + a.chunk);
-  for (int i = lo + threadIdx.x; i < hi; i += kTopkThreads) {
-    const uint32_t u = sortable_key(rf.src[i]);
-    if ((u & pmask) == prefix) atomicAdd(&lh[(u >> kShift) & (kBins - 1)], 1);
+  // eight loads in flight per thread, then their histogram updates
+  for (int base = lo + threadIdx.x; base < hi; base += 8 * kTopkThreads) {
+    uint32_t u[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int i = base + x * kTopkThreads;
+      u[x] = i < hi ? sortable_key(rf.src[i]) : 0u;  // slots past the chunk are skipped below
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      if (base + x * kTopkThreads < hi && (u[x] & pmask) == prefix) atomicAdd(&lh[(u[x] >> kShift) & (kBins - 1)], 1);
   }
   __syncthreads();
   int* gh = a.hist + (size_t)r * kRadixBins;
@@ -148,10 +156,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_count_kernel(const TopkLaun
   const int lo = blockIdx.x * a.chunk;
   const int hi = min(a.n, lo + a.chunk);
   int gt = 0, eq = 0;
-  for (int i = lo + threadIdx.x; i < hi; i += kTopkThreads) {
-    const uint32_t u = sortable_key(rf.src[i]);
-    gt += u > thr;
-    eq += u == thr;
+  for (int base = lo + threadIdx.x; base < hi; base += 8 * kTopkThreads) {
+    uint32_t u[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int i = base + x * kTopkThreads;
+      u[x] = i < hi ? sortable_key(rf.src[i]) : 0u;  // key 0 (a NaN pattern) is below every real key
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const bool in = base + x * kTopkThreads < hi;
+      gt += in && u[x] > thr;
+      eq += in && u[x] == thr;
+    }
   }
   gt = block_sum(gt, wsum);
   eq = block_sum(eq, wsum);

@@ -13,10 +13,12 @@
 //  * S^T = K Q_last^T on 32x32x16 bf16 MFMA (fp32 accumulate);
 //  * pass 1 keeps per-lane running (max, sum of exp2) per query row; chunk
 //    partials are merged in a fixed chunk order (no float atomics);
-//  * pass 2 recomputes the scores, normalises them, and reduces the 64x64
-//    probability tile along columns (complete column sums) and along its 127
-//    diagonals (per-tile partials; a diagonal spans at most two tiles and the
-//    two partials are added in tile order by a separate kernel);
+//  * pass 2 recomputes the scores as S = Q_last K^T (so a lane holds one key
+//    column and 16 query rows of each 32x32 product), normalises them, sums
+//    the columns in registers (complete column sums), and reduces the 64x64
+//    probability tile along its 127 diagonals through LDS (per-tile partials;
+//    a diagonal spans at most two tiles and the two partials are added in
+//    tile order by a separate kernel);
 //  * top-k (topk.hip) is a radix select on the sortable bit pattern spread
 //    over many workgroups per row, ties to the lower index, emitted in
 //    ascending index order.
@@ -30,17 +32,29 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int KSTR = 136;
-constexpr int PSTR = 64;   // floats per probability-tile row in LDS (rows stored skewed)
-constexpr int PROWS = 32;  // query rows of the probability tile staged at a time
+// Staged probability rows, 16 query rows at a time (rows t = 16 h + tl of round
+// h): row tl holds key c at column q = c - tl + 16, in [1, 79]. A row writes the
+// same 64 columns in every round, so the ones it never writes stay zero, and
+// column q of round h holds exactly the entries of diagonal e = t - c + 63 =
+// 16 h + 79 - q. A row pitch of 89 floats puts the two half-waves' writes (rows
+// tl and tl + 4, the same 32 keys) on complementary halves of the 64 banks; a
+// row's columns are read by consecutive lanes.
+constexpr int PSTR = 89;
+constexpr int PROWS = 16;
+constexpr int PCOLS = 80;
 // s_waitcnt immediate on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVmem0 = 0x0F70;
 
+// K tiles are double-buffered: tile T + 1 is stored into the other buffer
+// while other waves may still read tile T, so one barrier per tile suffices.
 struct VsSmem1 {
-  uint16_t kt[kBlock * KSTR];
+  uint16_t kt[2][kBlock * KSTR];
 };
 struct VsSmem2 {
-  uint16_t kt[kBlock * KSTR];
-  float pt[4][PROWS * PSTR];
+  uint16_t kt[2][kBlock * KSTR];
+  float pt[4][PROWS * PSTR + 64];  // + 64: lanes 16..63 read past the 80 columns of the last row
+  float pacc[4][4 * PCOLS];          // per wave: column partials of the four rounds of a tile
+  float crow[4][64];                 // per wave: max + log2(sum) of each last-query row
 };
 
 template <int PASS>
@@ -74,14 +88,11 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
   }
   float run_m[2] = {-INFINITY, -INFINITY};
   float run_l[2] = {0.f, 0.f};
-  float rm[2] = {0.f, 0.f}, ril[2] = {0.f, 0.f};
-  if constexpr (PASS == 2) if (active) {
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int t = 32 * nt + r32;
-      rm[nt] = a.row_m[slot * 64 + t];
-      ril[nt] = a.row_il[slot * 64 + t];
-    }
+  // pass 2: each row's normaliser in log2 units, max + log2(sum), kept in LDS;
+  // the staging rows start at zero
+  if constexpr (PASS == 2) {
+    sm.crow[wave][lane] = active ? a.row_m[slot * 64 + lane] : 0.f;
+    for (int x = lane; x < PROWS * PSTR + 64; x += 64) sm.pt[wave][x] = 0.f;
   }
 
   // K tiles: 16 threads per 256-byte row, rows kr + 16 i; the next tile is
@@ -96,16 +107,16 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
       kn[i] = j < n ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](uint16_t* kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(sm.kt + (kr + 16 * i) * KSTR + 8 * dc) = kn[i];
+    for (int i = 0; i < 4; ++i) *(u32x4*)(kt + (kr + 16 * i) * KSTR + 8 * dc) = kn[i];
   };
 
   const int t0 = ch * a.tiles_per_chunk;
   const int t1 = t0 + a.tiles_per_chunk < a.ntiles ? t0 + a.tiles_per_chunk : a.ntiles;
   if (t0 < t1) {
     load_tile(t0);
-    store_tile();
+    store_tile(sm.kt[0]);
   }
   // the query operands (and the row statistics) have arrived on every path
   // into the loop, so that the loop's wait counts only cover the next K tile
@@ -113,6 +124,7 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
   __syncthreads();
   for (int T = t0; T < t1; ++T) {
     if (T + 1 < t1) load_tile(T + 1);
+    const uint16_t* ktc = sm.kt[(T - t0) & 1];
     // the causal mask only bites in tiles that reach past the first last-query row
     const bool edge = (int64_t)T * kBlock + kBlock - 1 > (int64_t)n - r;
     if constexpr (PASS == 1) if (active) {
@@ -121,7 +133,7 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
       for (int mt = 0; mt < 2; ++mt) {
         s[mt][0] = f32x16{};
         s[mt][1] = f32x16{};
-        const uint16_t* kp = sm.kt + (32 * mt + r32) * KSTR + 8 * g;
+        const uint16_t* kp = ktc + (32 * mt + r32) * KSTR + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           const u32x4 av = *(const u32x4*)(kp + 16 * ks);
@@ -159,73 +171,118 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
       }
     }
     if constexpr (PASS == 2) {
-      // normalised probabilities, staged 32 query rows at a time with row t
-      // rotated by t, so that every diagonal e = t - c + 63 of the tile lies in
-      // one LDS column; the column sum (lane = key) and the diagonal partials
-      // (lane = column s: diagonals 63 - s and 127 - s) run over t in ascending
-      // order across the two halves, each a 32-step loop with no divergence
+      // normalised probabilities P = exp2(s sl2 - crow) of S = Q K^T: lane l holds
+      // key c = 32 mk + (l & 31) and, in accumulator slot i, query row
+      // t = 32 mq + 8 (i >> 2) + 4 g + (i & 3). Column sums add up in registers
+      // (then across the two half-waves); for the diagonal sums every 16 rows go
+      // through LDS, where lane s adds up column s (and lanes s < 16 column
+      // s + 64) over the 16 rows: one partial per round and column, merged per
+      // diagonal after the tile.
       float* pt = sm.pt[wave];
-      float cs = 0.f;
-      float ds[2] = {0.f, 0.f};
+      // row tl (of these 16), column c - tl + 16, with c = 32 mk + r32 and
+      // tl = 8 (e >> 2) + 4 g + (e & 3), is pw + 32 mk + (PSTR - 1)(8 (e >> 2) + (e & 3)):
+      // one lane base and a constant offset per store, the same in every round
+      float* const pw = pt + r32 + 4 * g * (PSTR - 1) + 16;
+      float* const pr = pt + lane;
+      float cs[2] = {0.f, 0.f};
+      float acc[4][2];  // round h, column lane (0) / lane + 64 (1, lanes < 16)
+      // every row present and the tile below the causal edge: nothing is masked
+      const bool plain = !edge && r == 64;
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int mq = 0; mq < 2; ++mq) {
+        f32x16 sc[2];
         if (active) {
-          // scores of this half's 32 query rows (S^T = K Q^T on MFMA)
-          f32x16 s[2];
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            s[mt] = f32x16{};
-            const uint16_t* kp = sm.kt + (32 * mt + r32) * KSTR + 8 * g;
+          for (int mk = 0; mk < 2; ++mk) {
+            sc[mk] = f32x16{};
+            const uint16_t* kp = ktc + (32 * mk + r32) * KSTR + 8 * g;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) s[mt] = mfma32(*(const u32x4*)(kp + 16 * ks), qr[nt][ks], s[mt]);
+            for (int ks = 0; ks < 8; ++ks) sc[mk] = mfma32(qr[mq][ks], *(const u32x4*)(kp + 16 * ks), sc[mk]);
           }
-          const int t = 32 * nt + r32;
-          const int64_t iq = (int64_t)n - r + t;
-          const bool row_ok = t < r;
+        }
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+        for (int hh = 0; hh < 2; ++hh) {  // round h = 2 mq + hh: rows 16 h .. + 15, slots i = 8 hh .. + 7
+          const int h = 2 * mq + hh;
+          if (active) {
+            float cr[8];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int kx = 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
-              const int64_t j = (int64_t)T * kBlock + kx;
-              const bool ok = row_ok && (!edge || j <= iq);
-              const float pv = ok ? fast_exp2(fmaf(s[mt][i], sl2, -rm[nt])) * ril[nt] : 0.f;
-              pt[r32 * PSTR + ((kx - t) & 63)] = pv;
+            for (int q2 = 0; q2 < 2; ++q2) {
+              const float4 v4 = *(const float4*)&sm.crow[wave][16 * h + 8 * q2 + 4 * g];
+              cr[4 * q2] = v4.x;
+              cr[4 * q2 + 1] = v4.y;
+              cr[4 * q2 + 2] = v4.z;
+              cr[4 * q2 + 3] = v4.w;
             }
-        }
-        // pt is private to the wave and a wave's LDS accesses complete in order:
-        // no workgroup barrier around its staging
-        __builtin_amdgcn_wave_barrier();
-        if (active) {
-          // row t holds key c at column (c - t) mod 64: key `lane` of row t is at
-          // (lane - t) mod 64, and column s holds diagonal 63 - s for t < 64 - s
-          // and diagonal 127 - s after (c = s + t, resp. s + t - 64)
-#pragma unroll 4
-          for (int tl = 0; tl < PROWS; ++tl) {
-            const int t = 32 * nt + tl;
-            cs += pt[tl * PSTR + ((lane - t) & 63)];
-            const float x = pt[tl * PSTR + lane];
-            if (t < 64 - lane)
-              ds[0] += x;
-            else
-              ds[1] += x;
+#pragma unroll
+            for (int mk = 0; mk < 2; ++mk) {
+              const int64_t j = (int64_t)T * kBlock + 32 * mk + r32;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int t = 16 * h + 8 * (e >> 2) + 4 * g + (e & 3);
+                float pv = fast_exp2(fmaf(sc[mk][8 * hh + e], sl2, -cr[e]));
+                if (!plain) pv = (t < r && (!edge || j <= (int64_t)n - r + t)) ? pv : 0.f;
+                cs[mk] += pv;
+                pw[32 * mk + (PSTR - 1) * (8 * (e >> 2) + (e & 3))] = pv;
+              }
+            }
           }
+          // pt is private to the wave and a wave's LDS accesses complete in order:
+          // no workgroup barrier around its staging
+          __builtin_amdgcn_wave_barrier();
+          if (active) {
+            float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+            for (int tl = 0; tl < PROWS; ++tl) {
+              a0 += pr[tl * PSTR];
+              a1 += pr[tl * PSTR + 64];  // a column of the row only for lanes < 16
+            }
+            acc[h][0] = a0;
+            acc[h][1] = a1;
+          }
+          __builtin_amdgcn_wave_barrier();  // the next rows overwrite pt
         }
-        __builtin_amdgcn_wave_barrier();  // the next half overwrites pt
       }
       if (active) {
+        // the other half-wave holds the same keys' other query rows
+        cs[0] += __shfl_xor(cs[0], 32);
+        cs[1] += __shfl_xor(cs[1], 32);
         const int64_t j = (int64_t)T * kBlock + lane;
-        if (j < n) a.vcol[(size_t)slot * n + j] = cs;
-        float* dp = a.dpart + ((size_t)slot * a.ntiles + T) * 128;
-        dp[63 - lane] = ds[0];
-        dp[127 - lane] = ds[1];
+        if (j < n) a.vcol[(size_t)slot * n + j] = g ? cs[1] : cs[0];
       }
+      // diagonal e = 16 h + 79 - q: the round partials go to LDS by (h, q), then lane l
+      // adds up diagonals l and l + 64 over the rounds, in round order
+      float* pa = sm.pacc[wave];
+      if (active) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          pa[h * PCOLS + lane] = acc[h][0];
+          if (lane < 16) pa[h * PCOLS + 64 + lane] = acc[h][1];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (active) {
+        float dd[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int e = lane + 64 * u;  // diagonal (e = 127 has no entries)
+          float x = 0.f;
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            const int q = 16 * h + 79 - e;
+            if (q >= 0 && q < PCOLS) x += pa[h * PCOLS + q];
+          }
+          dd[u] = x;
+        }
+        float* dp = a.dpart + ((size_t)slot * a.ntiles + T) * 128;
+        dp[lane] = dd[0];
+        dp[64 + lane] = dd[1];
+      }
+      __builtin_amdgcn_wave_barrier();  // the next tile overwrites pa
     }
-    __syncthreads();  // every wave is done with this K tile
-    if (T + 1 < t1) {
-      store_tile();
-      __syncthreads();
-    }
+    // tile T + 1 into the other buffer (every wave finished tile T - 1 there before the
+    // last barrier), then one barrier: tile T + 1 visible, tile T released
+    if (T + 1 < t1) store_tile(sm.kt[(T + 1 - t0) & 1]);
+    __syncthreads();
   }
   if constexpr (PASS == 1) if (active) {
 #pragma unroll
@@ -261,17 +318,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
 // Merge the chunk partials of every row in chunk order: max and 1 / sum.
 __global__ __launch_bounds__(64) void vs_row_combine_kernel(const VsLaunch a) {
-  const int slot = blockIdx.x;
-  const int t = threadIdx.x;
+  // one wave per (head, row): lane c takes chunks c, c + 64, ..., then a
+  // butterfly over the lanes (a fixed order) merges them
+  const int slot = blockIdx.y;
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
   const float* pm = a.part_m + ((size_t)slot * 64 + t) * a.nchunks;
   const float* pl = a.part_l + ((size_t)slot * 64 + t) * a.nchunks;
   float m = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) m = fmaxf(m, pm[c]);
+  for (int c = lane; c < a.nchunks; c += 64) m = fmaxf(m, pm[c]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
   const float mu = m == -INFINITY ? 0.f : m;
   float l = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) l += pl[c] * fast_exp2(pm[c] - mu);
-  a.row_m[slot * 64 + t] = mu;
-  a.row_il[slot * 64 + t] = l > 0.f ? 1.f / l : 0.f;
+  for (int c = lane; c < a.nchunks; c += 64) l += pl[c] * fast_exp2(pm[c] - mu);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+  if (lane == 0) {
+    // pass 2 normalises with exp2(x - (max + log2(sum)))
+    a.row_m[slot * 64 + t] = l > 0.f ? mu + __log2f(l) : INFINITY;
+    a.row_il[slot * 64 + t] = l > 0.f ? 1.f / l : 0.f;
+  }
 }
 
 // sl[dl] = sum over the (at most two) tiles whose diagonal window holds dl, in tile order.
@@ -302,7 +369,7 @@ hipError_t launch_vs_scores(const VsLaunch& a, hipStream_t stream) {
   hipLaunchKernelGGL(vs_pass_kernel<1>, grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_row_combine_kernel, dim3(a.n_slots), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(vs_row_combine_kernel, dim3(64, a.n_slots), dim3(64), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(vs_pass_kernel<2>, grid, dim3(kThreads), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -188,6 +188,32 @@ def test_vs_index(gpu_lib, n, k_v, k_s):
             assert ev and es, (t, ev, es)
 
 
+@pytest.mark.parametrize("n,k_v", [(40000, 1000), (5000, 300)])
+def test_vs_index_exact_ties_across_chunks(gpu_lib, n, k_v):
+    """Duplicated key rows give exactly equal column sums on both sides (the same
+    arithmetic per column); with k_v cutting through that group, the lower-index
+    rule fixes the selection, which must equal the oracle's exactly even though the
+    margin rule calls it ambiguous. The duplicated keys are spread over many top-k
+    chunks and the waves inside them."""
+    print(f"[case] exact ties n={n} k_v={k_v}", flush=True)
+    g = torch.Generator().manual_seed(n)
+    q = torch.randn((1, n, 128), generator=g)
+    k = torch.randn((1, n, 128), generator=g)
+    u = torch.randn(128, generator=g)
+    u = u / u.norm()
+    q[0, -64:] += 4.0 * u
+    dup = torch.arange(3, n - 200, 7)            # about n / 7 keys, all the same row
+    k[0, dup] = 8.0 * u + 0.1 * torch.randn(128, generator=g)
+    q, k = q.to(torch.bfloat16).cuda(), k.to(torch.bfloat16).cuda()
+    assert dup.numel() > k_v
+    gvi, _ = gpu_lib.minf_build_vs_index(q, k, [0], last_q=64, k_v=k_v, k_s=64, scale=SCALE)
+    torch.cuda.synchronize()
+    wvi, _, wv, _ = O.vs_index(to_np(q[0]), to_np(k[0]), 64, k_v, 64, SCALE)
+    # the duplicated columns carry the largest, exactly equal, sums
+    assert np.all(wv[dup.numpy()] == wv[dup[0].item()])
+    assert gvi[0].cpu().tolist() == wvi.tolist() == dup[:k_v].tolist()
+
+
 def test_vs_index_c1_exact_and_planted(gpu_lib):
     # 1 head, N = 4096, last_q = 64, k_v = k_s = 64, calibrated plant (7, 14)
     q, k, v, info = _qkv(4096, 1, 1, 1000)
