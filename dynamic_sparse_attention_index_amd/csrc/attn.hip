@@ -37,6 +37,8 @@
 //    original position of every row; a tile that is not entirely earlier than
 //    the wave's earliest query is masked by comparing positions, which the
 //    separate attn_kernel<true> instantiation handles.
+#include <stdlib.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -919,6 +921,13 @@ static bool rounds_supported(int xk) {
   return c == 1;
 }
 
+// MINF_ATTN_PP=1 in the environment (read on every call) gives supported launches
+// to the ping-pong kernel.
+static bool pp_enabled() {
+  const char* e = getenv("MINF_ATTN_PP");
+  return e != nullptr && e[0] == '1';
+}
+
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
   const int npairs = (a.nb + 1) / 2;
   if (npairs <= 0 || a.nh <= 0 || a.hgroup <= 0 || a.nh % a.hgroup != 0 || kChunk % a.hgroup != 0)
@@ -932,6 +941,7 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
     if (a.heads[i].pos != nullptr) xk |= kXkPos;
     if (a.heads[i].kind == KIND_VSW) xk |= kXkWin;
   }
+  if (xk == 0 && pp_enabled() && attn_pp_supported(a)) return launch_attn_pp(a, stream);
   AttnLaunch c = a;
   c.xcd_sync = nullptr;
   c.rounds_flag = nullptr;
