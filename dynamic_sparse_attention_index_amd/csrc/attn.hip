@@ -19,7 +19,7 @@
 //    O^T = V^T P^T, so a lane owns one query row in both the score and the
 //    output accumulators and the online-softmax rescale is lane-local.
 //  * K and V tiles go from HBM straight into LDS with 16-byte direct loads
-//    (global_load_lds_dwordx4: no staging registers, no VALU), row-major with
+//    (buffer_load_dwordx4 ... lds: no staging registers, no VALU), row-major with
 //    the 16-byte chunk index of each row XOR-swizzled so that both operand
 //    reads below are free of bank conflicts.
 //  * V is read with the CDNA4 LDS transpose load (ds_read_b64_tr_b16): each
@@ -223,33 +223,60 @@ __device__ __forceinline__ uint32_t tile_chunk_byte() {
   return (uint32_t)((((threadIdx.x & 63) & 15) ^ swz(tile_row_lo())) * 16);
 }
 
-// Tile of 64 consecutive key rows starting at a valid row with 64 rows left:
-// uniform base pointers and per-lane 32-bit offsets.
-__device__ __forceinline__ void issue_contig(const char* kbase, const char* vbase, uint16_t* kt, uint16_t* vt,
+// The copies are buffer loads into LDS (buffer_load_dwordx4 ... lds) over a
+// descriptor spanning one head's K (or V): 32-bit offsets, and the compiler's
+// wait-count tracking stays exact for the LDS operand reads that run while the
+// copies are in flight (with the global form it waits for every LDS read).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;  // descriptor word 3 of a raw (unformatted) buffer
+__device__ __forceinline__ rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
+__device__ __forceinline__ void copy16(rsrc_t r, uint16_t* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voff, soff, 0, 0);
+}
+
+// Tile of 64 consecutive key rows starting at byte tile_byte of the head (a
+// valid row with 64 rows left): a uniform offset and per-lane 32-bit offsets.
+__device__ __forceinline__ void issue_contig(rsrc_t kr, rsrc_t vr, uint32_t tile_byte, uint16_t* kt, uint16_t* vt,
                                              uint32_t lane_off) {
   const int wave = wave_index();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t off = lane_off + (uint32_t)i * 16 * 256;
-    __builtin_amdgcn_global_load_lds(kbase + off, (lds_ptr)(kt + (256 * i + 64 * wave) * 8), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vbase + off, (lds_ptr)(vt + (256 * i + 64 * wave) * 8), 16, 0, 0);
+    copy16(kr, kt + (256 * i + 64 * wave) * 8, off, tile_byte);
+    copy16(vr, vt + (256 * i + 64 * wave) * 8, off, tile_byte);
   }
 }
 
 // General tile: rows_of(x) gives the key index of tile row x (always a valid
 // row; rows past the mask are masked later).
 template <class RowFn>
-__device__ __forceinline__ void issue_rows(const uint16_t* kh, const uint16_t* vh, uint16_t* kt, uint16_t* vt,
-                                           RowFn rows_of) {
+__device__ __forceinline__ void issue_rows(rsrc_t kr, rsrc_t vr, uint16_t* kt, uint16_t* vt, RowFn rows_of) {
   const int wave = threadIdx.x >> 6;
   const int rlo = tile_row_lo();
   const uint32_t cb = tile_chunk_byte();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t off = (uint32_t)rows_of(16 * i + rlo) * 256u + cb;
-    __builtin_amdgcn_global_load_lds((const char*)kh + off, (lds_ptr)(kt + (256 * i + 64 * wave) * 8), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const char*)vh + off, (lds_ptr)(vt + (256 * i + 64 * wave) * 8), 16, 0, 0);
+    copy16(kr, kt + (256 * i + 64 * wave) * 8, off, 0u);
+    copy16(vr, vt + (256 * i + 64 * wave) * 8, off, 0u);
   }
+}
+
+// One of the two (K or V) of a tile: contiguous rows, then general rows.
+__device__ __forceinline__ void issue_contig1(rsrc_t r, uint32_t tile_byte, uint16_t* t, uint32_t lane_off) {
+  const int wave = wave_index();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) copy16(r, t + (256 * i + 64 * wave) * 8, lane_off + (uint32_t)i * 16 * 256, tile_byte);
+}
+template <class RowFn>
+__device__ __forceinline__ void issue_rows1(rsrc_t r, uint16_t* t, RowFn rows_of) {
+  const int wave = threadIdx.x >> 6;
+  const int rlo = tile_row_lo();
+  const uint32_t cb = tile_chunk_byte();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) copy16(r, t + (256 * i + 64 * wave) * 8, (uint32_t)rows_of(16 * i + rlo) * 256u + cb, 0u);
 }
 
 // Per-lane LDS byte offsets of the MFMA operands inside a tile.
@@ -299,25 +326,29 @@ constexpr float kRescaleSlack = 0.0f;
 enum : int { MASK_NONE = 0, MASK_CAUSAL = 1, MASK_GENERAL = 2, MASK_GATHER = 3, MASK_POS = 4, MASK_WIN = 5 };
 constexpr int kXkPos = 1, kXkWin = 2;  // extended plan kinds of an attention instantiation
 
-template <int XK>
-__device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
-                                             const uint16_t* vt, int MASK, int key0, const uint32_t* gcols,
-                                             int qsel, int row, int n, int causal, int ashape, int sink,
-                                             int local, float sl2) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;
+// S^T = K Q^T for one tile: two independent accumulation chains (keys 0-31, 32-63), interleaved.
+__device__ __forceinline__ void qk_tile(const WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
+                                        f32x16 (&s)[2]) {
   const char* kb = (const char*)kt;
-  // S^T = K Q^T: two independent accumulation chains (keys 0-31, 32-63), interleaved
-  f32x16 s[2] = {f32x16{}, f32x16{}};
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const int ko = oo.k ^ (ks << 5);
     const u32x4 a0 = *(const u32x4*)(kb + ko);
     const u32x4 a1 = *(const u32x4*)(kb + ko + 32 * 256);
-    s[0] = mfma32(a0, ws.qr[ks], s[0]);
-    s[1] = mfma32(a1, ws.qr[ks], s[1]);
+    s0 = mfma32(a0, ws.qr[ks], s0);
+    s1 = mfma32(a1, ws.qr[ks], s1);
   }
-  // the mask touches only the score registers; MASK is uniform across the wave
+  s[0] = s0;
+  s[1] = s1;
+}
+
+// The mask touches only the score registers; MASK is uniform across the wave.
+template <int XK>
+__device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int MASK, int key0, const uint32_t* gcols, int qsel,
+                                            int row, int n, int causal, int ashape, int sink, int local) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
   if (MASK == MASK_CAUSAL) {
     const int lim = row - key0 - 4 * g;  // key slot kx = kx0 + 4g is visible iff kx0 <= lim
 #pragma unroll
@@ -382,56 +413,172 @@ __device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets
         }
       }
   }
+}
+
+// Running-max update for one tile's scores. Sets m to the new max and scales
+// l by alpha = 2^(m_old - m_new) (exactly 1 when no row of this lane rose);
+// the O accumulators are scaled separately, only when some row of the wave
+// rose (`raise`), since alpha == 1 everywhere else.
+struct TileStats {
+  float alpha, m_use;
+  bool raise;
+};
+__device__ __forceinline__ TileStats tile_stats(WaveState& ws, const f32x16 (&s)[2], float sl2) {
   float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
   const float m_tile = pair_max32(mx) * sl2;
-  if (__any(m_tile > ws.m + kRescaleSlack)) {
-    const float m_new = fmaxf(ws.m, m_tile);
-    float alpha = fast_exp2(ws.m - (m_new == -INFINITY ? 0.f : m_new));
-    // keeps the rescale a real branch: its body cannot be speculated into a select
-    asm volatile("" : "+v"(alpha));
-    ws.l *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) ws.o[mt] *= alpha;
-    ws.m = m_new;
+  TileStats t;
+  t.raise = __any(m_tile > ws.m + kRescaleSlack);
+  const float m_new = fmaxf(ws.m, m_tile);
+  t.alpha = fast_exp2(ws.m - (m_new == -INFINITY ? 0.f : m_new));
+  {
+    // a multiply of its own (not fused with the later += of the tile's sum)
+#pragma clang fp contract(off)
+    ws.l *= t.alpha;
   }
-  const float m_use = ws.m == -INFINITY ? 0.f : ws.m;
+  ws.m = m_new;
+  t.m_use = m_new == -INFINITY ? 0.f : m_new;
+  return t;
+}
+
+__device__ __forceinline__ void rescale_o(WaveState& ws, float alpha) {
+  // keeps the rescale a real branch: its body cannot be speculated into a select
+  asm volatile("" : "+v"(alpha));
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) ws.o[mt] *= alpha;
+}
+
+// bf16 probabilities of 16 scores (one 32-key half of the tile) as two MFMA
+// operands, and their sum (in the order the PV product consumes them: one
+// v_dot2_f32_bf16 per packed pair, so the weights sum to exactly one after
+// normalisation).
+__device__ __forceinline__ void probs_half(const f32x16& s, float m_use, float sl2, u32x4& pa, u32x4& pb,
+                                           float& psum) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s[8 * h + e], sl2, -m_use));
+    const u32x4 w = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+    if (h == 0)
+      pa = w;
+    else
+      pb = w;
+  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w) psum = sum_bf16x2(pa[w], psum);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) psum = sum_bf16x2(pb[w], psum);
+}
+
+// O^T += V^T P^T for 16 keys (k-step kk): four independent accumulation chains (d = 0-31, ..., 96-127).
+__device__ __forceinline__ void pv_step(WaveState& ws, const OperandOffsets& oo, const char* vb, int kk,
+                                        const u32x4& p) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)((lds_ptr)(vb + oo.v[mt][0] + 4096 * kk)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)((lds_ptr)(vb + oo.v[mt][1] + 4096 * kk)));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    ws.o[mt] = mfma32(u32x4{l2[0], l2[1], h2[0], h2[1]}, p, ws.o[mt]);
+  }
+}
+
+// Softmax of an already masked tile followed by its PV product (no overlap).
+__device__ __forceinline__ void softmax_pv(WaveState& ws, const OperandOffsets& oo, const f32x16 (&s)[2],
+                                           const uint16_t* vt, float sl2) {
+  const TileStats st = tile_stats(ws, s, sl2);
+  if (st.raise) rescale_o(ws, st.alpha);
   u32x4 pk[4];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = fast_exp2(fmaf(s[mt][8 * h + e], sl2, -m_use));
-      pk[2 * mt + h] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                             pack_bf16x2(p[6], p[7])};
-    }
-  }
-  // row sum of the bf16 probabilities the PV product uses (so the weights sum to
-  // exactly one after normalisation): one v_dot2_f32_bf16 per packed pair
   float psum = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) psum = sum_bf16x2(pk[kk][w], psum);
+  probs_half(s[0], st.m_use, sl2, pk[0], pk[1], psum);
+  probs_half(s[1], st.m_use, sl2, pk[2], pk[3], psum);
   ws.l += psum;
-  // O^T += V^T P^T: four independent accumulation chains (d = 0-31, ..., 96-127), interleaved
   const char* vb = (const char*)vt;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
+  for (int kk = 0; kk < 4; ++kk) pv_step(ws, oo, vb, kk, pk[kk]);
+}
+
+// One tile for one wave, MASK as above.
+template <int XK>
+__device__ __forceinline__ void compute_tile(WaveState& ws, const OperandOffsets& oo, const uint16_t* kt,
+                                             const uint16_t* vt, int MASK, int key0, const uint32_t* gcols,
+                                             int qsel, int row, int n, int causal, int ashape, int sink,
+                                             int local, float sl2) {
+  f32x16 s[2];
+  qk_tile(ws, oo, kt, s);
+  mask_scores<XK>(s, MASK, key0, gcols, qsel, row, n, causal, ashape, sink, local);
+  softmax_pv(ws, oo, s, vt, sl2);
+}
+
+// Software pipeline of a wave over consecutive tiles t, t + 1 (both used by
+// the wave). After tile t's row statistics (and the rare rescale of O), the
+// scores of tile t + 1 are formed on the matrix cores while the vector ALUs
+// form tile t's probabilities, then tile t's PV product runs. The order is
+// written out step by step and fenced (sched_barrier), so the compiler keeps
+// it: each 32x32x16 product is followed by the LDS read of the operand four
+// products ahead and by one pair of probabilities (two exp2, one bf16 pack,
+// one dot2 of the row sum), which execute in the product's shadow. The two
+// score chains alternate as in qk_tile, the row-sum chain and the PV
+// accumulation run in softmax_pv's order: the results are bitwise the same.
+constexpr int kReadAhead = 4;
+__device__ __forceinline__ void fused_tile_pair(WaveState& ws, const OperandOffsets& oo, const f32x16 (&sc)[2],
+                                                const uint16_t* ktn, const uint16_t* vtc, f32x16 (&sn)[2],
+                                                float sl2) {
+  const TileStats st = tile_stats(ws, sc, sl2);
+  if (st.raise) rescale_o(ws, st.alpha);
+  const char* kb = (const char*)ktn;
+  const char* vb = (const char*)vtc;
+  // operand of QK product j = 2 ks + half (keys 32 half .. +31, d 16 ks .. +15)
+  auto kread = [&](int j) -> u32x4 { return *(const u32x4*)(kb + (oo.k ^ ((j >> 1) << 5)) + (j & 1) * 32 * 256); };
+  // operand of PV product j = 4 kk + mt (keys 16 kk .. +15, d 32 mt .. +31)
+  auto vread = [&](int j) -> u32x4 {
+    const int kk = j >> 2, mt = j & 3;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)((lds_ptr)(vb + oo.v[mt][0] + 4096 * kk)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)((lds_ptr)(vb + oo.v[mt][1] + 4096 * kk)));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+    const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+  };
+  u32x4 kop[16], vop[16], pk[4];
+  f32x16 n0 = f32x16{}, n1 = f32x16{};
+  float psum = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
-          (lds_ptr)(vb + oo.v[mt][0] + 4096 * kk)));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
-          (lds_ptr)(vb + oo.v[mt][1] + 4096 * kk)));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-      const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
-      ws.o[mt] = mfma32(u32x4{l2[0], l2[1], h2[0], h2[1]}, pk[kk], ws.o[mt]);
-    }
+  for (int j = 0; j < kReadAhead; ++j) kop[j] = kread(j);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j & 1)
+      n1 = mfma32(kop[j], ws.qr[j >> 1], n1);
+    else
+      n0 = mfma32(kop[j], ws.qr[j >> 1], n0);
+    if (j + kReadAhead < 16)
+      kop[j + kReadAhead] = kread(j + kReadAhead);
+    else
+      vop[j + kReadAhead - 16] = vread(j + kReadAhead - 16);
+    // probability pair j: word j & 3 of operand pk[j >> 2], from keys 8 h + 2 w, +1 of score half mt
+    const int q = j >> 2, w = j & 3, mt = q >> 1, h = q & 1;
+    const float p0 = fast_exp2(fmaf(sc[mt][8 * h + 2 * w], sl2, -st.m_use));
+    const float p1 = fast_exp2(fmaf(sc[mt][8 * h + 2 * w + 1], sl2, -st.m_use));
+    pk[q][w] = pack_bf16x2(p0, p1);
+    psum = sum_bf16x2(pk[q][w], psum);
+    __builtin_amdgcn_sched_barrier(0);
   }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    ws.o[j & 3] = mfma32(vop[j], pk[j >> 2], ws.o[j & 3]);
+    if (j + kReadAhead < 16) vop[j + kReadAhead] = vread(j + kReadAhead);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  ws.l += psum;
+  sn[0] = n0;
+  sn[1] = n1;
 }
 
 // XK: the extended plan kinds the launch holds (kXkPos: Block-Sparse heads on
@@ -473,6 +620,8 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
 
   const uint16_t* kh = p.k + (size_t)kvh * n * kHeadDim;
   const uint16_t* vh = p.v + (size_t)kvh * n * kHeadDim;
+  const rsrc_t kr = buffer_of(kh, (uint32_t)n * (kHeadDim * 2));
+  const rsrc_t vr = buffer_of(vh, (uint32_t)n * (kHeadDim * 2));
 
   WaveState ws;
   {
@@ -576,6 +725,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
   }
   // permuted sequences: each lane's query position and the wave's earliest one
   const bool posm = (XK & kXkPos) && hd.kind == KIND_BLOCK && hd.pos != nullptr;
+  const rsrc_t posr = buffer_of(posm ? (const void*)hd.pos : (const void*)kh, posm ? (uint32_t)n * 4u : 0u);
   int rpos = row, wminpos = 0;
   if (posm) {
     rpos = row < n ? hd.pos[row] : -1;
@@ -595,14 +745,14 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     const int causal_eff = p.causal || hd.kind != KIND_DENSE;
     auto issue_block = [&](int cblk, uint16_t* ktn, uint16_t* vtn, uint32_t* psn) {
       if ((cblk + 1) * kBlock <= n) {
-        const size_t base = (size_t)cblk * kBlock * (kHeadDim * 2);
-        issue_contig((const char*)kh + base, (const char*)vh + base, ktn, vtn, lane_off);
+        issue_contig(kr, vr, (uint32_t)cblk * kBlock * (kHeadDim * 2), ktn, vtn, lane_off);
         // permuted sequences: the tile's 64 key positions go to LDS with it
         if (posm && wave == 0)
-          __builtin_amdgcn_global_load_lds(hd.pos + (size_t)cblk * kBlock + lane, (lds_ptr)psn, 4, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(posr, (lds_ptr)psn, 4, (uint32_t)lane * 4u,
+                                                   (uint32_t)cblk * kBlock * 4u, 0, 0);
       } else {
         // partial last block: rows past n repeat row n - 1 and are always masked
-        issue_rows(kh, vh, ktn, vtn, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
+        issue_rows(kr, vr, ktn, vtn, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
         if (posm && wave == 0) {
           const int j = cblk * kBlock + lane;
           psn[lane] = j < n ? (uint32_t)hd.pos[j] : 0x3fffffffu;
@@ -623,10 +773,9 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       if ((XK & kXkWin) && vsw) {
         // 64 keys from key c; rows outside [0, n) load a valid row and are masked
         if (c >= 0 && c + kBlock <= n) {
-          const size_t base = (size_t)c * (kHeadDim * 2);
-          issue_contig((const char*)kh + base, (const char*)vh + base, ktn, vtn, lane_off);
+          issue_contig(kr, vr, (uint32_t)c * (kHeadDim * 2), ktn, vtn, lane_off);
         } else {
-          issue_rows(kh, vh, ktn, vtn, [&](int x) {
+          issue_rows(kr, vr, ktn, vtn, [&](int x) {
             const int j = c + x;
             return j < 0 ? 0 : (j < n ? j : n - 1);
           });
@@ -677,6 +826,86 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       bm_cur = bm_nxt;
       return hn;
     };
+    if constexpr (XK == 0) {
+      // Software-pipelined walk (dense, A-shape, VS and Block-Sparse heads on
+      // unpermuted sequences). Tile t's K sits in K buffer t % 2 and its V in V
+      // buffer t % 2. Step t forms the scores of tile t + 1 (K buffer (t + 1) % 2)
+      // while the softmax of tile t runs, then tile t's PV product (V buffer
+      // t % 2); meanwhile K of tile t + 2 streams into K buffer t % 2 (tile t's
+      // K was last read in step t - 1) and V of tile t + 1 into V buffer
+      // (t + 1) % 2 (last read in step t - 1). Both land before the step's
+      // closing barrier.
+      auto issue_k = [&](int cblk, uint16_t* dst) {
+        if ((cblk + 1) * kBlock <= n)
+          issue_contig1(kr, (uint32_t)cblk * kBlock * (kHeadDim * 2), dst, lane_off);
+        else
+          issue_rows1(kr, dst, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
+      };
+      auto issue_v = [&](int cblk, uint16_t* dst) {
+        if ((cblk + 1) * kBlock <= n)
+          issue_contig1(vr, (uint32_t)cblk * kBlock * (kHeadDim * 2), dst, lane_off);
+        else
+          issue_rows1(vr, dst, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
+      };
+      auto tile_mask_of = [&](int cblk) -> int {
+        bool full;
+        if (causal_eff) {
+          full = cblk < qb;
+          if (ashape && full)
+            full = ((int64_t)cblk * kBlock + kBlock - 1 < hd.sink) ||
+                   ((int64_t)qb * kBlock + kBlock - 1 - (int64_t)cblk * kBlock < hd.local);
+        } else {
+          full = (cblk + 1) * kBlock <= n;
+        }
+        return full ? MASK_NONE : ((causal_eff && !ashape) ? MASK_CAUSAL : MASK_GENERAL);
+      };
+      int c2 = 0, m2 = 0;
+      bool h0 = it.next(c_cur, m_cur), h1 = false;
+      if (h0) {
+        issue_k(c_cur, kt0);
+        issue_v(c_cur, vt0);
+        h1 = it.next(c_nxt, m_nxt);
+        if (h1) issue_k(c_nxt, kt1);
+      }
+      wait_vmem();
+      __syncthreads();
+      f32x16 sa[2], sb[2];
+      if (h0 && wave_on && ((m_cur >> qsel) & 1)) qk_tile(ws, oo, kt0, sa);
+      __syncthreads();  // every wave has read K buffer 0 before tile 2 overwrites it
+      auto pstep = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], uint16_t* kc, uint16_t* kn, uint16_t* vc,
+                       uint16_t* vn) -> bool {
+        const bool h2 = h1 && it.next(c2, m2);
+        if (h2) issue_k(c2, kc);
+        if (h1) issue_v(c_nxt, vn);
+        const bool u0 = wave_on && ((m_cur >> qsel) & 1);
+        const bool u1 = h1 && wave_on && ((m_nxt >> qsel) & 1);
+        if (u0) {
+          const int mask = tile_mask_of(c_cur);
+          if (mask != MASK_NONE)
+            mask_scores<XK>(sc, mask, c_cur * kBlock, nullptr, qsel, row, n, causal_eff, ashape, hd.sink, hd.local);
+          if (u1)
+            fused_tile_pair(ws, oo, sc, kn, vc, sn, sl2);
+          else
+            softmax_pv(ws, oo, sc, vc, sl2);
+        } else if (u1) {
+          qk_tile(ws, oo, kn, sn);
+        }
+        wait_vmem();
+        __syncthreads();
+        // tile t + 1 becomes the current one
+        h0 = h1;
+        c_cur = c_nxt;
+        m_cur = m_nxt;
+        h1 = h2;
+        c_nxt = c2;
+        m_nxt = m2;
+        return h0;
+      };
+      while (h0) {
+        if (!pstep(sa, sb, kt0, kt1, vt0, vt1)) break;
+        if (!pstep(sb, sa, kt1, kt0, vt1, vt0)) break;
+      }
+    } else {
     // key-position slots of the two tile buffers (phase B, which uses clist, never runs on BLOCK heads)
     uint32_t* ps0 = sm.clist;
     uint32_t* ps1 = sm.clist + kBlock;
@@ -688,6 +917,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     while (have) {
       if (!step(kt0, vt0, ps0, kt1, vt1, ps1)) break;
       have = step(kt1, vt1, ps1, kt0, vt0, ps0);
+    }
     }
   }
 
@@ -740,7 +970,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
           };
         };
         auto gstep = [&](int t, uint16_t* ktc, uint16_t* vtc, uint16_t* ktn, uint16_t* vtn) {
-          if (t + 1 < ntile) issue_rows(kh, vh, ktn, vtn, rows_of(t + 1));
+          if (t + 1 < ntile) issue_rows(kr, vr, ktn, vtn, rows_of(t + 1));
           if (wave_on) {
             // skip the tile when none of its columns belongs to this wave's query block
             // (padding slots were cleared, so they never count)
@@ -751,7 +981,7 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
           wait_vmem();
           __syncthreads();
         };
-        issue_rows(kh, vh, kt0, vt0, rows_of(0));
+        issue_rows(kr, vr, kt0, vt0, rows_of(0));
         wait_vmem();
         __syncthreads();
         for (int t = 0; t < ntile; t += 2) {
