@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libminf.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["attn.hip", "attn_pp.hip", "vs_index.hip", "vs_window.hip", "bs_index.hip", "topk.hip", "decode.hip", "search.hip", "api.cpp"]
+SOURCES = ["attn.hip", "vs_index.hip", "vs_window.hip", "bs_index.hip", "topk.hip", "decode.hip", "search.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -27,6 +27,22 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Direct HBM -> LDS copies go through buffer loads (buffer_load_dwordx4 ...
+// lds) over a descriptor spanning one head's K (or V): 32-bit offsets, and
+// the compiler's wait-count tracking stays exact for LDS operand reads issued
+// while copies are in flight (with the global form it waits for every one).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;  // descriptor word 3 of a raw (unformatted) buffer
+__device__ __forceinline__ rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferFlags);
+}
+// 16 bytes per lane at byte voff + soff of the buffer into LDS at dst + 16 * lane
+__device__ __forceinline__ void copy16(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, voff, soff, 0, 0);
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 

@@ -41,9 +41,6 @@ struct AttnLaunch {
 };
 
 hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream);
-// Ping-pong kernel (quads of query blocks, 8 waves): launches whose heads it supports
-bool attn_pp_supported(const AttnLaunch& a);
-hipError_t launch_attn_pp(const AttnLaunch& a, hipStream_t stream);
 hipError_t launch_vs_offset_bits(const int32_t* const* s_idx, const int32_t* k_s, uint32_t* const* bits,
                                  int count, int n, hipStream_t stream);
 // flag = 1 when the VS heads' offset bitmaps and the VS window heads' tile counts (up to 32 each)

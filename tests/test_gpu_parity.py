@@ -308,8 +308,6 @@ def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch, n):
         si = torch.randperm(n, generator=g)[:3000 + 500 * h].sort().values.to(torch.int32)
         vi = torch.randperm(n, generator=g)[:400].sort().values.to(torch.int32)
         plans.append(dict(kind="vs", v_idx=vi.cuda(), s_idx=si.cuda()))
-    # the rounds launch runs the pair kernel: compare it with that kernel's ordinary launch
-    monkeypatch.setenv("MINF_ATTN_PP", "0")
     monkeypatch.delenv("MINF_ATTN_ROUNDS", raising=False)
     o1, l1 = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
     monkeypatch.setenv("MINF_ATTN_ROUNDS", "0")
@@ -417,38 +415,3 @@ def test_vs_window_large_sampled_rows(gpu_lib):
         print(f"  head {h} ({plans[h]['kind']}): max-abs err {err:.3e}", flush=True)
         assert err <= OUT_TOL
         check_lse(lse[h][t].cpu().numpy(), wl[0])
-
-
-@pytest.mark.parametrize("n,hq,hkv", [(4096 + 100, 4, 2), (9000, 8, 8)])
-def test_pingpong_kernel_matches_pair_kernel(gpu_lib, monkeypatch, n, hq, hkv):
-    """The quad (ping-pong) kernel and the pair kernel visit each query block's key
-    tiles in the same order with the same per-tile arithmetic, so block tiles give
-    bitwise-equal results; gathered columns are grouped into tiles per quad instead of
-    per pair, so VS heads with verticals agree within rounding (and both with the oracle)."""
-    q, k, v, info = _qkv(n, hq, hkv, 27)
-    nb = (n + 63) // 64
-    bi, bc = gpu_lib.minf_build_block_index(q, k, list(range(hq)), k_b=7)
-    vi, si = gpu_lib.minf_build_vs_index(q, k, list(range(hq)), last_q=64, k_v=100, k_s=120, scale=SCALE)
-    e = torch.empty(0, dtype=torch.int32, device="cuda")
-    kinds = [dict(kind="dense"), dict(kind="ashape", sink=100, local=700),
-             dict(kind="vs", v_idx=e, s_idx=si[2].contiguous()),
-             dict(kind="block", blk_idx=bi[3].contiguous(), blk_cnt=bc[3].contiguous())]
-    plans = [kinds[h % 4] for h in range(hq)]
-    res = {}
-    for pp in ("0", "1"):
-        monkeypatch.setenv("MINF_ATTN_PP", pp)
-        res[pp] = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
-        res[pp + "d"] = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE)
-        res[pp + "n"] = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE, causal=False)
-    torch.cuda.synchronize()
-    for key in ("", "d", "n"):
-        assert torch.equal(res["0" + key][0], res["1" + key][0]), key
-        assert torch.equal(res["0" + key][1], res["1" + key][1]), key
-    # VS heads with verticals: both kernels against the oracle, and against each other
-    plans_v = [dict(kind="vs", v_idx=vi[h].contiguous(), s_idx=si[h].contiguous()) for h in range(hq)]
-    outs = []
-    for pp in ("0", "1"):
-        monkeypatch.setenv("MINF_ATTN_PP", pp)
-        outs.append(_attn_parity(gpu_lib, q, k, v, plans_v))
-    assert max_abs(to_np(outs[0][0]), to_np(outs[1][0])) <= 2e-2
-    assert nb > 4
