@@ -598,45 +598,56 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       bm_cur = bm_nxt;
       return hn;
     };
-    if constexpr (XK == 0) {
-      // Software-pipelined walk (dense, A-shape, VS and Block-Sparse heads on
-      // unpermuted sequences). Tile t's K sits in K buffer t % 2 and its V in V
-      // buffer t % 2. Step t forms the scores of tile t + 1 (K buffer (t + 1) % 2)
-      // while the softmax of tile t runs, then tile t's PV product (V buffer
-      // t % 2); meanwhile K of tile t + 2 streams into K buffer t % 2 (tile t's
-      // K was last read in step t - 1) and V of tile t + 1 into V buffer
-      // (t + 1) % 2 (last read in step t - 1). Both land before the step's
-      // closing barrier.
-      auto issue_k = [&](int cblk, uint16_t* dst) {
-        if ((cblk + 1) * kBlock <= n)
-          issue_contig1(kr, (uint32_t)cblk * kBlock * (kHeadDim * 2), dst, lane_off);
+    if constexpr (XK == 0 || XK == kXkWin) {
+      // Software-pipelined walk (dense, A-shape, VS, VS window and Block-Sparse
+      // heads on unpermuted sequences). Tile t's K sits in K buffer t % 2 and
+      // its V in V buffer t % 2. Step t forms the scores of tile t + 1 (K buffer
+      // (t + 1) % 2) while the softmax of tile t runs, then tile t's PV product
+      // (V buffer t % 2); meanwhile K of tile t + 2 streams into K buffer t % 2
+      // (tile t's K was last read in step t - 1) and V of tile t + 1 into V
+      // buffer (t + 1) % 2 (last read in step t - 1). Both land before the
+      // step's closing barrier. A tile is key block c (keys 64 c ..), or for a
+      // VS window head the 64 keys from key c.
+      auto kstart = [&](int c) -> int { return ((XK & kXkWin) && vsw) ? c : c * kBlock; };
+      auto issue_k = [&](int c, uint16_t* dst) {
+        const int j0 = kstart(c);
+        if (j0 >= 0 && j0 + kBlock <= n)
+          issue_contig1(kr, (uint32_t)j0 * (kHeadDim * 2), dst, lane_off);
         else
-          issue_rows1(kr, dst, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
+          issue_rows1(kr, dst, [&](int x) { const int j = j0 + x; return j < 0 ? 0 : (j < n ? j : n - 1); });
       };
-      auto issue_v = [&](int cblk, uint16_t* dst) {
-        if ((cblk + 1) * kBlock <= n)
-          issue_contig1(vr, (uint32_t)cblk * kBlock * (kHeadDim * 2), dst, lane_off);
+      auto issue_v = [&](int c, uint16_t* dst) {
+        const int j0 = kstart(c);
+        if (j0 >= 0 && j0 + kBlock <= n)
+          issue_contig1(vr, (uint32_t)j0 * (kHeadDim * 2), dst, lane_off);
         else
-          issue_rows1(vr, dst, [&](int x) { int j = cblk * kBlock + x; return j < n ? j : n - 1; });
+          issue_rows1(vr, dst, [&](int x) { const int j = j0 + x; return j < 0 ? 0 : (j < n ? j : n - 1); });
       };
-      auto tile_mask_of = [&](int cblk) -> int {
+      const int rmin = qb * kBlock + (wave & 1) * 32;  // the wave's first row
+      // mask of tile c for this wave's block; wend: the A-shape window, or the end of a VS window interval
+      auto tile_mask_of = [&](int c, int e0, int e1, int& wend) -> int {
+        wend = hd.local;
+        if ((XK & kXkWin) && vsw) {
+          wend = qsel ? e1 : e0;
+          return (c >= 0 && c + kBlock <= wend && c + kBlock - 1 <= rmin) ? MASK_NONE : MASK_WIN;
+        }
         bool full;
         if (causal_eff) {
-          full = cblk < qb;
+          full = c < qb;
           if (ashape && full)
-            full = ((int64_t)cblk * kBlock + kBlock - 1 < hd.sink) ||
-                   ((int64_t)qb * kBlock + kBlock - 1 - (int64_t)cblk * kBlock < hd.local);
+            full = ((int64_t)c * kBlock + kBlock - 1 < hd.sink) ||
+                   ((int64_t)qb * kBlock + kBlock - 1 - (int64_t)c * kBlock < hd.local);
         } else {
-          full = (cblk + 1) * kBlock <= n;
+          full = (c + 1) * kBlock <= n;
         }
         return full ? MASK_NONE : ((causal_eff && !ashape) ? MASK_CAUSAL : MASK_GENERAL);
       };
-      int c2 = 0, m2 = 0;
-      bool h0 = it.next(c_cur, m_cur), h1 = false;
+      int c2 = 0, m2 = 0, e02 = 0, e12 = 0;
+      bool h0 = next_tile(c_cur, m_cur, e0_cur, e1_cur), h1 = false;
       if (h0) {
         issue_k(c_cur, kt0);
         issue_v(c_cur, vt0);
-        h1 = it.next(c_nxt, m_nxt);
+        h1 = next_tile(c_nxt, m_nxt, e0_nxt, e1_nxt);
         if (h1) issue_k(c_nxt, kt1);
       }
       wait_vmem();
@@ -646,15 +657,16 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       __syncthreads();  // every wave has read K buffer 0 before tile 2 overwrites it
       auto pstep = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], uint16_t* kc, uint16_t* kn, uint16_t* vc,
                        uint16_t* vn) -> bool {
-        const bool h2 = h1 && it.next(c2, m2);
+        const bool h2 = h1 && next_tile(c2, m2, e02, e12);
         if (h2) issue_k(c2, kc);
         if (h1) issue_v(c_nxt, vn);
         const bool u0 = wave_on && ((m_cur >> qsel) & 1);
         const bool u1 = h1 && wave_on && ((m_nxt >> qsel) & 1);
         if (u0) {
-          const int mask = tile_mask_of(c_cur);
+          int wend;
+          const int mask = tile_mask_of(c_cur, e0_cur, e1_cur, wend);
           if (mask != MASK_NONE)
-            mask_scores<XK>(sc, mask, c_cur * kBlock, nullptr, qsel, row, n, causal_eff, ashape, hd.sink, hd.local);
+            mask_scores<XK>(sc, mask, kstart(c_cur), nullptr, qsel, row, n, causal_eff, ashape, hd.sink, wend);
           if (u1)
             fused_tile_pair(ws, oo, sc, kn, vc, sn, sl2);
           else
@@ -668,9 +680,13 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
         h0 = h1;
         c_cur = c_nxt;
         m_cur = m_nxt;
+        e0_cur = e0_nxt;
+        e1_cur = e1_nxt;
         h1 = h2;
         c_nxt = c2;
         m_nxt = m2;
+        e0_nxt = e02;
+        e1_nxt = e12;
         return h0;
       };
       while (h0) {
