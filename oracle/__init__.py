@@ -18,6 +18,7 @@ from .minf_oracle import (  # noqa: F401
     vs_mask_block,
     vs_window_set,
     vsw_mask_block,
+    vertical_tiles,
     pool_blocks,
     block_scores,
     block_index,

@@ -276,6 +276,23 @@ def vsw_mask_block(n: int, s_idx, v_idx, b: int, rows) -> np.ndarray:
     return (j[None, :] <= rows[:, None]) & sel[None, :]
 
 
+def vertical_tiles(n: int, s_idx, v_idx, b: int, windows: bool) -> list:
+    """The skip-column read of query block b's vertical lines ([T] MMInference
+    part: reading with skipped columns turns the lines into dense pieces): the
+    selected columns up to the block's last row that the block's slash tiles
+    do not already hold (its windows when `windows`, else the blocks of Bs(b)),
+    in ascending order, cut into tiles of 64 columns ([A] Fig. 4: verticals in
+    1x64 pieces). Against the block's rows each tile is dense except where a
+    column lies past a row (j > i), a staircase inside the diagonal block."""
+    last = min(BLOCK * b + BLOCK - 1, n - 1)
+    if windows:
+        held = set(vs_window_set(n, s_idx, b).tolist())
+        cols = sorted({int(j) for j in np.asarray(v_idx).tolist() if 0 <= j <= last and int(j) not in held})
+    else:
+        cols = vs_column_set(n, s_idx, v_idx, b).tolist()
+    return [np.array(cols[i:i + BLOCK], dtype=np.int64) for i in range(0, len(cols), BLOCK)]
+
+
 # ---------------------------------------------------------------------------
 # Block-Sparse online estimate ([A] "Method": mean pooling of Q and K, and the
 # commutativity of mean pooling with the matrix product, give the block index)

@@ -616,3 +616,49 @@ def test_vs_window_brute_force_and_full_budget():
     for b in range(3):
         rows = np.arange(64 * b, min(64 * b + 64, n))
         assert np.array_equal(O.vsw_mask_block(n, full, [], b, rows), np.arange(n)[None, :] <= rows[:, None])
+
+
+def test_vertical_tiles_complete_the_slash_tiles():
+    # the skip-column read: selected columns not held by the block's slash tiles, ascending,
+    # 64 per tile; with the slash tiles they give exactly the key set of the block's mask
+    rng = np.random.default_rng(43)
+    n = 64 * 9 + 21
+    s_idx = np.sort(rng.choice(n, 6, replace=False))
+    v_idx = np.sort(rng.choice(n, 150, replace=False))
+    for windows in (False, True):
+        for b in range((n + 63) // 64):
+            last = min(64 * b + 63, n - 1)
+            tiles = O.vertical_tiles(n, s_idx, v_idx, b, windows)
+            cols = [int(c) for t in tiles for c in t]
+            assert all(1 <= len(t) <= 64 for t in tiles) and all(len(t) == 64 for t in tiles[:-1])
+            assert cols == sorted(set(cols))
+            if windows:
+                held = set(O.vs_window_set(n, s_idx, b).tolist())
+                mask = O.vsw_mask_block(n, s_idx, v_idx, b, [last])[0]
+            else:
+                held = {j for c in O.vs_block_set(n, s_idx, b).tolist() for j in range(64 * c, min(64 * c + 64, n))}
+                mask = O.vs_mask_block(n, s_idx, v_idx, b, [last])[0]
+            # brute force from the definitions: columns of V up to the last row, not held
+            want = sorted({int(j) for j in v_idx if j <= last and int(j) not in held})
+            assert cols == want
+            # slash tiles and vertical tiles together: the mask's keys at the block's last row
+            keys = {j for j in held if j <= last} | set(cols)
+            assert keys == set(np.nonzero(mask)[0].tolist())
+
+
+def test_vertical_tiles_are_dense_triangles():
+    # against the block's rows, the visible columns of every row are a prefix of the tile:
+    # columns before the block are seen by every row, the block's own columns form a staircase
+    n = 64 * 4
+    s_idx = np.array([0, 130])
+    v_idx = np.array(list(range(0, 256, 3)))
+    for b in range(4):
+        rows = np.arange(64 * b, 64 * b + 64)
+        for t in O.vertical_tiles(n, s_idx, v_idx, b, True):
+            vis = t[None, :] <= rows[:, None]
+            counts = vis.sum(axis=1)
+            for r in range(64):
+                assert vis[r, :counts[r]].all() and not vis[r, counts[r]:].any()
+            assert np.all(np.diff(counts) >= 0)
+            assert vis[:, t < 64 * b].all()
+
