@@ -31,7 +31,8 @@ namespace minf {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int KSTR = 136;
+constexpr int kTileHalves = kBlock * kHeadDim;  // one 64 x 128 bf16 K tile, rows of 256 bytes
+constexpr int kRing = 3;                        // K tiles in LDS: T (read), T + 1 (landed), T + 2 (in flight)
 // Staged probability rows, 16 query rows at a time (rows t = 16 h + tl of round
 // h): row tl holds key c at column q = c - tl + 16, in [1, 79]. A row writes the
 // same 64 columns in every round, so the ones it never writes stay zero, and
@@ -44,14 +45,19 @@ constexpr int PROWS = 16;
 constexpr int PCOLS = 80;
 // s_waitcnt immediate on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVmem0 = 0x0F70;
+constexpr int kWaitVmem4 = 0x0F74;  // vmcnt(4): the newest tile's four copies may be in flight
 
-// K tiles are double-buffered: tile T + 1 is stored into the other buffer
-// while other waves may still read tile T, so one barrier per tile suffices.
+__device__ __forceinline__ int swz(int x) { return ((x & 3) << 2) | ((x >> 2) & 3); }
+
+// K tiles go HBM -> LDS with buffer loads into a ring of three buffers: tile
+// T + 2 streams into the buffer tile T - 1 used while tile T is worked on, so
+// one barrier per tile suffices. Rows of 256 bytes, the 16-byte chunk c of row
+// x at chunk position c ^ swz(x) (conflict-free operand reads of 16 rows).
 struct VsSmem1 {
-  uint16_t kt[2][kBlock * KSTR];
+  uint16_t kt[kRing][kTileHalves];
 };
 struct VsSmem2 {
-  uint16_t kt[2][kBlock * KSTR];
+  uint16_t kt[kRing][kTileHalves];
   float pt[4][PROWS * PSTR + 64];  // + 64: lanes 16..63 read past the 80 columns of the last row
   float pacc[4][4 * PCOLS];          // per wave: column partials of the four rounds of a tile
   float crow[4][64];                 // per wave: max + log2(sum) of each last-query row
@@ -95,36 +101,40 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
     for (int x = lane; x < PROWS * PSTR + 64; x += 64) sm.pt[wave][x] = 0.f;
   }
 
-  // K tiles: 16 threads per 256-byte row, rows kr + 16 i; the next tile is
-  // loaded into registers while the current one is worked on
-  const int dc = tid & 15;
-  const int kr = tid >> 4;
-  u32x4 kn[4];
-  auto load_tile = [&](int T) {
+  // K tiles: wave w's copy i fills LDS chunks [256 i + 64 w, +64) = rows
+  // 16 i + 4 w .. +3, 16 lanes per 256-byte row, from the swizzled source chunk;
+  // rows past n read row n - 1 (they are masked)
+  const rsrc_t kbuf = buffer_of(kh, (uint32_t)n * (kHeadDim * 2));
+  const int crow_lo = 4 * (tid >> 6) + ((tid & 63) >> 4);
+  const uint32_t cbyte = (uint32_t)(((tid & 15) ^ swz(crow_lo)) * 16);
+  auto issue_tile = [&](int T, uint16_t* kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t j = (int64_t)T * kBlock + kr + 16 * i;
-      kn[i] = j < n ? *(const u32x4*)(kh + (size_t)j * kHeadDim + 8 * dc) : u32x4{0, 0, 0, 0};
+      int j = T * kBlock + 16 * i + crow_lo;
+      j = j < n ? j : n - 1;
+      copy16(kbuf, kt + (256 * i + 64 * wave) * 8, (uint32_t)j * 256u + cbyte, 0u);
     }
   };
-  auto store_tile = [&](uint16_t* kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(kt + (kr + 16 * i) * KSTR + 8 * dc) = kn[i];
-  };
+  // operand reads: row x = 32 m + r32, chunk 2 ks + g, at kofs + 32 m rows, XOR (ks << 5)
+  const int kofs = r32 * 256 + ((g ^ swz(r32)) << 4);
 
   const int t0 = ch * a.tiles_per_chunk;
   const int t1 = t0 + a.tiles_per_chunk < a.ntiles ? t0 + a.tiles_per_chunk : a.ntiles;
-  if (t0 < t1) {
-    load_tile(t0);
-    store_tile(sm.kt[0]);
-  }
-  // the query operands (and the row statistics) have arrived on every path
-  // into the loop, so that the loop's wait counts only cover the next K tile
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  if (t0 < t1) issue_tile(t0, sm.kt[0]);
+  if (t0 + 1 < t1) issue_tile(t0 + 1, sm.kt[1]);
+  // tile t0 (and the query operands and row statistics) have arrived on every
+  // path into the loop, so that the loop's wait counts only cover K tiles
+  if (t0 + 1 < t1)
+    __builtin_amdgcn_s_waitcnt(kWaitVmem4);
+  else
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
   __syncthreads();
+  int cur = 0;  // ring slot of tile T
   for (int T = t0; T < t1; ++T) {
-    if (T + 1 < t1) load_tile(T + 1);
-    const uint16_t* ktc = sm.kt[(T - t0) & 1];
+    // tile T + 2 into the slot tile T - 1 used (every wave left it at the last barrier)
+    const int nxt2 = cur == 0 ? 2 : cur - 1;
+    if (T + 2 < t1) issue_tile(T + 2, sm.kt[nxt2]);
+    const char* ktc = (const char*)sm.kt[cur];
     // the causal mask only bites in tiles that reach past the first last-query row
     const bool edge = (int64_t)T * kBlock + kBlock - 1 > (int64_t)n - r;
     if constexpr (PASS == 1) if (active) {
@@ -133,10 +143,10 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
       for (int mt = 0; mt < 2; ++mt) {
         s[mt][0] = f32x16{};
         s[mt][1] = f32x16{};
-        const uint16_t* kp = ktc + (32 * mt + r32) * KSTR + 8 * g;
+        const char* kp = ktc + 32 * mt * 256;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const u32x4 av = *(const u32x4*)(kp + 16 * ks);
+          const u32x4 av = *(const u32x4*)(kp + (kofs ^ (ks << 5)));
           s[mt][0] = mfma32(av, qr[0][ks], s[mt][0]);
           s[mt][1] = mfma32(av, qr[1][ks], s[mt][1]);
         }
@@ -145,16 +155,16 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int t = 32 * nt + r32;
-          const int64_t iq = (int64_t)n - r + t;
-          const bool row_ok = t < r;
+          // key slot kx = 32 mt + 8 (i >> 2) + (i & 3) of this lane (key T 64 + kx + 4 g) is visible
+          // iff kx <= lim: every slot below the causal edge, none for a row past r
+          const int lim = t >= r ? -1 : (edge ? (n - r + t) - T * kBlock - 4 * g : kBlock);
           float mx = -INFINITY;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int64_t j = (int64_t)T * kBlock + 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
-              const bool ok = row_ok && (!edge || j <= iq);
-              const float x = ok ? s[mt][nt][i] * sl2 : -INFINITY;
+              const int kx = 32 * mt + 8 * (i >> 2) + (i & 3);
+              const float x = kx <= lim ? s[mt][nt][i] * sl2 : -INFINITY;
               s[mt][nt][i] = x;
               mx = fmaxf(mx, x);
             }
@@ -195,9 +205,10 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
 #pragma unroll
           for (int mk = 0; mk < 2; ++mk) {
             sc[mk] = f32x16{};
-            const uint16_t* kp = ktc + (32 * mk + r32) * KSTR + 8 * g;
+            const char* kp = ktc + 32 * mk * 256;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) sc[mk] = mfma32(qr[mq][ks], *(const u32x4*)(kp + 16 * ks), sc[mk]);
+            for (int ks = 0; ks < 8; ++ks)
+              sc[mk] = mfma32(qr[mq][ks], *(const u32x4*)(kp + (kofs ^ (ks << 5))), sc[mk]);
           }
         }
 #pragma unroll
@@ -279,10 +290,14 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
       }
       __builtin_amdgcn_wave_barrier();  // the next tile overwrites pa
     }
-    // tile T + 1 into the other buffer (every wave finished tile T - 1 there before the
-    // last barrier), then one barrier: tile T + 1 visible, tile T released
-    if (T + 1 < t1) store_tile(sm.kt[(T + 1 - t0) & 1]);
+    // tile T + 1 landed (only tile T + 2's copies may still be in flight), then one
+    // barrier: tile T + 1 visible to every wave, tile T released
+    if (T + 2 < t1)
+      __builtin_amdgcn_s_waitcnt(kWaitVmem4);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __syncthreads();
+    cur = cur == 2 ? 0 : cur + 1;
   }
   if constexpr (PASS == 1) if (active) {
 #pragma unroll

@@ -70,9 +70,9 @@ def test_decode_pool_keys_and_incremental_update(gpu_lib, n):
     assert torch.equal(part, full)
 
 
-# past 2048 blocks with k_b <= 256 the top-k runs in 2048-block segments merged by the last
-# finisher: two segments with an 11-block tail, four segments at the largest such k_b, and
-# one past it (a single workgroup per head)
+# past 2048 blocks with k_b <= 256 the top-k runs in 2048-block segments whose winners a
+# separate merge kernel selects from: two segments with an 11-block tail, four segments at the
+# largest such k_b, and one past it (a single workgroup per head)
 @pytest.mark.parametrize("n,hq,hkv,k_b", [(700, 8, 2, 3), (4096, 8, 2, 8), (33000, 8, 2, 40), (20000, 8, 1, 1),
                                           (2048 * 64 + 700, 8, 2, 40), (3 * 2048 * 64 + 320, 4, 2, 256),
                                           (2048 * 64 + 900, 4, 2, 257)])
