@@ -218,7 +218,7 @@ def profiled_traffic(workload):
             key, val = line.split("=", 1)
             kv[key.strip()] = val.strip()
     csrc = os.path.join(ROOT, "dynamic_sparse_attention_index_amd", "csrc")
-    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("attn.hip", "common.h")))
+    sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("attn.hip", "tile.h", "common.h")))
     if kv.get("source_sha256") != sha.hexdigest():
         return None
     return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
