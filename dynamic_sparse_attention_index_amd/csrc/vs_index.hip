@@ -16,9 +16,10 @@
 //  * pass 2 recomputes the scores as S = Q_last K^T (so a lane holds one key
 //    column and 16 query rows of each 32x32 product), normalises them, sums
 //    the columns in registers (complete column sums), and reduces the 64x64
-//    probability tile along its 127 diagonals through LDS (per-tile partials;
-//    a diagonal spans at most two tiles and the two partials are added in
-//    tile order by a separate kernel);
+//    probability tile along its 127 diagonals: four rows at a time by DPP
+//    lane shifts in registers, then through LDS (per-tile partials; a
+//    diagonal spans at most two tiles and the two partials are added in tile
+//    order by a separate kernel);
 //  * top-k (topk.hip) is a radix select on the sortable bit pattern spread
 //    over many workgroups per row, ties to the lower index, emitted in
 //    ascending index order.
@@ -30,24 +31,47 @@
 namespace minf {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;   // pass 1: one wave per query head of the group
+constexpr int kThreads2 = 512;  // pass 2: two waves per query head (32 query rows each)
 constexpr int kTileHalves = kBlock * kHeadDim;  // one 64 x 128 bf16 K tile, rows of 256 bytes
 constexpr int kRing = 3;                        // K tiles in LDS: T (read), T + 1 (landed), T + 2 (in flight)
-// Staged probability rows, 16 query rows at a time (rows t = 16 h + tl of round
-// h): row tl holds key c at column q = c - tl + 16, in [1, 79]. A row writes the
-// same 64 columns in every round, so the ones it never writes stay zero, and
-// column q of round h holds exactly the entries of diagonal e = t - c + 63 =
-// 16 h + 79 - q. A row pitch of 89 floats puts the two half-waves' writes (rows
-// tl and tl + 4, the same 32 keys) on complementary halves of the 64 banks; a
-// row's columns are read by consecutive lanes.
-constexpr int PSTR = 89;
-constexpr int PROWS = 16;
-constexpr int PCOLS = 80;
+// Diagonal sums of a 64 x 64 probability tile. In the MFMA layout a lane holds
+// one key column c and, in each group of four accumulator slots, four
+// consecutive query rows t0 .. t0 + 3. A chain of row shifts by one lane
+// (within 16-lane rows) adds those four rows along their diagonals in
+// registers: after it, lane c holds the sum over b of P[t0 + b][c - 3 + b]
+// (diagonal t0 + 3 - c), and the pieces that leave a 16-lane row at its top
+// lane are kept there as carries. The chain sums of 32 query rows (8 row groups
+// u) then go through LDS in a skewed layout: group u writes key c at column
+// c - 4u + 28 of row u, and the carries of groups u < 4 (u >= 4) go to row 8
+// (9) at the column of the diagonal they belong to (no two carries share a
+// cell). Column q of these ten rows then holds pieces of exactly one diagonal,
+// 32 mq + 94 - q for the query rows 32 mq .. + 31, and lane s adds up column s
+// (lanes < 32 also column s + 64) over the rows. Cells that are never written
+// stay zero. A row pitch of 100 floats puts the two half-waves' chain stores
+// on complementary halves of the 64 banks.
+constexpr int PSTR = 100;
+constexpr int PROWS = 10;
+constexpr int PCOLS = 96;
 // s_waitcnt immediate on gfx9: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVmem0 = 0x0F70;
 constexpr int kWaitVmem4 = 0x0F74;  // vmcnt(4): the newest tile's four copies may be in flight
 
 __device__ __forceinline__ int swz(int x) { return ((x & 3) << 2) | ((x >> 2) & 3); }
+
+// Four floats from 16-byte aligned LDS, read as one 128-bit integer vector. Read
+// as float4, the compiler makes this load wait for every buffer-to-LDS copy in
+// flight (here the next K tile, which it cannot tell apart), and the copy
+// would no longer overlap the tile's work.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
+  return __builtin_bit_cast(f32x4, *(const u32x4*)(const void*)p);
+}
+
+// x of the next lower lane within each 16-lane row, 0 in the row's lowest lane (DPP row_shr:1)
+__device__ __forceinline__ float row_shr1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xF, 0xF, true));
+}
 
 // K tiles go HBM -> LDS with buffer loads into a ring of three buffers: tile
 // T + 2 streams into the buffer tile T - 1 used while tile T is worked on, so
@@ -56,16 +80,23 @@ __device__ __forceinline__ int swz(int x) { return ((x & 3) << 2) | ((x >> 2) & 
 struct VsSmem1 {
   uint16_t kt[kRing][kTileHalves];
 };
-struct VsSmem2 {
-  uint16_t kt[kRing][kTileHalves];
-  float pt[4][PROWS * PSTR + 64];  // + 64: lanes 16..63 read past the 80 columns of the last row
-  float pacc[4][4 * PCOLS];          // per wave: column partials of the four rounds of a tile
-  float crow[4][64];                 // per wave: max + log2(sum) of each last-query row
+// Pass 2 holds two K tiles (T, and T + 1 in flight) so that two workgroups of
+// eight waves fit a compute unit. Results of a tile are exchanged between the
+// two waves of a head through buffers indexed by tile parity: the merge of tile
+// T (after the barrier that ends it) and the writes of tile T + 2 (after the
+// barrier that ends tile T + 1) never overlap.
+struct alignas(16) VsSmem2 {
+  uint16_t kt[2][kTileHalves];
+  float pt[8][PROWS * PSTR];     // per wave: diagonal staging rows
+  float pacc[2][4][2 * PCOLS];   // [parity][head]: diagonal columns of query rows 0..31, then 32..63
+  float csum[2][4][2][64];       // [parity][head][half]: column sums of 32 query rows
+  float crow[4][64];             // [head]: max + log2(sum) of each last-query row
 };
 
-template <int PASS>
-__device__ __forceinline__ void vs_pass(const VsLaunch& a) {
-  __shared__ typename std::conditional<PASS == 1, VsSmem1, VsSmem2>::type sm;
+// Pass 1: per-chunk (max, sum of exp2) of every last-query row.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void vs_pass1_kernel(
+    const VsLaunch a) {
+  __shared__ VsSmem1 sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -94,13 +125,6 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
   }
   float run_m[2] = {-INFINITY, -INFINITY};
   float run_l[2] = {0.f, 0.f};
-  // pass 2: each row's normaliser in log2 units, max + log2(sum), kept in LDS;
-  // the staging rows start at zero
-  if constexpr (PASS == 2) {
-    sm.crow[wave][lane] = active ? a.row_m[slot * 64 + lane] : 0.f;
-    for (int x = lane; x < PROWS * PSTR + 64; x += 64) sm.pt[wave][x] = 0.f;
-  }
-
   // K tiles: wave w's copy i fills LDS chunks [256 i + 64 w, +64) = rows
   // 16 i + 4 w .. +3, 16 lanes per 256-byte row, from the swizzled source chunk;
   // rows past n read row n - 1 (they are masked)
@@ -137,7 +161,7 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
     const char* ktc = (const char*)sm.kt[cur];
     // the causal mask only bites in tiles that reach past the first last-query row
     const bool edge = (int64_t)T * kBlock + kBlock - 1 > (int64_t)n - r;
-    if constexpr (PASS == 1) if (active) {
+    if (active) {
       f32x16 s[2][2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
@@ -180,116 +204,6 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
         }
       }
     }
-    if constexpr (PASS == 2) {
-      // normalised probabilities P = exp2(s sl2 - crow) of S = Q K^T: lane l holds
-      // key c = 32 mk + (l & 31) and, in accumulator slot i, query row
-      // t = 32 mq + 8 (i >> 2) + 4 g + (i & 3). Column sums add up in registers
-      // (then across the two half-waves); for the diagonal sums every 16 rows go
-      // through LDS, where lane s adds up column s (and lanes s < 16 column
-      // s + 64) over the 16 rows: one partial per round and column, merged per
-      // diagonal after the tile.
-      float* pt = sm.pt[wave];
-      // row tl (of these 16), column c - tl + 16, with c = 32 mk + r32 and
-      // tl = 8 (e >> 2) + 4 g + (e & 3), is pw + 32 mk + (PSTR - 1)(8 (e >> 2) + (e & 3)):
-      // one lane base and a constant offset per store, the same in every round
-      float* const pw = pt + r32 + 4 * g * (PSTR - 1) + 16;
-      float* const pr = pt + lane;
-      float cs[2] = {0.f, 0.f};
-      float acc[4][2];  // round h, column lane (0) / lane + 64 (1, lanes < 16)
-      // every row present and the tile below the causal edge: nothing is masked
-      const bool plain = !edge && r == 64;
-#pragma unroll
-      for (int mq = 0; mq < 2; ++mq) {
-        f32x16 sc[2];
-        if (active) {
-#pragma unroll
-          for (int mk = 0; mk < 2; ++mk) {
-            sc[mk] = f32x16{};
-            const char* kp = ktc + 32 * mk * 256;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-              sc[mk] = mfma32(qr[mq][ks], *(const u32x4*)(kp + (kofs ^ (ks << 5))), sc[mk]);
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {  // round h = 2 mq + hh: rows 16 h .. + 15, slots i = 8 hh .. + 7
-          const int h = 2 * mq + hh;
-          if (active) {
-            float cr[8];
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-              const float4 v4 = *(const float4*)&sm.crow[wave][16 * h + 8 * q2 + 4 * g];
-              cr[4 * q2] = v4.x;
-              cr[4 * q2 + 1] = v4.y;
-              cr[4 * q2 + 2] = v4.z;
-              cr[4 * q2 + 3] = v4.w;
-            }
-#pragma unroll
-            for (int mk = 0; mk < 2; ++mk) {
-              const int64_t j = (int64_t)T * kBlock + 32 * mk + r32;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int t = 16 * h + 8 * (e >> 2) + 4 * g + (e & 3);
-                float pv = fast_exp2(fmaf(sc[mk][8 * hh + e], sl2, -cr[e]));
-                if (!plain) pv = (t < r && (!edge || j <= (int64_t)n - r + t)) ? pv : 0.f;
-                cs[mk] += pv;
-                pw[32 * mk + (PSTR - 1) * (8 * (e >> 2) + (e & 3))] = pv;
-              }
-            }
-          }
-          // pt is private to the wave and a wave's LDS accesses complete in order:
-          // no workgroup barrier around its staging
-          __builtin_amdgcn_wave_barrier();
-          if (active) {
-            float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-            for (int tl = 0; tl < PROWS; ++tl) {
-              a0 += pr[tl * PSTR];
-              a1 += pr[tl * PSTR + 64];  // a column of the row only for lanes < 16
-            }
-            acc[h][0] = a0;
-            acc[h][1] = a1;
-          }
-          __builtin_amdgcn_wave_barrier();  // the next rows overwrite pt
-        }
-      }
-      if (active) {
-        // the other half-wave holds the same keys' other query rows
-        cs[0] += __shfl_xor(cs[0], 32);
-        cs[1] += __shfl_xor(cs[1], 32);
-        const int64_t j = (int64_t)T * kBlock + lane;
-        if (j < n) a.vcol[(size_t)slot * n + j] = g ? cs[1] : cs[0];
-      }
-      // diagonal e = 16 h + 79 - q: the round partials go to LDS by (h, q), then lane l
-      // adds up diagonals l and l + 64 over the rounds, in round order
-      float* pa = sm.pacc[wave];
-      if (active) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          pa[h * PCOLS + lane] = acc[h][0];
-          if (lane < 16) pa[h * PCOLS + 64 + lane] = acc[h][1];
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      if (active) {
-        float dd[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int e = lane + 64 * u;  // diagonal (e = 127 has no entries)
-          float x = 0.f;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            const int q = 16 * h + 79 - e;
-            if (q >= 0 && q < PCOLS) x += pa[h * PCOLS + q];
-          }
-          dd[u] = x;
-        }
-        float* dp = a.dpart + ((size_t)slot * a.ntiles + T) * 128;
-        dp[lane] = dd[0];
-        dp[64 + lane] = dd[1];
-      }
-      __builtin_amdgcn_wave_barrier();  // the next tile overwrites pa
-    }
     // tile T + 1 landed (only tile T + 2's copies may still be in flight), then one
     // barrier: tile T + 1 visible to every wave, tile T released
     if (T + 2 < t1)
@@ -299,7 +213,7 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
     __syncthreads();
     cur = cur == 2 ? 0 : cur + 1;
   }
-  if constexpr (PASS == 1) if (active) {
+  if (active) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const float om = __shfl_xor(run_m[nt], 32);
@@ -317,20 +231,184 @@ __device__ __forceinline__ void vs_pass(const VsLaunch& a) {
   }
 }
 
-// Pass 1 fits 3 waves per SIMD (168 VGPRs, a few spilled: 1.15 -> 0.96 ms at 1M
-// tokens); pass 2 runs 2 (at 3 waves it spilled 35 VGPRs and took 3.1 instead
-// of 2.0 ms).
-template <int PASS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void vs_pass_kernel(
+// Pass 2: normalised probabilities P = exp2(s sl2 - crow) of S = Q K^T, their
+// column sums and per-tile diagonal sums. Wave w takes query head w & 3 of the
+// group and query rows 32 mq .. + 31, mq = w >> 2: lane l holds key
+// c = 32 mk + (l & 31) and, in accumulator slot 4 a + b, query row
+// t = 32 mq + 8 a + 4 g + b.
+__global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(4))) void vs_pass2_kernel(
     const VsLaunch a) {
-  vs_pass<PASS>(a);
-}
-template <>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void vs_pass_kernel<1>(
-    const VsLaunch a) {
-  vs_pass<1>(a);
-}
+  __shared__ VsSmem2 sm;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hw = wave & 3;
+  const int mq = wave >> 2;
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+  const VsGroup* grp = &a.groups[blockIdx.y];
+  const int ch = blockIdx.x;
+  const int n = a.n;
+  const int r = a.r;
+  const bool active = hw < grp->cnt;
+  const int head = active ? grp->head[hw] : 0;
+  const int slot = active ? grp->slot[hw] : 0;
+  const uint16_t* kh = a.k + (size_t)grp->kv * n * kHeadDim;
+  const float sl2 = a.scale_log2;
 
+  // query rows t = 32 mq + r32 as MFMA A operands
+  u32x4 qr[8];
+  {
+    const int t = 32 * mq + r32;
+    const bool ok = active && t < r;
+    const int64_t i = (int64_t)n - r + (ok ? t : 0);
+    const uint16_t* qp = a.q + ((size_t)head * n + i) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qr[ks] = ok ? *(const u32x4*)(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+  }
+  // each row's normaliser in log2 units, max + log2(sum); the staging rows start at zero
+  if (g == 0) sm.crow[hw][32 * mq + r32] = active ? a.row_m[slot * 64 + 32 * mq + r32] : 0.f;
+  for (int x = lane; x < PROWS * PSTR; x += 64) sm.pt[wave][x] = 0.f;
+
+  // K tiles: wave w's copy i fills rows 32 i + 4 w .. + 3, 16 lanes per 256-byte
+  // row, from the swizzled source chunk; rows past n read row n - 1 (they are masked)
+  const rsrc_t kbuf = buffer_of(kh, (uint32_t)n * (kHeadDim * 2));
+  auto issue_tile = [&](int T, uint16_t* kt, int ln) {
+    const int crow_lo = 4 * wave + (ln >> 4);
+    const uint32_t cbyte = (uint32_t)(((ln & 15) ^ swz(crow_lo)) * 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int j = T * kBlock + 32 * i + crow_lo;
+      j = j < n ? j : n - 1;
+      copy16(kbuf, kt + (512 * i + 64 * wave) * 8, (uint32_t)j * 256u + cbyte, 0u);
+    }
+  };
+  float* const pt = sm.pt[wave];
+
+  const int t0 = ch * a.tiles_per_chunk;
+  const int t1 = t0 + a.tiles_per_chunk < a.ntiles ? t0 + a.tiles_per_chunk : a.ntiles;
+  if (t0 < t1) issue_tile(t0, sm.kt[0], lane);
+  // tile t0, the query operands and the row statistics have arrived
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+  __syncthreads();
+  int cur = 0;
+  for (int T = t0; T < t1; ++T) {
+    // Offsets derived from the lane index are recomputed in every tile (a few
+    // integer operations) from an opaque copy of it, rather than held in
+    // registers across the loop: at four waves per SIMD the registers are full.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lg = ln >> 5;
+    const int lr = ln & 31;
+    // tile T + 1 into the buffer tile T - 1 used (every wave left it at the last barrier)
+    if (T + 1 < t1) issue_tile(T + 1, sm.kt[cur ^ 1], ln);
+    const char* ktc = (const char*)sm.kt[cur];
+    const int par = (T - t0) & 1;
+    // the causal mask only bites in tiles that reach past the first last-query row
+    const bool edge = (int64_t)T * kBlock + kBlock - 1 > (int64_t)n - r;
+    // every row present and the tile below the causal edge: nothing is masked
+    const bool plain = !edge && r == 64;
+    float cs[2] = {0.f, 0.f};
+    if (active) {
+      // operand reads: row x = 32 mk + lr, chunk 2 ks + lg
+      const int kofs = lr * 256 + ((lg ^ swz(lr)) << 4);
+      f32x16 sc[2];
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk) {
+        sc[mk] = f32x16{};
+        const char* kp = ktc + 32 * mk * 256;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) sc[mk] = mfma32(qr[ks], *(const u32x4*)(kp + (kofs ^ (ks << 5))), sc[mk]);
+      }
+      // chain sum of block (mk, a): row u = 2 a + g, column 32 mk + r32 - 4 u + 28
+      float* const pw = pt + lg * (PSTR - 4) + lr + 28;
+      // carries of block (mk, a) (lanes r32 = 15, 31): row 8 + (a >> 1), columns
+      // 32 mk + r32 + 29 - 4 u (chain step 2), + 1 (step 1), + 2 (step 0)
+      float* const pc = pt + 8 * PSTR + lr + 29 - 4 * lg;
+      const bool carry_lane = (lr & 15) == 15;
+      // in edge tiles key slot c is visible to row t iff c - t <= n - r - 64 T
+      const int dlim = n - r - T * kBlock;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 cr = lds_f32x4(&sm.crow[hw][32 * mq + 8 * a4 + 4 * lg]);
+        float carry[2][3];
+#pragma unroll
+        for (int mk = 0; mk < 2; ++mk) {
+          float pv[4];
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const int t = 32 * mq + 8 * a4 + 4 * lg + b4;
+            const int c = 32 * mk + lr;
+            float p = fast_exp2(fmaf(sc[mk][4 * a4 + b4], sl2, -cr[b4]));
+            if (!plain) p = (t < r && (!edge || c - t <= dlim)) ? p : 0.f;
+            cs[mk] += p;
+            pv[b4] = p;
+          }
+          const float x0 = pv[0];
+          const float x1 = pv[1] + row_shr1(x0);
+          const float x2 = pv[2] + row_shr1(x1);
+          const float x3 = pv[3] + row_shr1(x2);
+          pw[a4 * (2 * PSTR - 8) + 32 * mk] = x3;
+          carry[mk][0] = x2;
+          carry[mk][1] = x1;
+          carry[mk][2] = x0;
+        }
+        if (carry_lane) {
+#pragma unroll
+          for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) pc[(a4 >> 1) * PSTR + 32 * mk - 8 * a4 + k] = carry[mk][k];
+        }
+      }
+    }
+    // pt is private to the wave and a wave's LDS accesses complete in order:
+    // no workgroup barrier around its staging
+    __builtin_amdgcn_wave_barrier();
+    if (active) {
+      float* pa = sm.pacc[par][hw] + mq * PCOLS;
+      const float* pr = pt + ln;
+      float a0 = 0.f;
+#pragma unroll
+      for (int row = 0; row < PROWS; ++row) a0 += pr[row * PSTR];
+      pa[ln] = a0;
+      if (ln < 32) {
+        float a1 = 0.f;
+#pragma unroll
+        for (int row = 0; row < PROWS; ++row) a1 += pr[row * PSTR + 64];
+        pa[64 + ln] = a1;
+      }
+      // the other half-wave holds the same keys' other four query rows of each group
+      cs[0] += __shfl_xor(cs[0], 32);
+      cs[1] += __shfl_xor(cs[1], 32);
+      sm.csum[par][hw][mq][ln] = lg ? cs[1] : cs[0];
+    }
+    __builtin_amdgcn_wave_barrier();  // the next tile's rows overwrite pt
+    // tile T + 1 landed; one barrier: it is visible to every wave, tile T released,
+    // and both halves of every head have left their sums of tile T
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __syncthreads();
+    if (active && mq == 0) {
+      const int64_t j = (int64_t)T * kBlock + ln;
+      if (j < n) a.vcol[(size_t)slot * n + j] = sm.csum[par][hw][0][ln] + sm.csum[par][hw][1][ln];
+      // diagonal e = t - c + 63 sits in column 94 - e of query rows 0..31 and in
+      // column 126 - e of rows 32..63; lane l takes diagonals l and l + 64 (127 has no entries)
+      const float* pa = sm.pacc[par][hw];
+      float dd[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = ln + 64 * u;
+        float x = 0.f;
+        if (e <= 94) x += pa[94 - e];
+        if (e >= 31 && e <= 126) x += pa[PCOLS + 126 - e];
+        dd[u] = x;
+      }
+      float* dp = a.dpart + ((size_t)slot * a.ntiles + T) * 128;
+      dp[ln] = dd[0];
+      dp[64 + ln] = dd[1];
+    }
+    cur ^= 1;
+  }
+}
 // Merge the chunk partials of every row in chunk order: max and 1 / sum.
 __global__ __launch_bounds__(64) void vs_row_combine_kernel(const VsLaunch a) {
   // one wave per (head, row): lane c takes chunks c, c + 64, ..., then a
@@ -381,12 +459,12 @@ __global__ __launch_bounds__(256) void vs_diag_reduce_kernel(const VsLaunch a) {
 
 hipError_t launch_vs_scores(const VsLaunch& a, hipStream_t stream) {
   dim3 grid(a.nchunks, a.ngroups);
-  hipLaunchKernelGGL(vs_pass_kernel<1>, grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(vs_pass1_kernel, grid, dim3(kThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(vs_row_combine_kernel, dim3(64, a.n_slots), dim3(64), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(vs_pass_kernel<2>, grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(vs_pass2_kernel, grid, dim3(kThreads2), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 g2((unsigned)((a.n + 255) / 256), a.n_slots);
   hipLaunchKernelGGL(vs_diag_reduce_kernel, g2, dim3(256), 0, stream, a);
