@@ -175,33 +175,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           s[mt][1] = mfma32(av, qr[1][ks], s[mt][1]);
         }
       }
-      {
+      // masked slots become -inf in the raw scores (only in tiles that reach
+      // past the first last-query row, or when fewer than 64 rows exist)
+      if (edge || r < 64) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           const int t = 32 * nt + r32;
           // key slot kx = 32 mt + 8 (i >> 2) + (i & 3) of this lane (key T 64 + kx + 4 g) is visible
           // iff kx <= lim: every slot below the causal edge, none for a row past r
           const int lim = t >= r ? -1 : (edge ? (n - r + t) - T * kBlock - 4 * g : kBlock);
-          float mx = -INFINITY;
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int kx = 32 * mt + 8 * (i >> 2) + (i & 3);
-              const float x = kx <= lim ? s[mt][nt][i] * sl2 : -INFINITY;
-              s[mt][nt][i] = x;
-              mx = fmaxf(mx, x);
+              s[mt][nt][i] = kx <= lim ? s[mt][nt][i] : -INFINITY;
             }
-          const float m_new = fmaxf(run_m[nt], mx);
-          const float m_use = m_new == -INFINITY ? 0.f : m_new;
-          float acc = 0.f;
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc += fast_exp2(s[mt][nt][i] - m_use);
-          run_l[nt] = run_l[nt] * fast_exp2(run_m[nt] - m_use) + acc;
-          run_m[nt] = m_new;
         }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        // the row max of the raw scores (scaling by sl2 > 0 keeps the order),
+        // as four three-input max chains
+        float mq4[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float x = fmaxf(s[0][nt][4 * c], s[0][nt][4 * c + 1]);
+          x = fmaxf(x, fmaxf(s[0][nt][4 * c + 2], s[0][nt][4 * c + 3]));
+          x = fmaxf(x, fmaxf(s[1][nt][4 * c], s[1][nt][4 * c + 1]));
+          mq4[c] = fmaxf(x, fmaxf(s[1][nt][4 * c + 2], s[1][nt][4 * c + 3]));
+        }
+        const float mx = fmaxf(fmaxf(mq4[0], mq4[1]), fmaxf(mq4[2], mq4[3])) * sl2;
+        const float m_new = fmaxf(run_m[nt], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        // sum of exp2(s sl2 - m), one fused multiply-add per element, in two chains
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          acc0 += fast_exp2(fmaf(s[0][nt][i], sl2, -m_use));
+          acc1 += fast_exp2(fmaf(s[1][nt][i], sl2, -m_use));
+        }
+        run_l[nt] = run_l[nt] * fast_exp2(run_m[nt] - m_use) + (acc0 + acc1);
+        run_m[nt] = m_new;
       }
     }
     // tile T + 1 landed (only tile T + 2's copies may still be in flight), then one
@@ -309,17 +324,12 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(4))) 
     // every row present and the tile below the causal edge: nothing is masked
     const bool plain = !edge && r == 64;
     float cs[2] = {0.f, 0.f};
-    if (active) {
-      // operand reads: row x = 32 mk + lr, chunk 2 ks + lg
-      const int kofs = lr * 256 + ((lg ^ swz(lr)) << 4);
-      f32x16 sc[2];
-#pragma unroll
-      for (int mk = 0; mk < 2; ++mk) {
-        sc[mk] = f32x16{};
-        const char* kp = ktc + 32 * mk * 256;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) sc[mk] = mfma32(qr[ks], *(const u32x4*)(kp + (kofs ^ (ks << 5))), sc[mk]);
-      }
+    // the tile's probabilities, column sums and diagonal chain sums; PLAIN:
+    // nothing of the tile is masked (a separate copy of the code, so that the
+    // common case carries no per-element test)
+    f32x16 sc[2];
+    auto tile_probs = [&](auto plain_c) {
+      constexpr bool PLAIN = decltype(plain_c)::value;
       // chain sum of block (mk, a): row u = 2 a + g, column 32 mk + r32 - 4 u + 28
       float* const pw = pt + lg * (PSTR - 4) + lr + 28;
       // carries of block (mk, a) (lanes r32 = 15, 31): row 8 + (a >> 1), columns
@@ -340,7 +350,7 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(4))) 
             const int t = 32 * mq + 8 * a4 + 4 * lg + b4;
             const int c = 32 * mk + lr;
             float p = fast_exp2(fmaf(sc[mk][4 * a4 + b4], sl2, -cr[b4]));
-            if (!plain) p = (t < r && (!edge || c - t <= dlim)) ? p : 0.f;
+            if (!PLAIN) p = (t < r && (!edge || c - t <= dlim)) ? p : 0.f;
             cs[mk] += p;
             pv[b4] = p;
           }
@@ -359,7 +369,24 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
             for (int k = 0; k < 3; ++k) pc[(a4 >> 1) * PSTR + 32 * mk - 8 * a4 + k] = carry[mk][k];
         }
+        // one group of four query rows at a time (keeps the live probabilities few)
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    if (active) {
+      // operand reads: row x = 32 mk + lr, chunk 2 ks + lg
+      const int kofs = lr * 256 + ((lg ^ swz(lr)) << 4);
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk) {
+        sc[mk] = f32x16{};
+        const char* kp = ktc + 32 * mk * 256;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) sc[mk] = mfma32(qr[ks], *(const u32x4*)(kp + (kofs ^ (ks << 5))), sc[mk]);
+      }
+      if (plain)
+        tile_probs(std::true_type{});
+      else
+        tile_probs(std::false_type{});
     }
     // pt is private to the wave and a wave's LDS accesses complete in order:
     // no workgroup barrier around its staging
