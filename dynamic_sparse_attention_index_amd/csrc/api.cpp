@@ -90,7 +90,7 @@ minf_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 int vs_max_chunks(int64_t n) { return (int)std::min<int64_t>(nblocks(n), 2048); }
 
 struct VsWs {
-  float *part_m, *part_l, *row_m, *row_il, *vcol, *slsum, *dpart;
+  float *part_m, *part_l, *row_m, *row_il, *vcol, *slsum, *dedge;
   int32_t *tk_hist, *tk_state, *tk_cnt;
   int tk_chunk, tk_nchunks;
   size_t bytes;
@@ -100,7 +100,6 @@ VsWs carve_vs(void* base, int64_t n, int n_heads) {
   Carver c{(char*)base};
   const size_t nh = (size_t)std::max(n_heads, 1);
   const size_t mc = (size_t)vs_max_chunks(n);
-  const size_t nt = (size_t)nblocks(n);
   VsWs w;
   w.part_m = c.take<float>(nh * 64 * mc);
   w.part_l = c.take<float>(nh * 64 * mc);
@@ -108,13 +107,13 @@ VsWs carve_vs(void* base, int64_t n, int n_heads) {
   w.row_il = c.take<float>(nh * 64);
   w.vcol = c.take<float>(nh * (size_t)n);
   w.slsum = c.take<float>(nh * (size_t)n);
-  w.dpart = c.take<float>(nh * nt * 128);
+  w.dedge = c.take<float>(nh * mc * 128);
   // top-k scratch for the two score rows of every head
   w.tk_chunk = topk_chunk_len((int)std::min<int64_t>(n, 1 << 30));
   w.tk_nchunks = (int)((n + w.tk_chunk - 1) / w.tk_chunk);
   w.tk_hist = c.take<int32_t>(2 * nh * 2048);
   w.tk_state = c.take<int32_t>(2 * nh * 4);
-  w.tk_cnt = c.take<int32_t>(2 * nh * 2 * (size_t)w.tk_nchunks);
+  w.tk_cnt = c.take<int32_t>(2 * nh * 2 * 4 * (size_t)w.tk_nchunks);
   w.bytes = c.off;
   return w;
 }
@@ -160,7 +159,7 @@ minf_status run_vs_scores(const void* q, const void* k, int64_t n, int hq, int h
     a.row_il = w.row_il;
     a.vcol = w.vcol;
     a.slsum = w.slsum;
-    a.dpart = w.dpart;
+    a.dedge = w.dedge;
     for (int i = 0; i < a.ngroups; ++i) a.groups[i] = groups[g0 + i];
     hipError_t e = launch_vs_scores(a, stream);
     if (e != hipSuccess) return hip_fail(e, "VS score kernels");

@@ -78,7 +78,7 @@ struct VsLaunch {
   float* row_il;   // [n_slots][64]
   float* vcol;     // [n_slots][n]
   float* slsum;    // [n_slots][n]
-  float* dpart;    // [n_slots][ntiles][128]
+  float* dedge;    // [n_slots][nchunks][128]: diagonals e = 0..62 of a chunk's last tile, e = 64..126 of its first
   VsGroup groups[kMaxVsGroups];
 };
 
@@ -97,7 +97,7 @@ struct TopkLaunch {
   int32_t n, chunk, nchunks;
   int32_t* hist;   // [rows][2048] scratch histograms
   int32_t* state;  // [rows][4] prefix, prefix mask, rank left
-  int32_t* cnt;    // [rows][2][nchunks] keys above / equal to the threshold per chunk
+  int32_t* cnt;    // [rows][2][nchunks * 4] keys above / equal to the threshold per chunk quarter
 };
 int topk_chunk_len(int n);
 hipError_t launch_topk(const TopkLaunch& a, hipStream_t stream);

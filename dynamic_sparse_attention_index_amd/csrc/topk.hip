@@ -14,9 +14,10 @@
 //  2. after the last pass the prefix is the exact k-th largest key T and the
 //     rank is the number of keys equal to T that are kept (lowest indices
 //     first); each chunk counts its keys > T and == T;
-//  3. each chunk adds up the counts of the chunks before it, keeps its keys
-//     > T and its share of the keys == T, and writes their indices in
-//     ascending order at its offset.
+//  3. each wave scans a contiguous quarter of a chunk: it adds up the counts
+//     of the quarters before it, keeps its keys > T and its share of the keys
+//     == T, and writes their indices in ascending order at its offset
+//     (positions from wave ballots, no block-wide synchronisation).
 //
 // Only integer atomics are used, so the result does not depend on the order
 // in which workgroups run.
@@ -132,92 +133,105 @@ __global__ __launch_bounds__(64) void topk_select_kernel(const TopkLaunch a) {
   }
 }
 
-__device__ __forceinline__ int block_sum(int x, int* wsum) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  if (lane == 0) wsum[wave] = x;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkThreads / 64; ++w) t += wsum[w];
-  __syncthreads();
-  return t;
+// Each wave scans a contiguous quarter of its chunk: [wlo, whi).
+__device__ __forceinline__ void wave_range(const TopkLaunch& a, int& wlo, int& whi) {
+  const int lo = blockIdx.x * a.chunk;
+  const int hi = min(a.n, lo + a.chunk);
+  const int sub = a.chunk / (kTopkThreads / 64);
+  wlo = min(hi, lo + (int)(threadIdx.x >> 6) * sub);
+  whi = min(hi, wlo + sub);
 }
 
-// Keys above and equal to the threshold in each chunk.
+// Keys above and equal to the threshold in each wave's quarter of each chunk.
 __global__ __launch_bounds__(kTopkThreads) void topk_count_kernel(const TopkLaunch a) {
-  __shared__ int wsum[kTopkThreads / 64];
   const int r = blockIdx.y;
   const RowRef rf = row_ref(a, r);
   if (rf.k <= 0 || rf.k >= a.n) return;
   const uint32_t thr = (uint32_t)a.state[4 * r];
-  const int lo = blockIdx.x * a.chunk;
-  const int hi = min(a.n, lo + a.chunk);
+  const int lane = threadIdx.x & 63;
+  int wlo, whi;
+  wave_range(a, wlo, whi);
   int gt = 0, eq = 0;
-  for (int base = lo + threadIdx.x; base < hi; base += 8 * kTopkThreads) {
+  for (int base = wlo + lane; base < whi; base += 8 * 64) {
     uint32_t u[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      const int i = base + x * kTopkThreads;
-      u[x] = i < hi ? sortable_key(rf.src[i]) : 0u;  // key 0 (a NaN pattern) is below every real key
+      const int i = base + x * 64;
+      u[x] = i < whi ? sortable_key(rf.src[i]) : 0u;  // key 0 (a NaN pattern) is below every real key
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
-      const bool in = base + x * kTopkThreads < hi;
+      const bool in = base + x * 64 < whi;
       gt += in && u[x] > thr;
       eq += in && u[x] == thr;
     }
   }
-  gt = block_sum(gt, wsum);
-  eq = block_sum(eq, wsum);
-  if (threadIdx.x == 0) {
-    int* c = a.cnt + (size_t)r * 2 * a.nchunks;
-    c[blockIdx.x] = gt;
-    c[a.nchunks + blockIdx.x] = eq;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    gt += __shfl_xor(gt, off);
+    eq += __shfl_xor(eq, off);
+  }
+  if (lane == 0) {
+    constexpr int kW = kTopkThreads / 64;
+    const int e = blockIdx.x * kW + (threadIdx.x >> 6);
+    int* c = a.cnt + (size_t)r * 2 * kW * a.nchunks;
+    c[e] = gt;
+    c[kW * a.nchunks + e] = eq;
   }
 }
 
-// Ordered write-out: chunk c starts after the keys kept by chunks 0..c-1.
+// Ordered write-out: each wave starts after the keys kept by the quarters
+// before it (all earlier chunks, then the earlier waves of its chunk) and
+// places its own with ballots, 64 keys at a time.
 __global__ __launch_bounds__(kTopkThreads) void topk_write_kernel(const TopkLaunch a) {
-  __shared__ int wsum[kTopkThreads / 64];
   const int r = blockIdx.y;
   const RowRef rf = row_ref(a, r);
   if (rf.k <= 0) return;
-  const int lo = blockIdx.x * a.chunk;
-  const int hi = min(a.n, lo + a.chunk);
+  const int lane = threadIdx.x & 63;
+  int wlo, whi;
+  wave_range(a, wlo, whi);
   if (rf.k >= a.n) {  // full budget: every index, in order
-    for (int i = lo + threadIdx.x; i < hi; i += kTopkThreads) rf.dst[i] = i;
+    for (int i = wlo + lane; i < whi; i += 64) rf.dst[i] = i;
     return;
   }
+  constexpr int kW = kTopkThreads / 64;
   const uint32_t thr = (uint32_t)a.state[4 * r];
   const int need_eq = a.state[4 * r + 2];
-  const int* c = a.cnt + (size_t)r * 2 * a.nchunks;
+  const int e = blockIdx.x * kW + (threadIdx.x >> 6);
+  const int* c = a.cnt + (size_t)r * 2 * kW * a.nchunks;
   int gt_before = 0, eq_before = 0;
-  for (int j = threadIdx.x; j < (int)blockIdx.x; j += kTopkThreads) {
+  for (int j = lane; j < e; j += 64) {
     gt_before += c[j];
-    eq_before += c[a.nchunks + j];
+    eq_before += c[kW * a.nchunks + j];
   }
-  gt_before = block_sum(gt_before, wsum);
-  eq_before = block_sum(eq_before, wsum);
-  const int eq_here = c[a.nchunks + blockIdx.x];
-  const int take_eq = max(0, min(eq_here, need_eq - eq_before));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    gt_before += __shfl_xor(gt_before, off);
+    eq_before += __shfl_xor(eq_before, off);
+  }
   int written = gt_before + min(eq_before, need_eq);
-  int eq_seen = 0;
-  for (int base = lo; base < hi; base += kTopkThreads) {
-    const int i = base + threadIdx.x;
-    const uint32_t u = i < hi ? sortable_key(rf.src[i]) : 0u;
-    const bool gt = i < hi && u > thr;
-    const bool eq = i < hi && u == thr;
-    int eq_tot;
-    const int eq_rank = block_excl_scan_count<kTopkThreads>(eq, wsum, eq_tot);
-    const bool sel = gt || (eq && eq_seen + eq_rank < take_eq);
-    int sel_tot;
-    const int pos = block_excl_scan_count<kTopkThreads>(sel, wsum, sel_tot);
-    if (sel) rf.dst[written + pos] = i;
-    eq_seen += eq_tot;
-    written += sel_tot;
+  int eq_seen = eq_before;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int base = wlo; base < whi; base += 8 * 64) {
+    uint32_t u[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int i = base + x * 64 + lane;
+      u[x] = i < whi ? sortable_key(rf.src[i]) : 0u;
+    }
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int i = base + x * 64 + lane;
+      const bool in = i < whi;
+      const bool gt = in && u[x] > thr;
+      const bool eq = in && u[x] == thr;
+      const uint64_t beq = __ballot(eq);
+      const bool sel = gt || (eq && eq_seen + (int)__popcll(beq & below) < need_eq);
+      const uint64_t bsel = __ballot(sel);
+      if (sel) rf.dst[written + (int)__popcll(bsel & below)] = i;
+      written += (int)__popcll(bsel);
+      eq_seen += (int)__popcll(beq);
+    }
   }
 }
 

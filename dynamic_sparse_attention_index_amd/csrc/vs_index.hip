@@ -17,9 +17,10 @@
 //    column and 16 query rows of each 32x32 product), normalises them, sums
 //    the columns in registers (complete column sums), and reduces the 64x64
 //    probability tile along its 127 diagonals: four rows at a time by DPP
-//    lane shifts in registers, then through LDS (per-tile partials; a
-//    diagonal spans at most two tiles and the two partials are added in tile
-//    order by a separate kernel);
+//    lane shifts in registers, then through LDS; a diagonal spans at most two
+//    consecutive tiles, whose partials are added in tile order by the
+//    workgroup that runs both, or for the tiles at a chunk edge by a small
+//    separate kernel;
 //  * top-k (topk.hip) is a radix select on the sortable bit pattern spread
 //    over many workgroups per row, ties to the lower index, emitted in
 //    ascending index order.
@@ -91,6 +92,7 @@ struct alignas(16) VsSmem2 {
   float pacc[2][4][2 * PCOLS];   // [parity][head]: diagonal columns of query rows 0..31, then 32..63
   float csum[2][4][2][64];       // [parity][head][half]: column sums of 32 query rows
   float crow[4][64];             // [head]: max + log2(sum) of each last-query row
+  float dkeep[4][64];            // [head]: diagonals e = 0..63 of the previous tile (merging wave only)
 };
 
 // Pass 1: per-chunk (max, sum of exp2) of every last-query row.
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ VsSmem1 sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps head, slot and pointers scalar
   const int g = lane >> 5;
   const int r32 = lane & 31;
   const VsGroup* grp = &a.groups[blockIdx.y];
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(4))) 
   __shared__ VsSmem2 sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps head, slot and pointers scalar
   const int hw = wave & 3;
   const int mq = wave >> 2;
   const int g = lane >> 5;
@@ -429,9 +431,37 @@ __global__ __launch_bounds__(kThreads2) __attribute__((amdgpu_waves_per_eu(4))) 
         if (e >= 31 && e <= 126) x += pa[PCOLS + 126 - e];
         dd[u] = x;
       }
-      float* dp = a.dpart + ((size_t)slot * a.ntiles + T) * 128;
-      dp[ln] = dd[0];
-      dp[64 + ln] = dd[1];
+      // Tile T holds diagonal dl = base + e, base = n - r - 64 T - 63. Its
+      // diagonals e = 64 + l (l <= 62) are the diagonals e = l of tile T - 1,
+      // which are summed first; e = 63 is in no other tile. Pairs inside the
+      // chunk are completed here, pairs across a chunk edge go to the edge
+      // buffer (lo: the chunk's last tile, hi: its first) and are added by
+      // vs_diag_edge_kernel; at the ends of the row a diagonal has one tile.
+      const int64_t base = (int64_t)n - r - (int64_t)T * kBlock - 63;
+      float* sl = a.slsum + (size_t)slot * n;
+      float* edge = a.dedge + ((size_t)slot * a.nchunks + ch) * 128;
+      if (ln == 63) {
+        if (base + 63 >= 0 && base + 63 < n) sl[base + 63] = 0.f + dd[0];
+      } else {
+        const int64_t dh = base + 64 + ln;  // diagonal e = 64 + ln of this tile
+        if (T > t0) {
+          // written by this lane at the previous tile (a wave's LDS accesses complete in order)
+          if (dh >= 0 && dh < n) sl[dh] = (0.f + sm.dkeep[hw][ln]) + dd[1];
+        } else if (T == 0) {
+          if (dh >= 0 && dh < n) sl[dh] = 0.f + dd[1];
+        } else {
+          edge[64 + ln] = dd[1];
+        }
+        if (T == t1 - 1) {
+          if (T == a.ntiles - 1) {
+            const int64_t dlo = base + ln;
+            if (dlo >= 0 && dlo < n) sl[dlo] = 0.f + dd[0];
+          } else {
+            edge[ln] = dd[0];
+          }
+        }
+        sm.dkeep[hw][ln] = dd[0];
+      }
     }
     cur ^= 1;
   }
@@ -461,24 +491,21 @@ __global__ __launch_bounds__(64) void vs_row_combine_kernel(const VsLaunch a) {
   }
 }
 
-// sl[dl] = sum over the (at most two) tiles whose diagonal window holds dl, in tile order.
-__global__ __launch_bounds__(256) void vs_diag_reduce_kernel(const VsLaunch a) {
+// Diagonals that straddle two chunks of tiles: dl = base(t0) + 64 + l is
+// e = l of tile t0 - 1 (the previous chunk's last tile) and e = 64 + l of
+// tile t0 (this chunk's first), added in tile order.
+__global__ __launch_bounds__(64) void vs_diag_edge_kernel(const VsLaunch a) {
   const int slot = blockIdx.y;
-  const int64_t dl = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t n = a.n;
-  if (dl >= n) return;
-  // tile T holds dl at e = dl - (n - r - 64T - 63), valid for e in [0, 126]
-  const int64_t base = n - a.r - 63 - dl;
-  int64_t tlo = -floor_div(-base, 64);  // ceil(base / 64)
-  int64_t thi = floor_div(base + 126, 64);
-  if (tlo < 0) tlo = 0;
-  if (thi > a.ntiles - 1) thi = a.ntiles - 1;
-  float s = 0.f;
-  for (int64_t T = tlo; T <= thi; ++T) {
-    const int64_t e = 64 * T - base;  // = dl - (n - r - 64T - 63), in [0, 126]
-    s += a.dpart[((size_t)slot * a.ntiles + T) * 128 + e];
-  }
-  a.slsum[(size_t)slot * n + dl] = s;
+  const int c = blockIdx.x + 1;  // chunk whose first tile closes the pair
+  const int l = threadIdx.x;
+  if (l > 62) return;
+  const int t0 = c * a.tiles_per_chunk;
+  if (t0 >= a.ntiles) return;
+  const int64_t dl = (int64_t)a.n - a.r - (int64_t)t0 * kBlock - 63 + 64 + l;
+  if (dl < 0 || dl >= a.n) return;
+  const float* prev = a.dedge + ((size_t)slot * a.nchunks + (c - 1)) * 128;
+  const float* cur = a.dedge + ((size_t)slot * a.nchunks + c) * 128;
+  a.slsum[(size_t)slot * a.n + dl] = (0.f + prev[l]) + cur[64 + l];
 }
 
 // Top-k of each row of a float matrix, ascending indices, ties to the lower index.
@@ -493,8 +520,7 @@ hipError_t launch_vs_scores(const VsLaunch& a, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(vs_pass2_kernel, grid, dim3(kThreads2), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 g2((unsigned)((a.n + 255) / 256), a.n_slots);
-  hipLaunchKernelGGL(vs_diag_reduce_kernel, g2, dim3(256), 0, stream, a);
+  if (a.nchunks > 1) hipLaunchKernelGGL(vs_diag_edge_kernel, dim3(a.nchunks - 1, a.n_slots), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
