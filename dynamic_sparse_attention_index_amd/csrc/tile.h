@@ -202,6 +202,9 @@ __device__ __forceinline__ void fused_tile_pair(WaveState& ws, const OperandOffs
   float psum = 0.f;
 #pragma unroll
   for (int j = 0; j < kReadAhead; ++j) kop[j] = kread(j);
+  // raised issue priority while the wave feeds the matrix cores: when both
+  // waves of a SIMD are ready, the one in this section issues first
+  __builtin_amdgcn_s_setprio(1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -228,6 +231,7 @@ __device__ __forceinline__ void fused_tile_pair(WaveState& ws, const OperandOffs
     if (j + kReadAhead < 16) vop[j + kReadAhead] = vread(j + kReadAhead);
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   ws.l += psum;
   sn[0] = n0;
   sn[1] = n1;
