@@ -477,7 +477,7 @@ static minf_status launch_all_heads(AttnLaunch& a, int hq, hipStream_t stream) {
   for (int h0 = 0; h0 < hq;) {
     int nh, hg;
     head_split(hq, a.grp, h0, true, nh, hg);
-    a.head0 = h0;
+    for (int i = 0; i < nh; ++i) a.heads[i].head = h0 + i;
     a.nh = nh;
     a.hgroup = hg;
     hipError_t e = launch_attn(a, stream);
@@ -597,13 +597,31 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
                                        pos_ws + (size_t)h * 2 * nbk + nbk, stream);
     if (e != hipSuccess) return hip_fail(e, "block position kernel");
   }
-  for (int h0 = 0; h0 < hq;) {
-    int nh, hg;
-    head_split(hq, a.grp, h0, false, nh, hg);
+  // Launch order: the Vertical-Slash heads (and VS windows) first, then the
+  // other heads, each in launches of up to kMaxLaunchHeads heads. A launch of
+  // VS heads only can take the rounds launch; the short Block-Sparse and
+  // A-shape items then do not hold back the rounds of the long VS items.
+  std::vector<int> order;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int h = 0; h < hq; ++h) {
+      const bool vs_class = plans[h].kind == MINF_KIND_VS || plans[h].kind == MINF_KIND_VS_WINDOW;
+      if (vs_class == (pass == 0)) order.push_back(h);
+    }
+  for (size_t i0 = 0; i0 < order.size();) {
+    const bool vs_class = plans[order[i0]].kind == MINF_KIND_VS || plans[order[i0]].kind == MINF_KIND_VS_WINDOW;
+    int nh = 0;
+    while (i0 + nh < order.size() && nh < kMaxLaunchHeads) {
+      const int h = order[i0 + nh];
+      const bool c = plans[h].kind == MINF_KIND_VS || plans[h].kind == MINF_KIND_VS_WINDOW;
+      if (c != vs_class) break;
+      ++nh;
+    }
     for (int i = 0; i < nh; ++i) {
-      const minf_head_plan& p = plans[h0 + i];
+      const int hid = order[i0 + i];
+      const minf_head_plan& p = plans[hid];
       AttnHead& d2 = a.heads[i];
       d2 = AttnHead{};
+      d2.head = hid;
       d2.kind = p.kind;
       d2.sink = p.sink;
       d2.local = p.local;
@@ -612,19 +630,19 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
         uint32_t* db;
         int2* wt;
         int32_t* wc;
-        vsw_area(h0 + i, db, wt, wc);
+        vsw_area(hid, db, wt, wc);
         d2.dbits = db;
         d2.wtiles = wt;
         d2.wcount = wc;
       }
       d2.k_b = p.k_b;
       d2.v_idx = p.v_idx;
-      d2.obits = p.kind == MINF_KIND_VS ? (const uint32_t*)workspace + (size_t)(h0 + i) * words : nullptr;
+      d2.obits = p.kind == MINF_KIND_VS ? (const uint32_t*)workspace + (size_t)hid * words : nullptr;
       d2.blk_idx = p.blk_idx;
       d2.blk_cnt = p.blk_cnt;
       if (p.pos) {
-        int first = h0 + i;
-        for (int g = 0; g < h0 + i; ++g)
+        int first = hid;
+        for (int g = 0; g < hid; ++g)
           if (plans[g].pos == p.pos) {
             first = g;
             break;
@@ -636,19 +654,15 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
     std::vector<uint32_t*> launch_bits;
     std::vector<const int32_t*> launch_wcount;
     for (int i = 0; i < nh; ++i) {
-      if (plans[h0 + i].kind == MINF_KIND_VS) launch_bits.push_back((uint32_t*)workspace + (size_t)(h0 + i) * words);
-      if (plans[h0 + i].kind == MINF_KIND_VS_WINDOW) launch_wcount.push_back(a.heads[i].wcount);
+      const int hid = order[i0 + i];
+      if (plans[hid].kind == MINF_KIND_VS) launch_bits.push_back((uint32_t*)workspace + (size_t)hid * words);
+      if (plans[hid].kind == MINF_KIND_VS_WINDOW) launch_wcount.push_back(a.heads[i].wcount);
     }
-    a.head0 = h0;
     a.nh = nh;
-    a.hgroup = hg;
+    a.hgroup = 1;  // sparse items: one head per work chunk
     a.xcd_sync = nullptr;
     a.rounds_flag = nullptr;
-    // only launches whose heads are all Vertical-Slash (or VS windows): with other
-    // kinds beside them the items of a round differ in length and the workgroups
-    // of a round wait for its longest (mixed 512K layer: rounds 1696 ms, ordinary 1647)
-    const bool all_vs = (int)(launch_bits.size() + launch_wcount.size()) == nh;
-    if (all_vs && n >= kRoundsMinTokens && rounds_enabled(stream)) {
+    if (vs_class && n >= kRoundsMinTokens && rounds_enabled(stream)) {
       int32_t* flag = sync_ws + 8;
       hipError_t e = launch_rounds_flag(launch_bits.data(), (int)launch_bits.size(), launch_wcount.data(),
                                         (int)launch_wcount.size(), (int)n, kRoundsMinTiles, flag, stream);
@@ -658,7 +672,7 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
     }
     hipError_t e = launch_attn(a, stream);
     if (e != hipSuccess) return hip_fail(e, "sparse attention kernel");
-    h0 += nh;
+    i0 += nh;
   }
   return MINF_OK;
 }

@@ -377,9 +377,9 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
   const int pr = (npb - 1 - chunk / nhg) * ppc + within / hg;
   if (pr >= npairs) return;
   const int hl = (chunk % nhg) * hg + within % hg;
-  const int h = p.head0 + hl;
-  const int kvh = h / p.grp;
   const AttnHead hd = p.heads[hl];
+  const int h = hd.head;
+  const int kvh = h / p.grp;
   const int n = p.n;
   const int b0 = 2 * pr;
   const int b1 = b0 + 1;

@@ -12,7 +12,7 @@ constexpr int kMaxVsGroups = 32;     // VS head groups in one index launch
 constexpr int64_t kMaxTokens = 1 << 20;  // largest n the in-LDS bitmaps cover (16384 blocks)
 
 struct AttnHead {
-  int32_t kind, sink, local, k_v, k_b, pad;
+  int32_t kind, sink, local, k_v, k_b, head;  // head: the query head this entry describes
   const int32_t* v_idx;    // VS: ascending columns
   const uint32_t* obits;   // VS: bitmap of block offsets covered by the slashes
   const int32_t* blk_idx;  // BLOCK
@@ -30,7 +30,7 @@ struct AttnLaunch {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int32_t n, nb, hq, hkv, grp, head0, nh, causal;
+  int32_t n, nb, hq, hkv, grp, nh, causal;
   int32_t hgroup;  // heads per work chunk: divides nh and 64; consecutive heads (they share K/V when
                    // they fall in one GQA group)
   float scale_log2;

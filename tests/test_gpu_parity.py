@@ -327,6 +327,57 @@ def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch, n):
     check_lse(l1[h][t].cpu().numpy(), wl[0])
 
 
+def _random_block_plan(n, k_b, seed):
+    # every query block b selects min(k_b, b + 1) random key blocks c <= b, ascending, padded with -1
+    nb = (n + 63) // 64
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    r = torch.rand(nb, nb, device="cuda", generator=g).tril() + torch.triu(torch.full((nb, nb), -1.0, device="cuda"), 1)
+    top = r.topk(k_b, dim=1).indices.sort(dim=1).values
+    cnt = torch.clamp(torch.arange(nb, device="cuda") + 1, max=k_b).to(torch.int32)
+    ar = torch.arange(k_b, device="cuda")[None, :]
+    bi = torch.where(ar < cnt[:, None], top, torch.full_like(top, -1)).to(torch.int32).contiguous()
+    return dict(kind="block", blk_idx=bi, blk_cnt=cnt.contiguous())
+
+
+def test_mixed_heads_rounds_partition_matches_ordinary(gpu_lib, monkeypatch):
+    # VS heads between A-shape and Block-Sparse heads at 2^19 + 37 tokens: the VS heads
+    # go to a launch of their own that takes the XCD-round launch, the others to an
+    # ordinary launch; MINF_ATTN_ROUNDS=0 keeps every launch ordinary
+    n, hq, hkv = (1 << 19) + 37, 8, 2
+    q, k, v, _ = _qkv(n, hq, hkv, 41)
+    g = torch.Generator().manual_seed(42)
+    plans = []
+    for h in range(hq):
+        kind = ("ashape", "vs", "block", "vs", "vs", "ashape", "block", "vs")[h]
+        if kind == "vs":
+            si = torch.randperm(n, generator=g)[:4000 + 300 * h].sort().values.to(torch.int32)
+            vi = torch.randperm(n, generator=g)[:300].sort().values.to(torch.int32)
+            plans.append(dict(kind="vs", v_idx=vi.cuda(), s_idx=si.cuda()))
+        elif kind == "block":
+            plans.append(_random_block_plan(n, 16, 43 + h))
+        else:
+            plans.append(dict(kind="ashape", sink=100 + h, local=3000 + 7 * h))
+    monkeypatch.delenv("MINF_ATTN_ROUNDS", raising=False)
+    o1, l1 = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    monkeypatch.setenv("MINF_ATTN_ROUNDS", "0")
+    o2, l2 = gpu_lib.minf_sparse_attn(q, k, v, plans, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # sampled rows of a VS, a Block-Sparse and an A-shape head against the oracle
+    rows = np.concatenate([np.arange(0, 64), np.arange(n // 2, n // 2 + 64), np.arange(64 * ((n - 1) // 64) - 64, n)])
+    t = torch.as_tensor(rows, device="cuda")
+    for h in (1, 2, 5):
+        kvh = h // (hq // hkv)
+        qh = np.zeros((1, n, 128), np.float32)
+        qh[0, rows] = to_np(q[h][t])
+        p = plans[h]
+        wo, wl = O.sparse_attn(qh, to_np(k[kvh:kvh + 1]), to_np(v[kvh:kvh + 1]), 1, 1, SCALE, _np_plans([p]), rows=rows)
+        err = max_abs(to_np(o1[h][t]), wo[0])
+        print(f"  head {h} ({p['kind']}): max-abs err {err:.3e}", flush=True)
+        assert err <= OUT_TOL
+        check_lse(l1[h][t].cpu().numpy(), wl[0])
+
+
 # ---------------------------------------------------------------- VS with slash-aligned windows
 def _window_plans(n, hq, seed, k_s, k_v, local=False, aligned=False):
     g = torch.Generator().manual_seed(seed)
