@@ -441,6 +441,36 @@ static bool rounds_enabled(hipStream_t stream) {
   return cs == hipStreamCaptureStatusNone;
 }
 
+// Dense causal attention from 2^17 tokens takes the rounds launch too: every
+// work item walks all its keys, so the 64 workgroups of an XCD share K/V tiles
+// through L2 as long as they stay together (32/8 heads: 128K 132.5 -> 128.5
+// ms, 1M 10.07 -> 8.04 s). Its barrier counters and its always-set flag live
+// in a static per-GPU array (dense calls take no workspace); calls that
+// overlap on one GPU share it, which can only slow their rounds (each wait is
+// bounded) and never changes a result.
+constexpr int64_t kDenseRoundsMinTokens = 1 << 17;
+static __device__ __align__(256) int32_t dense_rounds_state[kRoundXcds + 1];
+std::mutex g_dense_rounds_mu;
+int32_t* g_dense_rounds_ptr[64] = {};
+
+static int32_t* dense_rounds_state_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_dense_rounds_mu);
+  if (!g_dense_rounds_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(dense_rounds_state)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_dense_rounds_ptr[dev] = (int32_t*)ptr;
+  }
+  return g_dense_rounds_ptr[dev];
+}
+
 static minf_status check_attn_common(const void* q, const void* k, const void* v, void* o, int64_t n, int hq,
                                      int hkv, int d, float scale, int64_t max_n) {
   minf_status s;
@@ -780,6 +810,14 @@ minf_status minf_dense_attn(const void* q, const void* k, const void* v, void* o
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale * 1.4426950408889634f;
   for (int i = 0; i < kMaxLaunchHeads; ++i) a.heads[i] = AttnHead{};
+  if (causal && n >= kDenseRoundsMinTokens && rounds_enabled(stream)) {
+    int32_t* st = dense_rounds_state_ptr();
+    if (st) {
+      a.xcd_sync = st;
+      a.rounds_flag = st + kRoundXcds;
+      a.rounds_flag_set = st + kRoundXcds;
+    }
+  }
   return launch_all_heads(a, hq, stream);
 }
 

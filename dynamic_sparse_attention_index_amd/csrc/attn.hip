@@ -51,7 +51,7 @@ namespace minf {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kXcds = 8;     // MI355X: workgroups are dealt round-robin to 8 XCDs, each with its own L2
+constexpr int kXcds = kRoundXcds;  // MI355X: workgroups are dealt round-robin to 8 XCDs, each with its own L2
 constexpr int kChunk = 64;   // workgroups one XCD runs at once (32 CUs x 2)
 constexpr int kTileHalves = kBlock * kHeadDim;  // one 64 x 128 bf16 tile, 16 KiB, rows of 256 bytes
 constexpr int kBitWords = (kMaxTokens / kBlock) / 32 + 1;  // 513 words per bitmap
@@ -863,8 +863,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel_rounds(const AttnLaun
   }
 }
 
-__global__ void zero_counters_kernel(int32_t* c, int n) {
+__global__ void zero_counters_kernel(int32_t* c, int n, int32_t* flag_on) {
   if ((int)threadIdx.x < n) c[threadIdx.x] = 0;
+  if (flag_on != nullptr && threadIdx.x == 0) *flag_on = 1;
 }
 
 
@@ -959,7 +960,7 @@ hipError_t launch_attn(const AttnLaunch& a, hipStream_t stream) {
     // the rounds launch, then the ordinary one; the device-side flag lets exactly one of them work
     AttnLaunch b = a;
     b.rounds = (int)((chunks + kXcds - 1) / kXcds);
-    hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, b.xcd_sync, kXcds);
+    hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, stream, b.xcd_sync, kXcds, b.rounds_flag_set);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 gr(kXcds * kChunk), tr(kThreads);

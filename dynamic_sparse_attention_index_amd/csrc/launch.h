@@ -24,6 +24,8 @@ struct AttnHead {
   const uint32_t* dbits;   // VS windows: bitmap of the slash offsets over [0, n)
 };
 
+constexpr int kRoundXcds = 8;  // XCDs of an MI355X: one barrier counter each in a rounds launch
+
 struct AttnLaunch {
   const uint16_t* q;
   const uint16_t* k;
@@ -34,8 +36,9 @@ struct AttnLaunch {
   int32_t hgroup;  // heads per work chunk: divides nh and 64; consecutive heads (they share K/V when
                    // they fall in one GQA group)
   float scale_log2;
-  int32_t* xcd_sync;          // per-XCD barrier counters (8 ints) for a rounds launch, else null
+  int32_t* xcd_sync;          // per-XCD barrier counters (kRoundXcds ints) for a rounds launch, else null
   const int32_t* rounds_flag;  // device flag: 1 = the rounds launch works, 0 = the ordinary launch does
+  int32_t* rounds_flag_set;    // non-null: set to 1 before the launches (a launch known to take rounds)
   int32_t rounds;              // set by launch_attn
   AttnHead heads[kMaxLaunchHeads];
 };

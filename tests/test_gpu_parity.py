@@ -63,6 +63,32 @@ def test_dense_causal(gpu_lib, n, hq, hkv):
     check_lse(to_np(lse), wl)
 
 
+@pytest.mark.parametrize("n", [1 << 19, (1 << 19) + 37])
+def test_dense_rounds_launch_matches_ordinary(gpu_lib, monkeypatch, n):
+    # at 2^19+ tokens causal dense attention takes the XCD-round launch (counters in a
+    # static per-GPU array); MINF_ATTN_ROUNDS=0 forces the ordinary launch
+    hq, hkv = 4, 1
+    q, k, v, _ = _qkv(n, hq, hkv, 51)
+    monkeypatch.delenv("MINF_ATTN_ROUNDS", raising=False)
+    o1, l1 = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE)
+    o3, l3 = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE)  # a second call reuses the counters
+    monkeypatch.setenv("MINF_ATTN_ROUNDS", "0")
+    o2, l2 = gpu_lib.minf_dense_attn(q, k, v, scale=SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    rows = np.concatenate([np.arange(0, 64), np.arange(n // 2, n // 2 + 64), np.arange(64 * ((n - 1) // 64) - 64, n)])
+    t = torch.as_tensor(rows, device="cuda")
+    for h in (0, hq - 1):
+        qh = np.zeros((1, n, 128), np.float32)
+        qh[0, rows] = to_np(q[h][t])
+        wo, wl = O.dense_attn(qh, to_np(k), to_np(v), 1, 1, SCALE, rows=rows)
+        err = max_abs(to_np(o1[h][t]), wo[0])
+        print(f"  dense rounds launch, head {h}: max-abs err {err:.3e}", flush=True)
+        assert err <= OUT_TOL
+        check_lse(to_np(l1[h][t]), wl[0])
+
+
 @pytest.mark.parametrize("n", [200, 1000])
 def test_dense_noncausal(gpu_lib, n):
     q, k, v, _ = _qkv(n, 2, 1, 12)
