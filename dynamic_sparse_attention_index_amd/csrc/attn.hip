@@ -56,6 +56,7 @@ constexpr int kChunk = 64;   // workgroups one XCD runs at once (32 CUs x 2)
 constexpr int kTileHalves = kBlock * kHeadDim;  // one 64 x 128 bf16 tile, 16 KiB, rows of 256 bytes
 constexpr int kBitWords = (kMaxTokens / kBlock) / 32 + 1;  // 513 words per bitmap
 constexpr int kColChunk = 1024;  // candidate vertical columns compacted per round
+constexpr int kNzWords = (kBitWords + kThreads - 1) / kThreads * (kThreads / 32);  // summary words (24)
 
 // K/V tile buffers are four distinct LDS objects (not one array): the
 // compiler then knows that the direct loads filling one buffer cannot alias
@@ -63,6 +64,7 @@ constexpr int kColChunk = 1024;  // candidate vertical columns compacted per rou
 // computing on the current tile.
 struct Smem {
   uint32_t bits[2][kBitWords];
+  uint32_t nz[kNzWords];  // VS: bit w set when word w of either offset bitmap is non-zero
   uint32_t clist[kColChunk];
   int scan[16];
 };
@@ -110,6 +112,21 @@ struct BlockIter {
   // VS: block-offset bitmaps of b0 and b1 (they differ only for a partial last block).
   const uint32_t* bits0;
   const uint32_t* bits1;
+  const uint32_t* nzw;  // VS: non-empty words of the offset bitmaps
+
+  // VS: the highest word <= ww whose union can be non-zero, or -1. The union
+  // of word x reads bit 31 of word x - 1, so a non-empty word z makes words z
+  // and z + 1 candidates.
+  __device__ int prev_nonempty(int ww) {
+    int sw = ww >> 5;
+    uint32_t m = uniform_u32(nzw[sw]) & (0xffffffffu >> (31 - (ww & 31)));
+    while (m == 0u) {
+      if (--sw < 0) return -1;
+      m = uniform_u32(nzw[sw]);
+    }
+    const int z = (sw << 5) + 31 - __builtin_clz(m);
+    return z + 1 <= ww ? z + 1 : ww;
+  }
 
   // Reads word ww of both memberships from LDS (kept in registers until the
   // cursor leaves the word) and returns their union. The words are the same
@@ -181,10 +198,16 @@ struct BlockIter {
       return false;
     }
     if (kind == KIND_VS) {
-      // highest remaining offset v first: key block c = b0 + 1 - v ascending
+      // highest remaining offset v first: key block c = b0 + 1 - v ascending;
+      // below an empty word, the run of empty words is skipped through the summary
       while (rem == 0u) {
         if (--w < 0) return false;
         rem = union_word(w);
+        if (rem == 0u && w > 0) {
+          w = prev_nonempty(w - 1);
+          if (w < 0) return false;
+          rem = union_word(w);
+        }
       }
       const int bit = 31 - __builtin_clz(rem);
       rem ^= 1u << bit;
@@ -439,15 +462,39 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     it.wlo1 = wlo(b1);
     if (0 >= it.sb && 0 < it.wlo0) it.c = it.wlo0;
   } else if (hd.kind == KIND_VS) {
-    // offset bitmap of full blocks, and (when n % 64 != 0) of the partial last block
+    // offset bitmap of full blocks, and (when n % 64 != 0) of the partial
+    // last block, up to the pair's largest offset b0 + 1, with one summary bit
+    // per word (either bitmap non-zero); all loads are issued before any use
     const int nwords = (p.nb >> 5) + 1;
+    const int ncopy = ((b0 + 1) >> 5) + 1;
     const int last_partial = (n & (kBlock - 1)) != 0;
     const int need_last = last_partial && bmax == p.nb - 1;
-    for (int i = tid; i < nwords; i += kThreads) {
-      sm.bits[0][i] = hd.obits[i];
-      if (need_last) sm.bits[1][i] = hd.obits[nwords + i];
+    constexpr int kRounds = (kBitWords + kThreads - 1) / kThreads;
+    uint32_t wa[kRounds], wb[kRounds];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = r * kThreads + tid;
+      wa[r] = i < ncopy ? hd.obits[i] : 0u;
+      wb[r] = i < ncopy && need_last ? hd.obits[nwords + i] : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int i = r * kThreads + tid;
+      if (r * kThreads < ncopy) {  // uniform: every wave takes the ballot
+        if (i < ncopy) {
+          sm.bits[0][i] = wa[r];
+          if (need_last) sm.bits[1][i] = wb[r];
+        }
+        const uint64_t bal = __ballot((wa[r] | wb[r]) != 0u);
+        if (lane == 0) {
+          const int sw = (r * kThreads + 64 * wave) >> 5;
+          sm.nz[sw] = (uint32_t)bal;
+          sm.nz[sw + 1] = (uint32_t)(bal >> 32);
+        }
+      }
     }
     __syncthreads();
+    it.nzw = sm.nz;
     it.bits0 = (need_last && b0 == p.nb - 1) ? sm.bits[1] : sm.bits[0];
     it.bits1 = (need_last && b1 == p.nb - 1) ? sm.bits[1] : sm.bits[0];
     it.base = b0 + 1;
