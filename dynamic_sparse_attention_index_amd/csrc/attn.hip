@@ -56,7 +56,8 @@ constexpr int kChunk = 64;   // workgroups one XCD runs at once (32 CUs x 2)
 constexpr int kTileHalves = kBlock * kHeadDim;  // one 64 x 128 bf16 tile, 16 KiB, rows of 256 bytes
 constexpr int kBitWords = (kMaxTokens / kBlock) / 32 + 1;  // 513 words per bitmap
 constexpr int kColChunk = 1024;  // candidate vertical columns compacted per round
-constexpr int kNzWords = (kBitWords + kThreads - 1) / kThreads * (kThreads / 32);  // summary words (24)
+constexpr int kBitRounds = (kBitWords + kThreads - 1) / kThreads;  // bitmap words per thread (3)
+constexpr int kNzWords = kBitRounds * (kThreads / 32);               // summary words (24)
 
 // K/V tile buffers are four distinct LDS objects (not one array): the
 // compiler then knows that the direct loads filling one buffer cannot alias
@@ -64,7 +65,7 @@ constexpr int kNzWords = (kBitWords + kThreads - 1) / kThreads * (kThreads / 32)
 // computing on the current tile.
 struct Smem {
   uint32_t bits[2][kBitWords];
-  uint32_t nz[kNzWords];  // VS: bit w set when word w of either offset bitmap is non-zero
+  uint32_t nz[kNzWords];  // VS / BLOCK: bit w set when word w of either bitmap is non-zero
   uint32_t clist[kColChunk];
   int scan[16];
 };
@@ -112,7 +113,7 @@ struct BlockIter {
   // VS: block-offset bitmaps of b0 and b1 (they differ only for a partial last block).
   const uint32_t* bits0;
   const uint32_t* bits1;
-  const uint32_t* nzw;  // VS: non-empty words of the offset bitmaps
+  const uint32_t* nzw;  // VS / BLOCK: non-empty words of the bitmaps
 
   // VS: the highest word <= ww whose union can be non-zero, or -1. The union
   // of word x reads bit 31 of word x - 1, so a non-empty word z makes words z
@@ -126,6 +127,18 @@ struct BlockIter {
     }
     const int z = (sw << 5) + 31 - __builtin_clz(m);
     return z + 1 <= ww ? z + 1 : ww;
+  }
+
+  // BLOCK: the lowest word >= ww with a set bit, or wmax + 1.
+  __device__ int next_nonempty(int ww) {
+    int sw = ww >> 5;
+    const int swmax = wmax >> 5;
+    uint32_t m = uniform_u32(nzw[sw]) & (0xffffffffu << (ww & 31));
+    while (m == 0u) {
+      if (++sw > swmax) return wmax + 1;
+      m = uniform_u32(nzw[sw]);
+    }
+    return (sw << 5) + __builtin_ctz(m);
   }
 
   // Reads word ww of both memberships from LDS (kept in registers until the
@@ -216,10 +229,16 @@ struct BlockIter {
       mem = (int)((mw0 >> bit) & 1u) | ((int)((mw1 >> bit) & 1u) << 1);
       return true;
     }
-    // bitmap kinds: iterate set bits of the union word by word
+    // bitmap kinds: iterate set bits of the union word by word; above an
+    // empty word, the run of empty words is skipped through the summary
     while (rem == 0u) {
       if (++w > wmax) return false;
       uint32_t u = union_word(w);
+      if (u == 0u && w < wmax) {
+        w = next_nonempty(w + 1);
+        if (w > wmax) return false;
+        u = union_word(w);
+      }
       if (w == wmax) {
         const int top = cmax & 31;
         u &= top == 31 ? 0xffffffffu : ((1u << (top + 1)) - 1u);
@@ -469,16 +488,15 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     const int ncopy = ((b0 + 1) >> 5) + 1;
     const int last_partial = (n & (kBlock - 1)) != 0;
     const int need_last = last_partial && bmax == p.nb - 1;
-    constexpr int kRounds = (kBitWords + kThreads - 1) / kThreads;
-    uint32_t wa[kRounds], wb[kRounds];
+    uint32_t wa[kBitRounds], wb[kBitRounds];
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
+    for (int r = 0; r < kBitRounds; ++r) {
       const int i = r * kThreads + tid;
       wa[r] = i < ncopy ? hd.obits[i] : 0u;
       wb[r] = i < ncopy && need_last ? hd.obits[nwords + i] : 0u;
     }
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
+    for (int r = 0; r < kBitRounds; ++r) {
       const int i = r * kThreads + tid;
       if (r * kThreads < ncopy) {  // uniform: every wave takes the ballot
         if (i < ncopy) {
@@ -539,6 +557,21 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       }
     }
     __syncthreads();
+    // summary of the non-empty words (every wave takes the ballots)
+#pragma unroll
+    for (int r = 0; r < kBitRounds; ++r) {
+      if (r * kThreads < nwords) {
+        const int i = r * kThreads + tid;
+        const uint64_t bal = __ballot(i < nwords && (sm.bits[0][i] | sm.bits[1][i]) != 0u);
+        if (lane == 0) {
+          const int sw = (r * kThreads + 64 * wave) >> 5;
+          sm.nz[sw] = (uint32_t)bal;
+          sm.nz[sw + 1] = (uint32_t)(bal >> 32);
+        }
+      }
+    }
+    __syncthreads();
+    it.nzw = sm.nz;
     it.cmax = cmax_blk;
     it.init_bitmap_cursor(cmax_blk);
   }
