@@ -27,14 +27,14 @@
 //    the A-operand layout of O^T = V^T P^T; the key order inside each 16-key
 //    step matches the score accumulator's row order, so P goes from
 //    accumulator to MFMA operand without any cross-lane movement.
-//  * K and V have rings of two LDS buffers each, one barrier per tile. Dense,
-//    A-shape, VS block tiles and Block-Sparse plans on unpermuted sequences
-//    run a software pipeline per wave (tile.h): the scores of tile t + 1 are
-//    formed on the matrix cores while the vector ALUs compute tile t's
-//    probabilities, then tile t's PV product runs; K of tile t + 2 and V of
-//    tile t + 1 stream in meanwhile. The other launches (gathered columns,
-//    permuted sequences, VS windows) compute one tile per step with the next
-//    tile's K and V in flight.
+//  * K and V have rings of two LDS buffers each, one barrier per tile. Key
+//    blocks and windows of every kind (Block-Sparse also on permuted
+//    sequences) run a software pipeline per wave (tile.h): the scores of tile
+//    t + 1 are formed on the matrix cores while the vector ALUs compute tile
+//    t's probabilities, then tile t's PV product runs; K of tile t + 2 and V
+//    of tile t + 1 stream in meanwhile. Gathered columns (and launches that
+//    would mix permuted and window heads) compute one tile per step with the
+//    next tile's K and V in flight.
 //  * every kind walks its key tiles in ascending key order, and the work map
 //    gives each XCD whole chunks of 64 workgroups (one head x 64 pairs for
 //    sparse plans, one GQA group x 16 pairs for dense) that move through the
@@ -678,9 +678,9 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       bm_cur = bm_nxt;
       return hn;
     };
-    if constexpr (XK == 0 || XK == kXkWin) {
+    if constexpr (XK == 0 || XK == kXkWin || XK == kXkPos) {
       // Software-pipelined walk (dense, A-shape, VS, VS window and Block-Sparse
-      // heads on unpermuted sequences). Tile t's K sits in K buffer t % 2 and
+      // heads, Block-Sparse also on permuted sequences). Tile t's K sits in K buffer t % 2 and
       // its V in V buffer t % 2. Step t forms the scores of tile t + 1 (K buffer
       // (t + 1) % 2) while the softmax of tile t runs, then tile t's PV product
       // (V buffer t % 2); meanwhile K of tile t + 2 streams into K buffer t % 2
@@ -702,6 +702,21 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
           issue_contig1(vr, (uint32_t)j0 * (kHeadDim * 2), dst, lane_off);
         else
           issue_rows1(vr, dst, [&](int x) { const int j = j0 + x; return j < 0 ? 0 : (j < n ? j : n - 1); });
+      };
+      // permuted sequences: a tile's key positions go to LDS with its V rows (slot
+      // t % 2, read when tile t is masked) and its key block's latest position to
+      // a register, both one step ahead
+      uint32_t* ps0 = sm.clist;
+      uint32_t* ps1 = sm.clist + kBlock;
+      auto issue_pos = [&](int cblk, uint32_t* psn) {
+        if (wave != 0) return;
+        if ((cblk + 1) * kBlock <= n) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(posr, (lds_ptr)psn, 4, (uint32_t)lane * 4u,
+                                                   (uint32_t)cblk * kBlock * 4u, 0, 0);
+        } else {
+          const int j = cblk * kBlock + lane;
+          psn[lane] = j < n ? (uint32_t)hd.pos[j] : 0x3fffffffu;
+        }
       };
       const int rmin = qb * kBlock + (wave & 1) * 32;  // the wave's first row
       // mask of tile c for this wave's block; wend: the A-shape window, or the end of a VS window interval
@@ -727,6 +742,10 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       if (h0) {
         issue_k(c_cur, kt0);
         issue_v(c_cur, vt0);
+        if ((XK & kXkPos) && posm) {
+          issue_pos(c_cur, ps0);
+          bm_cur = hd.blkmax[c_cur];
+        }
         h1 = next_tile(c_nxt, m_nxt, e0_nxt, e1_nxt);
         if (h1) issue_k(c_nxt, kt1);
       }
@@ -736,17 +755,28 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
       if (h0 && wave_on && ((m_cur >> qsel) & 1)) qk_tile(ws, oo, kt0, sa);
       __syncthreads();  // every wave has read K buffer 0 before tile 2 overwrites it
       auto pstep = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], uint16_t* kc, uint16_t* kn, uint16_t* vc,
-                       uint16_t* vn) -> bool {
+                       uint16_t* vn, uint32_t* pc, uint32_t* pn) -> bool {
         const bool h2 = h1 && next_tile(c2, m2, e02, e12);
         if (h2) issue_k(c2, kc);
-        if (h1) issue_v(c_nxt, vn);
+        if (h1) {
+          issue_v(c_nxt, vn);
+          if ((XK & kXkPos) && posm) {
+            issue_pos(c_nxt, pn);
+            bm_nxt = hd.blkmax[c_nxt];
+          }
+        }
         const bool u0 = wave_on && ((m_cur >> qsel) & 1);
         const bool u1 = h1 && wave_on && ((m_nxt >> qsel) & 1);
         if (u0) {
           int wend;
-          const int mask = tile_mask_of(c_cur, e0_cur, e1_cur, wend);
+          int mask = tile_mask_of(c_cur, e0_cur, e1_cur, wend);
+          // permuted sequences: the tile is fully visible when its key block's
+          // latest position is at most the wave's earliest query position
+          if ((XK & kXkPos) && posm) mask = bm_cur <= wminpos ? MASK_NONE : MASK_POS;
+          // rpos is the query row itself unless the sequence is permuted
           if (mask != MASK_NONE)
-            mask_scores<XK>(sc, mask, kstart(c_cur), nullptr, qsel, row, n, causal_eff, ashape, hd.sink, wend);
+            mask_scores<XK>(sc, mask, kstart(c_cur), (XK & kXkPos) ? pc : nullptr, qsel, rpos, n, causal_eff, ashape,
+                            hd.sink, wend);
           if (u1)
             fused_tile_pair(ws, oo, sc, kn, vc, sn, sl2);
           else
@@ -767,11 +797,12 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
         m_nxt = m2;
         e0_nxt = e02;
         e1_nxt = e12;
+        bm_cur = bm_nxt;
         return h0;
       };
       while (h0) {
-        if (!pstep(sa, sb, kt0, kt1, vt0, vt1)) break;
-        if (!pstep(sb, sa, kt1, kt0, vt1, vt0)) break;
+        if (!pstep(sa, sb, kt0, kt1, vt0, vt1, ps0, ps1)) break;
+        if (!pstep(sb, sa, kt1, kt0, vt1, vt0, ps1, ps0)) break;
       }
     } else {
     // key-position slots of the two tile buffers (phase B, which uses clist, never runs on BLOCK heads)

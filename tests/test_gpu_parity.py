@@ -284,6 +284,32 @@ def test_vs_empty_rows(gpu_lib):
     assert (o[1, :64] == 0).all() and torch.isneginf(lse[1, :64]).all()
 
 
+def test_vs_and_block_sparse_bitmaps_word_edges(gpu_lib):
+    # offsets and key blocks on the 32-bit word edges of the kernel's bitmaps, with long runs of
+    # empty words between them (the cursors skip those runs), at a ragged length
+    n = 64 * 3000 + 23
+    nb = (n + 63) // 64
+    q, k, v, _ = _qkv(n, 3, 1, 41)
+    dev = "cuda"
+    s0 = torch.tensor([64 * 31, 64 * 1023 + 1], dtype=torch.int32, device=dev)
+    s1 = torch.tensor([0, 64 * 31, 64 * 63, 64 * 64 + 5, 64 * 1023, 64 * 2000 + 17, 64 * 2999], dtype=torch.int32,
+                      device=dev)
+    g = torch.Generator().manual_seed(42)
+    vi = torch.randperm(n, generator=g)[:50].sort().values.to(torch.int32).to(dev)
+    kb = 6
+    rows_b = []
+    for b in range(nb):
+        cand = sorted({c for c in (31, 32, 1023, 1024, b - 1, b) if 0 <= c <= b})
+        rows_b.append(cand + [-1] * (kb - len(cand)))
+    bi = torch.tensor(rows_b, dtype=torch.int32, device=dev)
+    bc = (bi >= 0).sum(dim=1).to(torch.int32)
+    plans = [dict(kind="vs", v_idx=vi, s_idx=s0), dict(kind="vs", v_idx=vi, s_idx=s1),
+             dict(kind="block", blk_idx=bi.contiguous(), blk_cnt=bc.contiguous())]
+    rows = np.concatenate([np.arange(0, 130), np.arange(64 * 1023 - 40, 64 * 1025 + 40),
+                           np.arange(64 * 2047, 64 * 2049), np.arange(n - 150, n)])
+    _attn_parity(gpu_lib, q, k, v, plans, rows=rows)
+
+
 @pytest.mark.parametrize("n", [200, 2048 + 64])
 def test_full_budgets_match_dense(gpu_lib, n):
     q, k, v, _ = _qkv(n, 4, 2, 23)
