@@ -42,7 +42,9 @@
 //  * Block-Sparse plans on a permuted sequence (the grid pattern) carry the
 //    original position of every row; a tile that is not entirely earlier than
 //    the wave's earliest query is masked by comparing positions, which the
-//    separate attn_kernel<true> instantiation handles.
+//    instantiations with the kXkPos bit handle.
+//  * VS and Block-Sparse items keep a summary bit per 32-bit word of their
+//    bitmaps in LDS, so the tile cursor skips runs of empty words.
 #include "common.h"
 #include "launch.h"
 #include "tile.h"
