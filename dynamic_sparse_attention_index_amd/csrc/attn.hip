@@ -111,6 +111,7 @@ struct BlockIter {
   // next tile of b0 and of b1, and the blocks' first rows
   const int2* wt;
   int nwt, i0, i1, wb0, wb1;
+  int2 w0, w1;  // entries i0 and i1 of wt, loaded one call ahead (the same in every lane)
   // BLOCK: membership bitmaps over key blocks c of b0 and b1.
   // VS: block-offset bitmaps of b0 and b1 (they differ only for a partial last block).
   const uint32_t* bits0;
@@ -176,16 +177,20 @@ struct BlockIter {
   // tile's first key (may be negative near the start), e0 / e1 the end of the
   // tile's interval for b0 / b1.
   __device__ bool next_window(int& t, int& mem, int& e0, int& e1) {
-    const int s0 = i0 < nwt ? wb0 + wt[i0].x : 0x7fffffff;
-    const int s1 = i1 < nwt ? wb1 + wt[i1].x : 0x7fffffff;
+    const int s0 = i0 < nwt ? wb0 + (int)uniform_u32((uint32_t)w0.x) : 0x7fffffff;
+    const int s1 = i1 < nwt ? wb1 + (int)uniform_u32((uint32_t)w1.x) : 0x7fffffff;
     if (s0 == 0x7fffffff && s1 == 0x7fffffff) return false;
     t = s0 < s1 ? s0 : s1;
     const int m0 = s0 == t, m1 = s1 == t;
-    e0 = m0 ? wb0 + wt[i0].y : 0;
-    e1 = m1 ? wb1 + wt[i1].y : 0;
+    e0 = m0 ? wb0 + (int)uniform_u32((uint32_t)w0.y) : 0;
+    e1 = m1 ? wb1 + (int)uniform_u32((uint32_t)w1.y) : 0;
     i0 += m0;
     i1 += m1;
     mem = m0 | (m1 << 1);
+    // the entries the next call reads: loaded now, so their latency overlaps
+    // the step (the step's closing wait for its copies covers them)
+    if (m0 && i0 < nwt) w0 = wt[i0];
+    if (m1 && i1 < nwt) w1 = wt[i1];
     return true;
   }
 
@@ -525,19 +530,33 @@ __device__ __forceinline__ void attn_item(const AttnLaunch& p, const int item, S
     it.nwt = (int)uniform_u32((uint32_t)*hd.wcount);
     it.wb0 = b0 * kBlock;
     it.wb1 = b1 * kBlock;
+    // 64-way search: each round the 64 lanes test 64 evenly spaced entries
+    // (tile ends ascend) with one load each, so a few rounds of loads replace a
+    // chain of dependent ones
     auto first_tile = [&](int wb) -> int {
-      int lo = 0, hi = it.nwt;
+      int lo = 0, hi = it.nwt;  // entries below lo end at or before key 0, entries from hi on after it
       while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (wb + it.wt[mid].y > 0)
-          hi = mid;
-        else
-          lo = mid + 1;
+        const int step = (hi - lo + 63) >> 6;
+        const int idx = lo + lane * step;
+        const bool after = idx >= hi || wb + it.wt[idx].y > 0;
+        const uint64_t bal = __ballot(after);
+        if (bal == 0ull) {
+          lo += 63 * step + 1;
+        } else {
+          const int f = __builtin_ctzll(bal);
+          const int nhi = min(hi, lo + f * step);
+          if (f > 0) lo += (f - 1) * step + 1;
+          hi = nhi;
+        }
+        lo = (int)uniform_u32((uint32_t)lo);
+        hi = (int)uniform_u32((uint32_t)hi);
       }
-      return (int)uniform_u32((uint32_t)lo);
+      return lo;
     };
     it.i0 = first_tile(it.wb0);
     it.i1 = has_b1 ? first_tile(it.wb1) : it.nwt;
+    it.w0 = it.i0 < it.nwt ? it.wt[it.i0] : int2{0, 0};
+    it.w1 = it.i1 < it.nwt ? it.wt[it.i1] : int2{0, 0};
   } else {  // KIND_BLOCK (on a permuted sequence: every key block can be selected)
     const int cmax_blk = hd.pos ? p.nb - 1 : bmax;
     const int nwords = (cmax_blk >> 5) + 1;
