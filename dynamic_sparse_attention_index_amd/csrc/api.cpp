@@ -424,7 +424,7 @@ size_t minf_sparse_attn_workspace_size(int64_t n, int hq) {
 // MINF_ATTN_ROUNDS=0 in the environment (read on every call), or a stream in
 // graph capture, keeps the ordinary launch only; both give bitwise-identical
 // results.
-constexpr int64_t kRoundsMinTokens = 1 << 19;
+constexpr int64_t kRoundsMinTokens = 1 << 17;
 constexpr int kRoundsMinTiles = 1024;
 
 static bool rounds_enabled(hipStream_t stream) {

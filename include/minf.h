@@ -212,7 +212,7 @@ minf_status minf_sparse_attn(const void* q, const void* k, const void* v, void* 
                              const minf_head_plan* plans, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
-/* Launch order: with Vertical-Slash heads and n >= 2^19, the heads' offset
+/* Launch order: with Vertical-Slash heads and n >= 2^17, the heads' offset
  * sets decide on the device whether the workgroups of each XCD take their
  * work items in rounds that start together (long items share K/V tiles in
  * L2) or as one ordinary launch; results are bitwise identical either way.

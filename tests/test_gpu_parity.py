@@ -348,9 +348,9 @@ def test_mixed_heads_gqa_and_determinism(gpu_lib):
     assert torch.equal(vi, vi2) and torch.equal(si, si2) and torch.equal(bi, bi2) and torch.equal(bc, bc2)
 
 
-@pytest.mark.parametrize("n", [1 << 19, (1 << 19) + 37])
+@pytest.mark.parametrize("n", [(1 << 17) + 37, 1 << 19, (1 << 19) + 37])
 def test_rounds_launch_matches_ordinary(gpu_lib, monkeypatch, n):
-    # 2^19 tokens (and a ragged length), scattered slash offsets: long work items,
+    # 2^17 and 2^19 tokens (and ragged lengths), scattered slash offsets: long work items,
     # so the XCD-round launch takes the work; MINF_ATTN_ROUNDS=0 forces the ordinary launch
     hq = 4
     q, k, v, _ = _qkv(n, hq, 1, 25)
